@@ -1,0 +1,156 @@
+/*
+ * w4a16.h -- W4A16 mixed-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *   Y[M][N] = X[M][K] . W[K][N],   W[k][n] = (q[k][n] - z[k/G][n]) * s[k/G][n]
+ *
+ * X and Y are fp16, q and z are unsigned 4-bit codes (0..15), s is fp16, and
+ * all products are accumulated in fp32. The dequantization formula is the one
+ * given in "LMDeploy Guide: Fast Mixed-Precision LLM Inference Engine",
+ * section 3 "Instruction-Level Parallelism (ILP) for Zero-Overhead
+ * Dequantization"; 4-bit weights in groups with one scale per group and
+ * 16-bit activations are W4A16 as "LMDeploy, in depth" defines it (section
+ * "Quantization: AWQ weights and KV cache"). Groups run along K: rows
+ * [g*G, (g+1)*G) of column n share s[g][n] and z[g][n].
+ *
+ * The library has two parts, as the GEMM pipeline on those pages does
+ * ("LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind",
+ * abstract: offline weight packing plus online acceleration):
+ *   - w4a16_pack: an offline, lossless relayout of (q, z, s) into one packed
+ *     buffer laid out in the order the gfx950 matrix instructions consume it;
+ *   - w4a16_gemm: the online dequantize-and-multiply.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers (memory from hipMalloc or
+ *     torch), C-contiguous, row-major, and at least 16-byte aligned.
+ *   - fp16 tensors are passed as uint16_t bit patterns.
+ *   - The caller owns every buffer; the library keeps no pointer after a call
+ *     returns (apart from its own internal workspace, see w4a16_gemm).
+ *   - `stream` is a hipStream_t (0 = the null stream).
+ *   - Every argument is validated on the host before any HIP call; on a
+ *     validation error nothing is launched and outputs are untouched.
+ *   - Return value: W4A16_OK (0) or a negative W4A16_ERR_* code;
+ *     w4a16_last_error() gives a message for the calling thread.
+ *   - Shapes: K % 128 == 0, N % 16 == 0, G in {32, 64, 128, 256} with
+ *     K % G == 0, M >= 1. Anything else is W4A16_ERR_SHAPE.
+ *
+ * Packed layout, version 1 (bytes, little-endian):
+ *   [0, K*N/2)            weights. Weight (k, n) lives in the 1024-byte tile
+ *                         (n/16)*(K/128) + k/128, in the 32-bit word at byte
+ *                         16*(16*((k%32)/8) + n%16) + 4*((k%128)/32) of the
+ *                         tile, in nibble slot (k%8)/2 + 4*(k%2). One wave64
+ *                         load of 16 bytes per lane reads one whole tile, and
+ *                         (word >> 4i) & 0x000F000F yields the codes of k and
+ *                         k+1 in the two 16-bit halves.
+ *   next 2*N*(K/G)        fp16 scales, s[g][n] at element ((n/16)*(K/G)+g)*16 + n%16.
+ *   next N*(K/G)/2        4-bit zeros, z[g][n] in byte ((n/16)*(K/G)+g)*8 + (n%16)/2,
+ *                         low nibble for even n, high nibble for odd n.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_LAYOUT_VERSION 1
+
+#define W4A16_OK 0
+#define W4A16_ERR_NULL (-1)      /* a required pointer is NULL */
+#define W4A16_ERR_SHAPE (-2)     /* M, N, K or G outside the supported set */
+#define W4A16_ERR_ALIGN (-3)     /* a device pointer is not 16-byte aligned */
+#define W4A16_ERR_RANGE (-4)     /* pack: a q or z code is larger than 15 */
+#define W4A16_ERR_HIP (-5)       /* a HIP runtime call or kernel launch failed */
+#define W4A16_ERR_WORKSPACE (-6) /* workspace missing or smaller than required */
+#define W4A16_ERR_ARG (-7)       /* path or split selector out of range */
+
+/* Execution paths for w4a16_gemm_ex. */
+#define W4A16_PATH_AUTO 0
+#define W4A16_PATH_DECODE 1  /* split-K, HBM-bound; M <= 64 */
+#define W4A16_PATH_PREFILL 2 /* LDS-tiled MFMA, compute-bound; any M */
+
+/*
+ * Size in bytes of the packed buffer for a K x N weight with groups of G;
+ * 0 if the shape is not supported. Host-only, no HIP call.
+ * Equals K*N/2 + 2.5*N*K/G.
+ */
+size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t G);
+
+/*
+ * Offline packing ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
+ * Engine", section 1 "Hardware-Aware Weight Packing (GEMM Pipeline)"): writes
+ * the packed buffer from
+ *   q       uint8 [K][N]     codes 0..15 (one code per byte)
+ *   zeros   uint8 [K/G][N]   codes 0..15
+ *   scales  fp16  [K/G][N]
+ * into `packed` (w4a16_packed_bytes(K, N, G) bytes, caller-allocated).
+ * Enqueued on `stream`, then synchronizes that stream (the pass is offline)
+ * to report W4A16_ERR_RANGE if any code exceeds 15; on that error the packed
+ * contents are unspecified.
+ */
+int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales,
+               int64_t K, int64_t N, int64_t G, void *packed, void *stream);
+
+/*
+ * Exact inverse of w4a16_pack: recovers q, zeros and scales (same layouts as
+ * the inputs of w4a16_pack) from a packed buffer. Synchronizes `stream`.
+ */
+int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G,
+                 uint8_t *q, uint8_t *zeros, uint16_t *scales, void *stream);
+
+/*
+ * Online GEMM ("LMDeploy Guide: Fast Mixed-Precision LLM Inference Engine",
+ * architecture figure, pipeline A, and section 3): Y[M][N] (fp16) =
+ * X[M][K] (fp16) . dequant(packed). The 4-bit codes are turned into fp16 by
+ * an exponent-OR bit trick, the zero is subtracted exactly and the scale is
+ * applied, all inside the kernel; products accumulate in fp32 and Y is
+ * rounded to nearest-even once.
+ *
+ * Asynchronous: enqueued on `stream`, no host synchronization. If the chosen
+ * plan splits K across workgroups (see w4a16_workspace_bytes), a per-device
+ * library workspace is allocated with hipMalloc on first need and reused;
+ * calls that need it must therefore not run concurrently on two streams of
+ * one device (use w4a16_gemm_ex with separate workspaces for that).
+ */
+int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
+               int64_t G, uint16_t *Y, void *stream);
+
+/*
+ * Workspace bytes w4a16_gemm_ex needs for this shape and plan (`path` one of
+ * W4A16_PATH_*, `splits` 0 = automatic, else the number of K splits across
+ * workgroups on the decode path). 0 means the plan needs none. Host-only.
+ */
+size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits);
+
+/*
+ * w4a16_gemm with an explicit plan and a caller-owned workspace.
+ *   path     W4A16_PATH_AUTO / _DECODE / _PREFILL (decode requires M <= 64)
+ *   splits   0 = automatic; otherwise 1 .. K/128 workgroup splits of K
+ *            (decode path only; must be 0 or 1 for prefill)
+ *   workspace, workspace_bytes: at least w4a16_workspace_bytes(...) bytes of
+ *            device memory, or NULL/0 if that is 0. Its first use must find it
+ *            zero-filled; every completed call leaves it in that state again.
+ *            Calls sharing one workspace must be ordered (same stream).
+ * The result does not depend on `path` or `splits` beyond fp32 rounding
+ * order; for a fixed plan it is bitwise reproducible.
+ */
+int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
+                  int64_t G, uint16_t *Y, void *workspace, size_t workspace_bytes,
+                  int path, int splits, void *stream);
+
+/* Static description of a status code. */
+const char *w4a16_status_string(int status);
+
+/* Message of the last failing call on the calling thread ("" if none). */
+const char *w4a16_last_error(void);
+
+/* W4A16_LAYOUT_VERSION of the compiled library. */
+int w4a16_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,103 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments before any HIP call (so this runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import w4a16_mixed_precision_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
+              "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
+              "w4a16_layout_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = w4.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_packed_bytes_matches_layout_spec():
+    for K, N, G in [(256, 256, 128), (4096, 6144, 128), (29568, 8192, 64), (512, 16, 32), (512, 32, 256)]:
+        assert w4.w4a16_packed_bytes(K, N, G) == oracle.packed_bytes(K, N, G)
+    for K, N, G in [(100, 16, 4), (128, 8, 128), (128, 16, 96), (0, 16, 128), (192, 16, 64), (128, 16, 512)]:
+        assert w4.w4a16_packed_bytes(K, N, G) == 0
+
+
+def test_layout_version():
+    assert w4.w4a16_layout_version() == 1
+
+
+def test_gemm_validation_before_any_hip_call():
+    L = w4.lib()
+    assert L.w4a16_gemm(None, FAKE, 1, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemm(FAKE, FAKE, 0, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm(FAKE, FAKE, 1, 250, 256, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm(FAKE, FAKE, 1, 256, 200, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm(FAKE, FAKE, 1, 256, 256, 96, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm(MISALIGNED, FAKE, 1, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_ALIGN
+    assert "16-byte" in w4.w4a16_last_error()
+    assert L.w4a16_gemm(FAKE, FAKE, 1, 256, 256, 128, MISALIGNED, None) == w4.W4A16_ERR_ALIGN
+
+
+def test_gemm_ex_plan_and_workspace_validation():
+    L = w4.lib()
+    # path out of range
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 7, 1, None) == w4.W4A16_ERR_ARG
+    # decode path is limited to M <= 64
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 65, 256, 256, 128, FAKE, None, 0, 1, 1, None) == w4.W4A16_ERR_ARG
+    # more splits than 128-row blocks
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 1, 3, None) == w4.W4A16_ERR_ARG
+    # prefill does not split
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 2, 2, None) == w4.W4A16_ERR_ARG
+    # a split plan without (enough) workspace
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 1, 2, None) == w4.W4A16_ERR_WORKSPACE
+    need = w4.w4a16_workspace_bytes(4, 256, 256, 128, w4.W4A16_PATH_DECODE, 2)
+    assert need > 0
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, FAKE, need - 1, 1, 2, None) == w4.W4A16_ERR_WORKSPACE
+    # unsplit plans need none
+    assert w4.w4a16_workspace_bytes(4, 256, 256, 128, w4.W4A16_PATH_DECODE, 1) == 0
+    assert w4.w4a16_workspace_bytes(4, 256, 256, 128, w4.W4A16_PATH_PREFILL, 1) == 0
+    # split workspace covers S * M * N fp32 partials plus counters
+    assert w4.w4a16_workspace_bytes(16, 4096, 14336, 128, w4.W4A16_PATH_DECODE, 8) >= 8 * 16 * 4096 * 4
+
+
+def test_pack_validation_before_any_hip_call():
+    L = w4.lib()
+    assert L.w4a16_pack(None, FAKE, FAKE, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_pack(FAKE, FAKE, FAKE, 256, 250, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_pack(FAKE, FAKE, FAKE, 256, 256, 128, MISALIGNED, None) == w4.W4A16_ERR_ALIGN
+    assert L.w4a16_unpack(FAKE, 256, 256, 128, None, FAKE, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_unpack(FAKE, 256, 256, 100, FAKE, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        assert w4.w4a16_status_string(code) not in ("", "unknown status")
+    assert w4.w4a16_status_string(-99) == "unknown status"
+
+
+def test_python_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    X = torch.zeros((1, 256), dtype=torch.float16)
+    packed = torch.zeros(w4.w4a16_packed_bytes(256, 256, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        w4.w4a16_gemm(X, packed, 256, 256, 128)

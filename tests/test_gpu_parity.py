@@ -1,0 +1,201 @@
+"""Parity of the HIP path against the CPU oracle, through the C ABI.
+
+Element by element on seeded inputs at sizes the oracle finishes in seconds
+(several tiles, ragged M, both execution paths, every supported group size,
+split and unsplit K), plus the exact special cases: pack bytes equal to the
+written-out layout, identity activations (bit-exact dequantization), integer
+weights (bit-exact GEMM) and zero results.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a16_mixed_precision_amd as w4
+from gpu_util import assert_parity, dev, host, pack_dev, run_gemm, say
+
+pytestmark = pytest.mark.gpu
+
+DECODE, PREFILL = w4.W4A16_PATH_DECODE, w4.W4A16_PATH_PREFILL
+
+
+def _weights(K, N, G, seed):
+    q, z, s, _, rng = synth.draw_weights(K, N, G, seed=seed)
+    return q, z, s, rng
+
+
+# ------------------------------------------------------------------ pack
+
+@pytest.mark.parametrize("K,N,G", [(256, 256, 128), (384, 48, 32), (1152, 80, 64), (512, 32, 256),
+                                   (4096, 6144, 128)])
+def test_pack_bytes_match_layout_and_unpack_round_trips(K, N, G):
+    say(f"pack K={K} N={N} G={G}")
+    q, z, s, _ = _weights(K, N, G, seed=K + N + G)
+    packed = pack_dev(q, z, s, G)
+    got = host(packed)
+    assert got.size == oracle.packed_bytes(K, N, G)
+    assert np.array_equal(got, oracle.layout_pack(q, z, s, G))
+    q2, z2, s2 = w4.w4a16_unpack(packed, K, N, G)
+    assert np.array_equal(host(q2), q) and np.array_equal(host(z2), z)
+    assert np.array_equal(host(s2).view(np.uint16), s.view(np.uint16))
+    # deterministic
+    assert np.array_equal(host(pack_dev(q, z, s, G)), got)
+
+
+def test_pack_rejects_codes_above_15():
+    q, z, s, _ = _weights(256, 64, 128, seed=1)
+    q[17, 5] = 16
+    with pytest.raises(w4.W4A16Error) as e:
+        pack_dev(q, z, s, 128)
+    assert e.value.status == w4.W4A16_ERR_RANGE
+    q[17, 5] = 0
+    z[1, 3] = 99
+    with pytest.raises(w4.W4A16Error) as e:
+        pack_dev(q, z, s, 128)
+    assert e.value.status == w4.W4A16_ERR_RANGE
+
+
+# ------------------------------------------------------------------ exact cases
+
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
+def test_identity_activations_give_fp16_weights_bit_exact(G):
+    # X = I: every output is one exact product (q - z) * s plus exact zeros,
+    # rounded once to fp16, on both paths.
+    K, N = 256, 96
+    q, z, s, _ = _weights(K, N, G, seed=G)
+    packed = pack_dev(q, z, s, G)
+    expect = oracle.dequant(q, z, s, G).astype(np.float16)
+    eye = np.eye(K, dtype=np.float16)
+    Y = run_gemm(eye, packed, N, K, G, path=PREFILL)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+    # decode path: one-hot rows (M <= 64) picking scattered k
+    ks = [0, 1, 7, 8, 31, 32, 63, 64, 100, 127, 128, 129, 200, 254, 255, 130]
+    Y = run_gemm(eye[ks], packed, N, K, G, path=DECODE, splits=1)
+    assert np.array_equal(Y.view(np.uint16), expect[ks].view(np.uint16))
+    Y = run_gemm(eye[ks], packed, N, K, G, path=DECODE, splits=2)
+    assert np.array_equal(Y.view(np.uint16), expect[ks].view(np.uint16))
+
+
+@pytest.mark.parametrize("path,M", [(DECODE, 1), (DECODE, 13), (DECODE, 64), (PREFILL, 5), (PREFILL, 300)])
+def test_integer_weights_bit_exact(path, M):
+    # s = 1, X in {-1, 0, 1}, K = 128: |Y| <= 15 * 128 < 2048, exact in fp16.
+    K, N, G = 128, 160, 64
+    rng = np.random.default_rng(M)
+    q = rng.integers(0, 16, (K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, (K // G, N), dtype=np.uint8)
+    s = np.ones((K // G, N), dtype=np.float16)
+    Xi = rng.integers(-1, 2, (M, K))
+    exact = Xi @ (q.astype(np.int64) - np.repeat(z, G, 0).astype(np.int64))
+    Y = run_gemm(Xi.astype(np.float16), pack_dev(q, z, s, G), N, K, G, path=path)
+    assert np.array_equal(Y.astype(np.int64), exact)
+    assert np.array_equal(oracle.gemm(Xi.astype(np.float16), q, z, s, G), exact.astype(np.float64))
+
+
+@pytest.mark.parametrize("path", [DECODE, PREFILL])
+def test_zero_results(path):
+    K, N, G, M = 256, 64, 128, 9
+    q, z, s, rng = _weights(K, N, G, seed=3)
+    X = synth.draw_x(rng, M, K)
+    q2 = np.repeat(z, G, axis=0)  # q == z everywhere
+    Y = run_gemm(X, pack_dev(q2, z, s, G), N, K, G, path=path)
+    assert np.all(Y == 0)
+    Y = run_gemm(X, pack_dev(np.zeros_like(q), np.zeros_like(z), s, G), N, K, G, path=path)
+    assert np.all(Y == 0)
+
+
+# ------------------------------------------------------------------ oracle parity
+
+SMALL = [
+    # (M, K, N, G, path, splits)
+    (1, 256, 256, 128, DECODE, 1),
+    (4, 256, 256, 128, 0, 0),            # the tiny workload, automatic plan
+    (3, 1152, 272, 64, DECODE, 1),
+    (3, 1152, 272, 64, DECODE, 3),
+    (16, 2048, 1040, 128, DECODE, 4),
+    (17, 1024, 400, 32, DECODE, 2),
+    (33, 1024, 208, 256, DECODE, 7),
+    (64, 1024, 512, 128, DECODE, 1),
+    (64, 1024, 512, 128, PREFILL, 1),
+    (65, 1024, 528, 128, 0, 0),
+    (100, 640, 336, 64, PREFILL, 1),
+    (257, 1024, 1088, 128, 0, 0),
+    (300, 512, 256, 32, PREFILL, 1),
+    (513, 768, 320, 256, 0, 0),
+    (1, 29568, 64, 64, DECODE, 0),
+    (40, 29568, 64, 64, 0, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,G,path,splits", SMALL)
+def test_parity_small(M, K, N, G, path, splits):
+    say(f"parity M={M} K={K} N={N} G={G} path={path} splits={splits}")
+    q, z, s, rng = _weights(K, N, G, seed=M * 7 + K + N)
+    X = synth.draw_x(rng, M, K)
+    Y = run_gemm(X, pack_dev(q, z, s, G), N, K, G, path=path, splits=splits)
+    assert_parity(Y, oracle.gemm(X, q, z, s, G), f"M={M} K={K} N={N} G={G}")
+
+
+def test_parity_with_activation_outliers_both_paths():
+    K, N, G, M = 2048, 512, 128, 48
+    q, z, s, idx, rng = synth.draw_weights(K, N, G, seed=5, outliers=True)
+    X = synth.draw_x(rng, M, K, idx)
+    packed = pack_dev(q, z, s, G)
+    ref = oracle.gemm(X, q, z, s, G)
+    for path, splits in ((DECODE, 1), (DECODE, 4), (PREFILL, 1)):
+        assert_parity(run_gemm(X, packed, N, K, G, path=path, splits=splits), ref, f"path={path}")
+
+
+# ------------------------------------------------------------------ run-time properties
+
+def test_results_are_reproducible_and_workspace_is_reusable():
+    import torch
+    K, N, G, M = 2048, 768, 128, 16
+    q, z, s, rng = _weights(K, N, G, seed=11)
+    X = dev(synth.draw_x(rng, M, K))
+    packed = pack_dev(q, z, s, G)
+    nbytes = w4.w4a16_workspace_bytes(M, N, K, G, DECODE, 4)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        outs.append(host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=DECODE, splits=4)))
+    torch.cuda.synchronize()
+    assert all(np.array_equal(o.view(np.uint16), outs[0].view(np.uint16)) for o in outs)
+    # counters are back to zero after every call
+    tiles = (N // 16 + 3) // 4
+    assert int(ws[: 4 * tiles].view(torch.int32).abs().sum().item()) == 0
+    a = host(w4.w4a16_gemm_ex(X, packed, N, K, G, path=PREFILL))
+    b = host(w4.w4a16_gemm_ex(X, packed, N, K, G, path=PREFILL))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_non_default_stream():
+    import torch
+    K, N, G, M = 1024, 256, 128, 8
+    q, z, s, rng = _weights(K, N, G, seed=12)
+    X = synth.draw_x(rng, M, K)
+    packed = pack_dev(q, z, s, G)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        Xd = dev(X)
+        Y = w4.w4a16_gemm(Xd, packed, N, K, G, stream=st)
+        Y2 = w4.w4a16_gemm_ex(dev(np.repeat(X, 9, 0)), packed, N, K, G, stream=st)
+    st.synchronize()
+    assert_parity(host(Y), oracle.gemm(X, q, z, s, G), "side stream decode")
+    assert_parity(host(Y2), oracle.gemm(np.repeat(X, 9, 0), q, z, s, G), "side stream prefill")
+
+
+def test_rows_do_not_depend_on_batch():
+    # Each output row's accumulation order is fixed by the kernel and plan, so
+    # a row computed alone equals the same row computed inside a batch.
+    K, N, G = 1024, 320, 64
+    q, z, s, rng = _weights(K, N, G, seed=13)
+    X = synth.draw_x(rng, 37, K)
+    packed = pack_dev(q, z, s, G)
+    full = run_gemm(X, packed, N, K, G, path=PREFILL)
+    for m in (0, 16, 36):
+        one = run_gemm(X[m:m + 1], packed, N, K, G, path=PREFILL)
+        assert np.array_equal(one.view(np.uint16), full[m:m + 1].view(np.uint16))
+    block = run_gemm(X[:16], packed, N, K, G, path=DECODE, splits=2)
+    for m in (0, 5, 15):
+        one = run_gemm(X[m:m + 1], packed, N, K, G, path=DECODE, splits=2)
+        assert np.array_equal(one.view(np.uint16), block[m:m + 1].view(np.uint16))

@@ -1,0 +1,191 @@
+"""Python binding of libw4a16.so, the W4A16 GEMM library for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/w4a16.h``. PyTorch supplies
+device memory and streams; tensors are passed as raw device pointers. The
+functions carry the C names and follow the C argument order; shapes are
+taken from the tensors where the C call needs them explicitly.
+
+If the library is not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "W4A16Error", "lib", "library_path",
+    "W4A16_OK", "W4A16_ERR_NULL", "W4A16_ERR_SHAPE", "W4A16_ERR_ALIGN", "W4A16_ERR_RANGE",
+    "W4A16_ERR_HIP", "W4A16_ERR_WORKSPACE", "W4A16_ERR_ARG",
+    "W4A16_PATH_AUTO", "W4A16_PATH_DECODE", "W4A16_PATH_PREFILL",
+    "w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
+    "w4a16_layout_version",
+]
+
+W4A16_OK = 0
+W4A16_ERR_NULL = -1
+W4A16_ERR_SHAPE = -2
+W4A16_ERR_ALIGN = -3
+W4A16_ERR_RANGE = -4
+W4A16_ERR_HIP = -5
+W4A16_ERR_WORKSPACE = -6
+W4A16_ERR_ARG = -7
+W4A16_PATH_AUTO = 0
+W4A16_PATH_DECODE = 1
+W4A16_PATH_PREFILL = 2
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded C library (ctypes.CDLL). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it with `python -m w4a16_mixed_precision_amd.build`")
+    L = ctypes.CDLL(library_path)
+    P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    L.w4a16_packed_bytes.argtypes = [I64, I64, I64]
+    L.w4a16_packed_bytes.restype = SZ
+    L.w4a16_pack.argtypes = [P, P, P, I64, I64, I64, P, P]
+    L.w4a16_pack.restype = I
+    L.w4a16_unpack.argtypes = [P, I64, I64, I64, P, P, P, P]
+    L.w4a16_unpack.restype = I
+    L.w4a16_workspace_bytes.argtypes = [I64, I64, I64, I64, I, I]
+    L.w4a16_workspace_bytes.restype = SZ
+    L.w4a16_gemm.argtypes = [P, P, I64, I64, I64, I64, P, P]
+    L.w4a16_gemm.restype = I
+    L.w4a16_gemm_ex.argtypes = [P, P, I64, I64, I64, I64, P, P, SZ, I, I, P]
+    L.w4a16_gemm_ex.restype = I
+    L.w4a16_status_string.argtypes = [I]
+    L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_last_error.argtypes = []
+    L.w4a16_last_error.restype = ctypes.c_char_p
+    L.w4a16_layout_version.argtypes = []
+    L.w4a16_layout_version.restype = I
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, lib().w4a16_last_error().decode() or
+                         lib().w4a16_status_string(rc).decode())
+
+
+def _dev_ptr(t, dtype, name):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def w4a16_status_string(status: int) -> str:
+    return lib().w4a16_status_string(int(status)).decode()
+
+
+def w4a16_last_error() -> str:
+    return lib().w4a16_last_error().decode()
+
+
+def w4a16_layout_version() -> int:
+    return int(lib().w4a16_layout_version())
+
+
+def w4a16_packed_bytes(K: int, N: int, G: int) -> int:
+    return int(lib().w4a16_packed_bytes(K, N, G))
+
+
+def w4a16_workspace_bytes(M: int, N: int, K: int, G: int, path: int = W4A16_PATH_AUTO,
+                          splits: int = 0) -> int:
+    return int(lib().w4a16_workspace_bytes(M, N, K, G, path, splits))
+
+
+def w4a16_pack(q, zeros, scales, G: int, packed=None, stream=None):
+    """Pack uint8 q [K][N], uint8 zeros [K/G][N], fp16 scales [K/G][N] (device
+    tensors) into a uint8 device tensor of w4a16_packed_bytes(K, N, G) bytes."""
+    import torch
+    K, N = q.shape
+    nbytes = w4a16_packed_bytes(K, N, G)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if zeros.shape != (K // G, N) or scales.shape != (K // G, N):
+        raise ValueError("zeros and scales must be [K/G][N]")
+    _check(lib().w4a16_pack(_dev_ptr(q, torch.uint8, "q"), _dev_ptr(zeros, torch.uint8, "zeros"),
+                            _dev_ptr(scales, torch.float16, "scales"), K, N, G,
+                            _dev_ptr(packed, torch.uint8, "packed"), _stream(stream, q.device)))
+    return packed
+
+
+def w4a16_unpack(packed, K: int, N: int, G: int, stream=None):
+    """Inverse of w4a16_pack: (q, zeros, scales) device tensors."""
+    import torch
+    dev = packed.device
+    q = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    z = torch.empty((K // G, N), dtype=torch.uint8, device=dev)
+    s = torch.empty((K // G, N), dtype=torch.float16, device=dev)
+    _check(lib().w4a16_unpack(_dev_ptr(packed, torch.uint8, "packed"), K, N, G, q.data_ptr(),
+                              z.data_ptr(), s.data_ptr(), _stream(stream, dev)))
+    return q, z, s
+
+
+def w4a16_gemm(X, packed, N: int, K: int, G: int, Y=None, stream=None):
+    """Y[M][N] (fp16) = X[M][K] (fp16) . dequant(packed). Asynchronous."""
+    import torch
+    M = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [M][K]")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    elif tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [M][N]")
+    _check(lib().w4a16_gemm(_dev_ptr(X, torch.float16, "X"), _dev_ptr(packed, torch.uint8, "packed"),
+                            M, N, K, G, _dev_ptr(Y, torch.float16, "Y"), _stream(stream, X.device)))
+    return Y
+
+
+def w4a16_gemm_ex(X, packed, N: int, K: int, G: int, Y=None, workspace=None,
+                  path: int = W4A16_PATH_AUTO, splits: int = 0, stream=None):
+    """w4a16_gemm with an explicit plan and caller-owned workspace (a zeroed
+    uint8 device tensor of at least w4a16_workspace_bytes(...) bytes)."""
+    import torch
+    M = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [M][K]")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    elif tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [M][N]")
+    ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().w4a16_gemm_ex(_dev_ptr(X, torch.float16, "X"), _dev_ptr(packed, torch.uint8, "packed"),
+                               M, N, K, G, _dev_ptr(Y, torch.float16, "Y"), ws_ptr, ws_bytes,
+                               path, splits, _stream(stream, X.device)))
+    return Y

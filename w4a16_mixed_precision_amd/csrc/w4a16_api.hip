@@ -1,0 +1,294 @@
+// C ABI of the W4A16 library: argument validation, plan selection and the
+// per-device state (a small status word for pack, the lazily grown split-K
+// workspace of w4a16_gemm). The declarations and their contract are in
+// include/w4a16.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/w4a16.h"
+#include "w4a16_device.h"
+#include "w4a16_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int fail_hip(hipError_t e, const char *what) {
+    return fail(W4A16_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool shape_ok(int64_t K, int64_t N, int64_t G) {
+    if (K <= 0 || N <= 0 || K > kMaxDim || N > kMaxDim) return false;
+    if (K % 128 != 0 || N % 16 != 0) return false;
+    if (G != 32 && G != 64 && G != 128 && G != 256) return false;
+    return K % G == 0;
+}
+
+int check_shape(int64_t K, int64_t N, int64_t G) {
+    if (!shape_ok(K, N, G))
+        return fail(W4A16_ERR_SHAPE,
+                    "unsupported shape K=%lld N=%lld G=%lld (need K%%128==0, N%%16==0, "
+                    "G in {32,64,128,256}, K%%G==0)",
+                    (long long)K, (long long)N, (long long)G);
+    return W4A16_OK;
+}
+
+// ------------------------------------------------------------- device state
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    std::mutex mu;
+    int num_cus = 0;
+    int *flag = nullptr;       // pack range-error word
+    void *ws = nullptr;        // w4a16_gemm split-K workspace
+    size_t ws_bytes = 0;
+};
+
+DeviceState g_dev[kMaxDevices];
+
+int current_device(int *dev) {
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (*dev < 0 || *dev >= kMaxDevices) return fail(W4A16_ERR_HIP, "device index %d out of range", *dev);
+    return W4A16_OK;
+}
+
+int device_cus(int dev, int *cus) {
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lk(d.mu);
+    if (d.num_cus == 0) {
+        int v = 0;
+        hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute");
+        d.num_cus = v > 0 ? v : 1;
+    }
+    *cus = d.num_cus;
+    return W4A16_OK;
+}
+
+int device_flag(int dev, int **flag) {
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lk(d.mu);
+    if (!d.flag) {
+        hipError_t e = hipMalloc((void **)&d.flag, 256);
+        if (e != hipSuccess) return fail_hip(e, "hipMalloc(status word)");
+    }
+    *flag = d.flag;
+    return W4A16_OK;
+}
+
+// Grows the per-device workspace to `bytes` (zero-filled on `stream`).
+int device_workspace(int dev, size_t bytes, hipStream_t stream, void **ws) {
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lk(d.mu);
+    if (d.ws_bytes < bytes) {
+        if (d.ws) {
+            hipError_t e = hipFree(d.ws);  // synchronizes the device
+            if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
+            d.ws = nullptr;
+            d.ws_bytes = 0;
+        }
+        size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+        hipError_t e = hipMalloc(&d.ws, want);
+        if (e != hipSuccess) return fail_hip(e, "hipMalloc(workspace)");
+        e = hipMemsetAsync(d.ws, 0, want, stream);
+        if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync(workspace)");
+        d.ws_bytes = want;
+    }
+    *ws = d.ws;
+    return W4A16_OK;
+}
+
+// ------------------------------------------------------------- planning
+struct Plan {
+    int path;
+    int splits;
+};
+
+int make_plan(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits, int num_cus, Plan *p) {
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_DECODE && path != W4A16_PATH_PREFILL)
+        return fail(W4A16_ERR_ARG, "path %d is not one of W4A16_PATH_*", path);
+    if (path == W4A16_PATH_AUTO) path = M <= 32 ? W4A16_PATH_DECODE : W4A16_PATH_PREFILL;
+    if (path == W4A16_PATH_DECODE) {
+        if (M > w4a16::kDecodeMaxM)
+            return fail(W4A16_ERR_ARG, "decode path needs M <= %d (M=%lld)", w4a16::kDecodeMaxM, (long long)M);
+        const int maxs = w4a16::decode_max_splits((int)M, (int)N, (int)K);
+        if (splits < 0 || splits > maxs)
+            return fail(W4A16_ERR_ARG, "splits=%d outside 0..%d", splits, maxs);
+        if (splits == 0) splits = w4a16::decode_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus);
+    } else {
+        if (splits > 1 || splits < 0)
+            return fail(W4A16_ERR_ARG, "prefill path takes splits 0 or 1 (got %d)", splits);
+        splits = 1;
+    }
+    p->path = path;
+    p->splits = splits;
+    return W4A16_OK;
+}
+
+size_t plan_workspace(const Plan &p, int64_t M, int64_t N, int64_t K, int64_t G) {
+    if (p.path == W4A16_PATH_DECODE)
+        return w4a16::decode_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits);
+    return 0;
+}
+
+int check_gemm_args(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
+                    int64_t G, uint16_t *Y) {
+    if (!X || !packed || !Y) return fail(W4A16_ERR_NULL, "X, packed and Y must be non-NULL");
+    if (M < 1 || M > kMaxDim) return fail(W4A16_ERR_SHAPE, "M=%lld out of range", (long long)M);
+    int rc = check_shape(K, N, G);
+    if (rc) return rc;
+    if (!aligned16(X) || !aligned16(packed) || !aligned16(Y))
+        return fail(W4A16_ERR_ALIGN, "X, packed and Y must be 16-byte aligned");
+    return W4A16_OK;
+}
+
+int launch(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
+           uint16_t *Y, void *ws, const Plan &p, hipStream_t stream) {
+    hipError_t e;
+    if (p.path == W4A16_PATH_DECODE)
+        e = w4a16::launch_decode(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, ws,
+                                 p.splits, stream);
+    else
+        e = w4a16::launch_prefill(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, stream);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t G) {
+    if (!shape_ok(K, N, G)) return 0;
+    return w4a16::weight_bytes(K, N) + w4a16::scale_bytes(K, N, G) + w4a16::zero_bytes(K, N, G);
+}
+
+int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales, int64_t K, int64_t N,
+               int64_t G, void *packed, void *stream) {
+    if (!q || !zeros || !scales || !packed)
+        return fail(W4A16_ERR_NULL, "q, zeros, scales and packed must be non-NULL");
+    int rc = check_shape(K, N, G);
+    if (rc) return rc;
+    if (!aligned16(packed)) return fail(W4A16_ERR_ALIGN, "packed must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    int dev;
+    if ((rc = current_device(&dev))) return rc;
+    int *flag;
+    if ((rc = device_flag(dev, &flag))) return rc;
+    hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
+    if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
+    e = w4a16::launch_pack(q, zeros, scales, (int)K, (int)N, (int)G, (uint8_t *)packed, flag, st);
+    if (e != hipSuccess) return fail_hip(e, "pack launch");
+    int host_flag = 0;
+    e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    if (host_flag) return fail(W4A16_ERR_RANGE, "a q or zero code is larger than 15");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
+int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G, uint8_t *q, uint8_t *zeros,
+                 uint16_t *scales, void *stream) {
+    if (!q || !zeros || !scales || !packed)
+        return fail(W4A16_ERR_NULL, "packed, q, zeros and scales must be non-NULL");
+    int rc = check_shape(K, N, G);
+    if (rc) return rc;
+    if (!aligned16(packed)) return fail(W4A16_ERR_ALIGN, "packed must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = w4a16::launch_unpack((const uint8_t *)packed, (int)K, (int)N, (int)G, q, zeros,
+                                        scales, st);
+    if (e != hipSuccess) return fail_hip(e, "unpack launch");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
+size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits) {
+    if (M < 1 || M > kMaxDim || !shape_ok(K, N, G)) return 0;
+    // The automatic split count depends on the device's CU count; size for
+    // the current device when one is available, else for 256 CUs.
+    int cus = 256, dev = 0;
+    if (splits == 0 && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        int v = 0;
+        if (device_cus(dev, &v) == W4A16_OK) cus = v;
+    }
+    Plan p;
+    if (make_plan(M, N, K, G, path, splits, cus, &p) != W4A16_OK) return 0;
+    return plan_workspace(p, M, N, K, G);
+}
+
+int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
+               uint16_t *Y, void *stream) {
+    int rc = check_gemm_args(X, packed, M, N, K, G, Y);
+    if (rc) return rc;
+    int dev, cus;
+    if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
+    Plan p;
+    if ((rc = make_plan(M, N, K, G, W4A16_PATH_AUTO, 0, cus, &p))) return rc;
+    void *ws = nullptr;
+    const size_t need = plan_workspace(p, M, N, K, G);
+    if (need && (rc = device_workspace(dev, need, (hipStream_t)stream, &ws))) return rc;
+    return launch(X, packed, M, N, K, G, Y, ws, p, (hipStream_t)stream);
+}
+
+int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
+                  uint16_t *Y, void *workspace, size_t workspace_bytes, int path, int splits,
+                  void *stream) {
+    int rc = check_gemm_args(X, packed, M, N, K, G, Y);
+    if (rc) return rc;
+    int cus = 256;
+    Plan p;
+    if (splits == 0) {
+        int dev;
+        if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
+    }
+    if ((rc = make_plan(M, N, K, G, path, splits, cus, &p))) return rc;
+    const size_t need = plan_workspace(p, M, N, K, G);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(W4A16_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (need && !aligned16(workspace)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return launch(X, packed, M, N, K, G, Y, workspace, p, (hipStream_t)stream);
+}
+
+const char *w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_NULL: return "null pointer";
+        case W4A16_ERR_SHAPE: return "unsupported shape";
+        case W4A16_ERR_ALIGN: return "misaligned pointer";
+        case W4A16_ERR_RANGE: return "code out of range";
+        case W4A16_ERR_HIP: return "HIP runtime error";
+        case W4A16_ERR_WORKSPACE: return "workspace too small";
+        case W4A16_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+const char *w4a16_last_error(void) { return g_last_error; }
+
+int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Host-side interfaces between the C ABI layer and the kernel launchers.
+// Internal header: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// Offline relayout (pack) and its inverse (unpack). `bad` is a device int set
+// to nonzero by pack when a code is larger than 15.
+hipError_t launch_pack(const uint8_t *q, const uint8_t *z, const uint16_t *s, int K, int N, int G,
+                       uint8_t *packed, int *bad, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t *packed, int K, int N, int G, uint8_t *q, uint8_t *z,
+                         uint16_t *s, hipStream_t stream);
+
+// Decode path (M <= 64): split-K over workgroups, MFMA with M padded to 16.
+constexpr int kDecodeMaxM = 64;
+int decode_auto_splits(int M, int N, int K, int G, int num_cus);
+int decode_max_splits(int M, int N, int K);
+size_t decode_workspace_bytes(int M, int N, int K, int G, int splits);
+hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
+                         uint16_t *Y, void *workspace, int splits, hipStream_t stream);
+
+// Prefill path (any M): LDS-staged activations, MFMA tiles.
+hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
+                          uint16_t *Y, hipStream_t stream);
+
+}  // namespace w4a16
