@@ -31,16 +31,21 @@
  *   - Return value: W4A16_OK (0) or a negative W4A16_ERR_* code;
  *     w4a16_last_error() gives a message for the calling thread.
  *   - Shapes: K % 128 == 0, N % 16 == 0, G in {32, 64, 128, 256} with
- *     K % G == 0, M >= 1. Anything else is W4A16_ERR_SHAPE.
+ *     K % G == 0, 1 <= M <= 2^30, K and N <= 2^24. Anything else is
+ *     W4A16_ERR_SHAPE.
  *
- * Packed layout, version 1 (bytes, little-endian):
+ * Packed layout, version 2 (bytes, little-endian):
  *   [0, K*N/2)            weights. Weight (k, n) lives in the 1024-byte tile
  *                         (n/16)*(K/128) + k/128, in the 32-bit word at byte
- *                         16*(16*((k%32)/8) + n%16) + 4*((k%128)/32) of the
- *                         tile, in nibble slot (k%8)/2 + 4*(k%2). One wave64
- *                         load of 16 bytes per lane reads one whole tile, and
- *                         (word >> 4i) & 0x000F000F yields the codes of k and
- *                         k+1 in the two 16-bit halves.
+ *                         16*(16*((k%32)/8) + n%16) + 4*((k%8)/2) of the tile,
+ *                         in nibble slot 4*(k%2) + 2*(t%2) + t/2 with step
+ *                         t = (k%128)/32. One wave64 load of 16 bytes per
+ *                         lane reads one whole tile; lane l then holds the
+ *                         B-operand codes of column l%16, rows 8*(l/16)..+7,
+ *                         of all four 32-row steps, and the masks 0x000F000F
+ *                         and 0x00F000F0 on a word and on the word shifted
+ *                         right by 8 give the (k, k+1) code pairs of steps
+ *                         0, 2, 1 and 3 in the two 16-bit halves.
  *   next 2*N*(K/G)        fp16 scales, s[g][n] at element ((n/16)*(K/G)+g)*16 + n%16.
  *   next N*(K/G)/2        4-bit zeros, z[g][n] in byte ((n/16)*(K/G)+g)*8 + (n%16)/2,
  *                         low nibble for even n, high nibble for odd n.
@@ -55,7 +60,7 @@
 extern "C" {
 #endif
 
-#define W4A16_LAYOUT_VERSION 1
+#define W4A16_LAYOUT_VERSION 2
 
 #define W4A16_OK 0
 #define W4A16_ERR_NULL (-1)      /* a required pointer is NULL */
@@ -130,9 +135,10 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int pat
  *   splits   0 = automatic; otherwise 1 .. K/128 workgroup splits of K
  *            (decode path only; must be 0 or 1 for prefill)
  *   workspace, workspace_bytes: at least w4a16_workspace_bytes(...) bytes of
- *            device memory, or NULL/0 if that is 0. Its first use must find it
- *            zero-filled; every completed call leaves it in that state again.
- *            Calls sharing one workspace must be ordered (same stream).
+ *            device memory (any contents), or NULL/0 if that is 0. It holds
+ *            the fp32 partial sums of the K splits between the GEMM kernel
+ *            and the reduce kernel, so calls sharing one workspace must be
+ *            ordered (same stream).
  * The result does not depend on `path` or `splits` beyond fp32 rounding
  * order; for a fixed plan it is bitwise reproducible.
  */

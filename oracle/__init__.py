@@ -20,15 +20,18 @@ Contents
   the order in which the matrix instructions consume them; the byte layout
   itself is this library's own, documented below and in ``include/w4a16.h``.
 
-Packed layout, version 1 (K % 128 == 0, N % 16 == 0, G in {32, 64, 128, 256},
+Packed layout, version 2 (K % 128 == 0, N % 16 == 0, G in {32, 64, 128, 256},
 G divides K):
 
 * Weight region, bytes [0, K*N/2): for weight (k, n), strip sn = n // 16 and
   block kb = k // 128 select a 1024-byte tile at offset
   1024 * (sn * (K/128) + kb). Inside it, lane = 16 * ((k % 32) // 8) + n % 16
-  and word t = (k % 128) // 32 select the little-endian 32-bit word at byte
-  16 * lane + 4 * t. Inside the word the code sits in nibble slot
-  (k % 8) // 2 + 4 * (k % 2), bits [4*slot, 4*slot + 4).
+  and word v = (k % 8) // 2 select the little-endian 32-bit word at byte
+  16 * lane + 4 * v. With step t = (k % 128) // 32 and parity e = k % 2, the
+  code sits in nibble slot 4 * e + 2 * (t % 2) + t // 2, bits
+  [4*slot, 4*slot + 4). So one word holds the k pair (2v, 2v+1) of all four
+  32-row steps of the lane, and the masks 0x000F000F / 0x00F000F0 applied to
+  the word and to the word shifted right by 8 give steps 0, 2, 1, 3.
 * Scale region, K*N/2 + [0, 2*N*K/G): fp16 s[g][n] at element
   ((n // 16) * (K/G) + g) * 16 + n % 16.
 * Zero region, following it, N*K/(2G) bytes: z[g][n] in byte
@@ -181,9 +184,10 @@ def _weight_coords(K: int, N: int):
     n = np.arange(N, dtype=np.int64)[None, :]
     tile = (n // 16) * (K // 128) + k // 128
     lane = 16 * ((k % 32) // 8) + n % 16
-    word = (k % 128) // 32
+    word = (k % 8) // 2
     byte = 1024 * tile + 16 * lane + 4 * word
-    slot = (k % 8) // 2 + 4 * (k % 2)
+    step = (k % 128) // 32
+    slot = 4 * (k % 2) + 2 * (step % 2) + step // 2
     return byte, 4 * slot
 
 

@@ -43,7 +43,7 @@ def test_packed_bytes_matches_layout_spec():
 
 
 def test_layout_version():
-    assert w4.w4a16_layout_version() == 1
+    assert w4.w4a16_layout_version() == 2
 
 
 def test_gemm_validation_before_any_hip_call():

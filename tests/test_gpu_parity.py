@@ -160,9 +160,10 @@ def test_results_are_reproducible_and_workspace_is_reusable():
         outs.append(host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=DECODE, splits=4)))
     torch.cuda.synchronize()
     assert all(np.array_equal(o.view(np.uint16), outs[0].view(np.uint16)) for o in outs)
-    # counters are back to zero after every call
-    tiles = (N // 16 + 3) // 4
-    assert int(ws[: 4 * tiles].view(torch.int32).abs().sum().item()) == 0
+    # a workspace full of garbage gives the same result
+    ws.fill_(0xFF)
+    again = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=DECODE, splits=4))
+    assert np.array_equal(again.view(np.uint16), outs[0].view(np.uint16))
     a = host(w4.w4a16_gemm_ex(X, packed, N, K, G, path=PREFILL))
     b = host(w4.w4a16_gemm_ex(X, packed, N, K, G, path=PREFILL))
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

@@ -67,10 +67,13 @@ def test_each_tile_holds_one_128_by_16_block():
             assert np.all(tiles[sn, kb] == v | (v << 4))
 
 
-def test_word_shift_mask_gives_consecutive_k_pairs():
-    # For lane l and word t of a tile, (w >> 4i) & 0x000F000F carries
-    # (k, k+1) = (128 kb + 32 t + 8 (l // 16) + 2 i, +1) of column 16 sn + l % 16
-    # in its low and high 16-bit halves.
+def test_word_masks_give_consecutive_k_pairs_of_each_step():
+    # For lane l and word v of a tile, with w the word and w8 = w >> 8:
+    #   w  & 0x000F000F -> codes of (k, k+1) of step 0,
+    #   w8 & 0x000F000F -> step 1,
+    #   w  & 0x00F000F0 -> step 2 (times 16),
+    #   w8 & 0x00F000F0 -> step 3 (times 16),
+    # where k = 128 kb + 32 t + 8 (l // 16) + 2 v, column 16 sn + l % 16.
     K, N, G = 256, 32, 128
     q, z, s = _rand(K, N, G, seed=9)
     buf = oracle.layout_pack(q, z, s, G)
@@ -79,13 +82,15 @@ def test_word_shift_mask_gives_consecutive_k_pairs():
         for kb in range(K // 128):
             for lane in range(64):
                 n = 16 * sn + lane % 16
-                for t in range(4):
-                    w = int(words[sn, kb, lane, t])
-                    for i in range(4):
-                        k = 128 * kb + 32 * t + 8 * (lane // 16) + 2 * i
-                        pair = (w >> (4 * i)) & 0x000F000F
-                        assert pair & 0xFFFF == q[k, n]
-                        assert pair >> 16 == q[k + 1, n]
+                for v in range(4):
+                    w = int(words[sn, kb, lane, v])
+                    w8 = w >> 8
+                    got = {0: w & 0x000F000F, 1: w8 & 0x000F000F,
+                           2: (w & 0x00F000F0) >> 4, 3: (w8 & 0x00F000F0) >> 4}
+                    for t in range(4):
+                        k = 128 * kb + 32 * t + 8 * (lane // 16) + 2 * v
+                        assert got[t] & 0xFFFF == q[k, n]
+                        assert got[t] >> 16 == q[k + 1, n]
 
 
 def test_scale_and_zero_records():

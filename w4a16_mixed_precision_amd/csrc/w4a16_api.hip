@@ -32,10 +32,11 @@ int fail_hip(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // M
+constexpr int64_t kMaxKN = (int64_t)1 << 24;   // K and N (32-bit buffer offsets)
 
 bool shape_ok(int64_t K, int64_t N, int64_t G) {
-    if (K <= 0 || N <= 0 || K > kMaxDim || N > kMaxDim) return false;
+    if (K <= 0 || N <= 0 || K > kMaxKN || N > kMaxKN) return false;
     if (K % 128 != 0 || N % 16 != 0) return false;
     if (G != 32 && G != 64 && G != 128 && G != 256) return false;
     return K % G == 0;
@@ -94,8 +95,8 @@ int device_flag(int dev, int **flag) {
     return W4A16_OK;
 }
 
-// Grows the per-device workspace to `bytes` (zero-filled on `stream`).
-int device_workspace(int dev, size_t bytes, hipStream_t stream, void **ws) {
+// Grows the per-device split-K workspace to at least `bytes`.
+int device_workspace(int dev, size_t bytes, void **ws) {
     DeviceState &d = g_dev[dev];
     std::lock_guard<std::mutex> lk(d.mu);
     if (d.ws_bytes < bytes) {
@@ -108,8 +109,6 @@ int device_workspace(int dev, size_t bytes, hipStream_t stream, void **ws) {
         size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
         hipError_t e = hipMalloc(&d.ws, want);
         if (e != hipSuccess) return fail_hip(e, "hipMalloc(workspace)");
-        e = hipMemsetAsync(d.ws, 0, want, stream);
-        if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync(workspace)");
         d.ws_bytes = want;
     }
     *ws = d.ws;
@@ -161,11 +160,11 @@ int check_gemm_args(const uint16_t *X, const void *packed, int64_t M, int64_t N,
 }
 
 int launch(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
-           uint16_t *Y, void *ws, const Plan &p, hipStream_t stream) {
+           uint16_t *Y, void *ws, const Plan &p, int num_cus, hipStream_t stream) {
     hipError_t e;
     if (p.path == W4A16_PATH_DECODE)
         e = w4a16::launch_decode(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, ws,
-                                 p.splits, stream);
+                                 p.splits, num_cus, stream);
     else
         e = w4a16::launch_prefill(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
@@ -249,8 +248,8 @@ int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int6
     if ((rc = make_plan(M, N, K, G, W4A16_PATH_AUTO, 0, cus, &p))) return rc;
     void *ws = nullptr;
     const size_t need = plan_workspace(p, M, N, K, G);
-    if (need && (rc = device_workspace(dev, need, (hipStream_t)stream, &ws))) return rc;
-    return launch(X, packed, M, N, K, G, Y, ws, p, (hipStream_t)stream);
+    if (need && (rc = device_workspace(dev, need, &ws))) return rc;
+    return launch(X, packed, M, N, K, G, Y, ws, p, cus, (hipStream_t)stream);
 }
 
 int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
@@ -258,19 +257,24 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
                   void *stream) {
     int rc = check_gemm_args(X, packed, M, N, K, G, Y);
     if (rc) return rc;
-    int cus = 256;
+    // Plan and workspace checks first: they need no device.
     Plan p;
-    if (splits == 0) {
-        int dev;
-        if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
+    if (splits != 0) {
+        if ((rc = make_plan(M, N, K, G, path, splits, 256, &p))) return rc;
+        const size_t need = plan_workspace(p, M, N, K, G);
+        if (need && (!workspace || workspace_bytes < need))
+            return fail(W4A16_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need,
+                        workspace ? workspace_bytes : (size_t)0);
     }
+    int dev, cus;
+    if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
     if ((rc = make_plan(M, N, K, G, path, splits, cus, &p))) return rc;
     const size_t need = plan_workspace(p, M, N, K, G);
     if (need && (!workspace || workspace_bytes < need))
         return fail(W4A16_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);
     if (need && !aligned16(workspace)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
-    return launch(X, packed, M, N, K, G, Y, workspace, p, (hipStream_t)stream);
+    return launch(X, packed, M, N, K, G, Y, workspace, p, cus, (hipStream_t)stream);
 }
 
 const char *w4a16_status_string(int status) {

@@ -46,10 +46,15 @@ __device__ inline uint32_t load_scale_zero(const PackedView &pv, size_t rec, int
     return sc | (zc << 16);
 }
 
-// -(1024 + z) as an fp16 pair: 1024 + z is exponent 10 with z in the low
-// mantissa bits (0x6400 | z); the sign bit makes it negative.
+// -(1024 + z) and -(1024 + 16 z) as fp16 pairs: 1024 + z is exponent 10
+// with z in the low mantissa bits (0x6400 | z), 1024 + 16 z puts z four bits
+// higher; the sign bit makes them negative.
 __device__ inline uint32_t neg_bias_pair(uint32_t sz) {
     uint32_t h = 0xE400u | (sz >> 16);
+    return h | (h << 16);
+}
+__device__ inline uint32_t neg_bias16_pair(uint32_t sz) {
+    uint32_t h = 0xE400u | ((sz >> 16) << 4);
     return h | (h << 16);
 }
 
@@ -57,45 +62,85 @@ __device__ inline float scale_of(uint32_t sz) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
 }
 
-// Eight 4-bit codes of one packed word -> four fp16 pairs holding 1024 + q.
-// Setting the exponent field of a half to 10 (0x6400) and OR-ing the code
-// into the low mantissa bits gives exactly 1024 + q without any
-// integer-to-float conversion instruction. Nibble slots are ordered so that
-// shift i and the mask 0x000F000F yield the codes of k = 2i and 2i + 1.
-__device__ inline void biased_halves(uint32_t w, uint32_t h[4]) {
-    h[0] = (w & 0x000F000Fu) | 0x64006400u;
-    h[1] = ((w >> 4) & 0x000F000Fu) | 0x64006400u;
-    h[2] = ((w >> 8) & 0x000F000Fu) | 0x64006400u;
-    h[3] = ((w >> 12) & 0x000F000Fu) | 0x64006400u;
+// (x & mask) | magic in one VALU op. gfx9 VOP3 reads at most one scalar
+// operand, so the mask goes in an SGPR and the magic number in a VGPR.
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+    return r;
 }
+
+// Exponent-OR conversion: a half with exponent field 10 (0x6400) and a code
+// c in its low mantissa bits is exactly 1024 + c, so OR-ing the code into
+// 0x6400 converts it to fp16 without an integer-to-float instruction. Codes
+// sitting four bits higher give 1024 + 16 c, also exact.
+constexpr uint32_t kMagic = 0x64006400u;
+constexpr uint32_t kLoMask = 0x000F000Fu;
+constexpr uint32_t kHiMask = 0x00F000F0u;
 
 __device__ inline half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
-__device__ inline uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 
-// B operand (8 halves) of exact integers q - z for one packed word:
-// (1024 + q) - (1024 + z) is exact in fp16 (both in [1024, 1040)).
-__device__ inline half8 dequant_qz(uint32_t w, uint32_t nb2) {
-    uint32_t h[4];
-    biased_halves(w, h);
-    half2v nb = as_h2(nb2);
-    half2v r0 = as_h2(h[0]) + nb, r1 = as_h2(h[1]) + nb, r2 = as_h2(h[2]) + nb, r3 = as_h2(h[3]) + nb;
+__device__ inline half8 pack_h8(half2v r0, half2v r1, half2v r2, half2v r3) {
     half8 out;
     out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
     out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];
     return out;
 }
 
-// B operand of fp16 weights (q - z) * s, rounded once to nearest-even.
-__device__ inline half8 dequant_w(uint32_t w, uint32_t nb2, uint32_t s2) {
-    uint32_t h[4];
-    biased_halves(w, h);
-    half2v nb = as_h2(nb2), sc = as_h2(s2);
-    half2v r0 = (as_h2(h[0]) + nb) * sc, r1 = (as_h2(h[1]) + nb) * sc;
-    half2v r2 = (as_h2(h[2]) + nb) * sc, r3 = (as_h2(h[3]) + nb) * sc;
-    half8 out;
-    out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
-    out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];
-    return out;
+// One lane's 16-byte slice of a packed tile holds four words; word v carries
+// the k pair (2v, 2v+1) of each of the four 32-row steps of the tile: steps
+// 0 and 1 in the low nibble of bytes 0/2 and 1/3, steps 2 and 3 in their high
+// nibble (see the layout in include/w4a16.h).
+//
+// B operand of exact integers for step T: (q - z) for T = 0, 1 and 16 (q - z)
+// for T = 2, 3 (the caller folds the 1/16 into the scale). (1024 + q) -
+// (1024 + z) and (1024 + 16 q) - (1024 + 16 z) are exact in fp16 (all
+// operands in [1024, 1264]). w8[v] = w[v] >> 8, computed once per word.
+template <int T>
+__device__ inline half8 dequant_qz_step(const u32x4 &w, const u32x4 &w8, uint32_t nb_lo,
+                                        uint32_t nb_hi, uint32_t magic) {
+    const uint32_t mask = (T < 2) ? kLoMask : kHiMask;
+    const uint32_t nb = (T < 2) ? nb_lo : nb_hi;
+    half2v r[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const uint32_t src = (T & 1) ? w8[v] : w[v];
+        r[v] = as_h2(and_or(src, mask, magic)) + as_h2(nb);
+    }
+    return pack_h8(r[0], r[1], r[2], r[3]);
+}
+
+// B operand of fp16 weights for step T: ((1024 + q) - (1024 + z)) * s, the
+// exact q - z rounded once to fp16 by the multiply with s.
+template <int T>
+__device__ inline half8 dequant_w_step(const u32x4 &w, uint32_t nb_lo, uint32_t s2, uint32_t magic) {
+    constexpr int shift = T == 0 ? 0 : (T == 1 ? 8 : (T == 2 ? 4 : 12));
+    half2v r[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const uint32_t src = shift ? (w[v] >> shift) : w[v];
+        r[v] = (as_h2(and_or(src, kLoMask, magic)) + as_h2(nb_lo)) * as_h2(s2);
+    }
+    return pack_h8(r[0], r[1], r[2], r[3]);
+}
+
+// Runtime-step dispatch for code that loops over steps.
+__device__ inline half8 dequant_w(int t, const u32x4 &w, uint32_t nb_lo, uint32_t s2, uint32_t magic) {
+    switch (t) {
+        case 0: return dequant_w_step<0>(w, nb_lo, s2, magic);
+        case 1: return dequant_w_step<1>(w, nb_lo, s2, magic);
+        case 2: return dequant_w_step<2>(w, nb_lo, s2, magic);
+        default: return dequant_w_step<3>(w, nb_lo, s2, magic);
+    }
+}
+__device__ inline half8 dequant_qz(int t, const u32x4 &w, const u32x4 &w8, uint32_t nb_lo,
+                                   uint32_t nb_hi, uint32_t magic) {
+    switch (t) {
+        case 0: return dequant_qz_step<0>(w, w8, nb_lo, nb_hi, magic);
+        case 1: return dequant_qz_step<1>(w, w8, nb_lo, nb_hi, magic);
+        case 2: return dequant_qz_step<2>(w, w8, nb_lo, nb_hi, magic);
+        default: return dequant_qz_step<3>(w, w8, nb_lo, nb_hi, magic);
+    }
 }
 
 // D += A . B on a 16 x 16 output tile with K = 32 (fp16 in, fp32 accumulate).
@@ -107,6 +152,12 @@ __device__ inline floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
 
 __device__ inline uint16_t f32_to_f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
+// descriptor: stride 0, 32-bit data format word).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 }  // namespace w4a16

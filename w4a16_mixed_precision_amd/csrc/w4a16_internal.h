@@ -15,13 +15,15 @@ hipError_t launch_pack(const uint8_t *q, const uint8_t *z, const uint16_t *s, in
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int G, uint8_t *q, uint8_t *z,
                          uint16_t *s, hipStream_t stream);
 
-// Decode path (M <= 64): split-K over workgroups, MFMA with M padded to 16.
+// Decode path (M <= 64): one 16-column strip per workgroup, waves split K,
+// MFMA with M padded to 16; optional split of K across workgroups (narrow N)
+// with fp32 partials in a workspace and a second reduce kernel.
 constexpr int kDecodeMaxM = 64;
 int decode_auto_splits(int M, int N, int K, int G, int num_cus);
 int decode_max_splits(int M, int N, int K);
 size_t decode_workspace_bytes(int M, int N, int K, int G, int splits);
 hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
-                         uint16_t *Y, void *workspace, int splits, hipStream_t stream);
+                         uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 
 // Prefill path (any M): LDS-staged activations, MFMA tiles.
 hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,

@@ -17,8 +17,12 @@
 namespace w4a16 {
 namespace {
 
-// k offset (within 8) stored in nibble slot j of a packed word.
-__device__ inline int slot_k(int j) { return (j & 3) * 2 + (j >> 2); }
+// Nibble slot j of word v in a lane's 16 bytes holds k offset
+// 32 * step(j) + 2 * v + (j >> 2) from the lane's first row, where the slot
+// order (steps 0, 2, 1, 3 in the low and high 16-bit halves) lets one shift
+// by 8 plus two masks expose all four 32-row steps of a word.
+__device__ inline int slot_step(int j) { return 2 * (j & 1) + ((j >> 1) & 1); }
+__device__ inline int slot_k(int v, int j) { return 32 * slot_step(j) + 2 * v + (j >> 2); }
 
 __global__ void __launch_bounds__(256)
 pack_weights_kernel(const uint8_t *__restrict__ q, int K, int N, u32x4 *__restrict__ out,
@@ -36,16 +40,16 @@ pack_weights_kernel(const uint8_t *__restrict__ q, int K, int N, u32x4 *__restri
         u32x4 v;
         uint32_t over = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int w = 0; w < 4; ++w) {
             uint32_t word = 0;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int k = kbase + 32 * t + slot_k(j);
+                const int k = kbase + slot_k(w, j);
                 const uint32_t c = q[(int64_t)k * N + n];
                 over |= c;
                 word |= (c & 15u) << (4 * j);
             }
-            v[t] = word;
+            v[w] = word;
         }
         out[idx] = v;
         if (over > 15u) atomicOr(bad, 1);
@@ -88,11 +92,11 @@ unpack_weights_kernel(const u32x4 *__restrict__ in, int K, int N, uint8_t *__res
         const int kbase = blk * kBlockK + 8 * (lane >> 4);
         const u32x4 v = in[idx];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int w = 0; w < 4; ++w) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int k = kbase + 32 * t + slot_k(j);
-                q[(int64_t)k * N + n] = (uint8_t)((v[t] >> (4 * j)) & 15u);
+                const int k = kbase + slot_k(w, j);
+                q[(int64_t)k * N + n] = (uint8_t)((v[w] >> (4 * j)) & 15u);
             }
         }
     }

@@ -56,6 +56,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     const int m0 = tm * BM;
     const int strip_w = tn * 4 * NSW + wave * NSW;  // first strip of this wave
     const PackedView pv = packed_view(packed, K, N, 32 * GS);
+    const uint32_t magic = kMagic;
 
     // Global source of this thread's X chunks (row clamped into [0, M)).
     const uint16_t *xsrc[XLOADS];
@@ -121,7 +122,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
             for (int j = 0; j < NSW; ++j) {
                 const uint32_t sz = szc[f][j];
                 const uint32_t s2 = (sz & 0xFFFFu) | (sz << 16);
-                bw[j] = dequant_w(wc[j][t], neg_bias_pair(sz), s2);
+                bw[j] = dequant_w(t, wc[j], neg_bias_pair(sz), s2, magic);
             }
             const int chunk = (4 * t + kq) ^ col;
 #pragma unroll
