@@ -31,7 +31,7 @@
  *   - Return value: W4A16_OK (0) or a negative W4A16_ERR_* code;
  *     w4a16_last_error() gives a message for the calling thread.
  *   - Shapes: K % 128 == 0, N % 16 == 0, G in {32, 64, 128, 256} with
- *     K % G == 0, 1 <= M <= 2^30, K and N <= 2^24. Anything else is
+ *     K % G == 0, 1 <= M <= 2^30, K and N <= 2^22. Anything else is
  *     W4A16_ERR_SHAPE.
  *
  * Packed layout, version 2 (bytes, little-endian):
@@ -73,7 +73,7 @@ extern "C" {
 
 /* Execution paths for w4a16_gemm_ex. */
 #define W4A16_PATH_AUTO 0
-#define W4A16_PATH_DECODE 1  /* split-K, HBM-bound; M <= 64 */
+#define W4A16_PATH_DECODE 1  /* weight-streaming, HBM-bound; M <= 64 */
 #define W4A16_PATH_PREFILL 2 /* LDS-tiled MFMA, compute-bound; any M */
 
 /*
@@ -125,7 +125,8 @@ int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int6
 /*
  * Workspace bytes w4a16_gemm_ex needs for this shape and plan (`path` one of
  * W4A16_PATH_*, `splits` 0 = automatic, else the number of K splits across
- * workgroups on the decode path). 0 means the plan needs none. Host-only.
+ * workgroups). 0 means the plan needs none. Host-only apart from reading the
+ * current device's CU count when `splits` is 0.
  */
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits);
 
@@ -133,7 +134,8 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int pat
  * w4a16_gemm with an explicit plan and a caller-owned workspace.
  *   path     W4A16_PATH_AUTO / _DECODE / _PREFILL (decode requires M <= 64)
  *   splits   0 = automatic; otherwise 1 .. K/128 workgroup splits of K
- *            (decode path only; must be 0 or 1 for prefill)
+ *            (rounded to whole quantization groups per split, and raised
+ *            where the decode path's on-chip staging needs it)
  *   workspace, workspace_bytes: at least w4a16_workspace_bytes(...) bytes of
  *            device memory (any contents), or NULL/0 if that is 0. It holds
  *            the fp32 partial sums of the K splits between the GEMM kernel

@@ -66,8 +66,8 @@ def test_gemm_ex_plan_and_workspace_validation():
     assert L.w4a16_gemm_ex(FAKE, FAKE, 65, 256, 256, 128, FAKE, None, 0, 1, 1, None) == w4.W4A16_ERR_ARG
     # more splits than 128-row blocks
     assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 1, 3, None) == w4.W4A16_ERR_ARG
-    # prefill does not split
-    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 2, 2, None) == w4.W4A16_ERR_ARG
+    # negative split counts
+    assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 2, -1, None) == w4.W4A16_ERR_ARG
     # a split plan without (enough) workspace
     assert L.w4a16_gemm_ex(FAKE, FAKE, 4, 256, 256, 128, FAKE, None, 0, 1, 2, None) == w4.W4A16_ERR_WORKSPACE
     need = w4.w4a16_workspace_bytes(4, 256, 256, 128, w4.W4A16_PATH_DECODE, 2)
@@ -76,6 +76,7 @@ def test_gemm_ex_plan_and_workspace_validation():
     # unsplit plans need none
     assert w4.w4a16_workspace_bytes(4, 256, 256, 128, w4.W4A16_PATH_DECODE, 1) == 0
     assert w4.w4a16_workspace_bytes(4, 256, 256, 128, w4.W4A16_PATH_PREFILL, 1) == 0
+    assert w4.w4a16_workspace_bytes(512, 8192, 8192, 64, w4.W4A16_PATH_PREFILL, 4) == 4 * 512 * 8192 * 4
     # split workspace covers S * M * N fp32 partials plus counters
     assert w4.w4a16_workspace_bytes(16, 4096, 14336, 128, w4.W4A16_PATH_DECODE, 8) >= 8 * 16 * 4096 * 4
 

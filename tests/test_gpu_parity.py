@@ -116,10 +116,13 @@ SMALL = [
     (33, 1024, 208, 256, DECODE, 7),
     (64, 1024, 512, 128, DECODE, 1),
     (64, 1024, 512, 128, PREFILL, 1),
+    (64, 1024, 512, 128, PREFILL, 3),
     (65, 1024, 528, 128, 0, 0),
     (100, 640, 336, 64, PREFILL, 1),
     (257, 1024, 1088, 128, 0, 0),
     (300, 512, 256, 32, PREFILL, 1),
+    (300, 1152, 256, 64, PREFILL, 0),
+    (517, 2304, 784, 256, PREFILL, 2),
     (513, 768, 320, 256, 0, 0),
     (1, 29568, 64, 64, DECODE, 0),
     (40, 29568, 64, 64, 0, 0),
@@ -164,9 +167,12 @@ def test_results_are_reproducible_and_workspace_is_reusable():
     ws.fill_(0xFF)
     again = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=DECODE, splits=4))
     assert np.array_equal(again.view(np.uint16), outs[0].view(np.uint16))
-    a = host(w4.w4a16_gemm_ex(X, packed, N, K, G, path=PREFILL))
-    b = host(w4.w4a16_gemm_ex(X, packed, N, K, G, path=PREFILL))
-    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    for splits in (1, 3):
+        nbytes = w4.w4a16_workspace_bytes(M, N, K, G, PREFILL, splits)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        a = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=PREFILL, splits=splits))
+        b = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=PREFILL, splits=splits))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
 def test_non_default_stream():
@@ -179,7 +185,7 @@ def test_non_default_stream():
     with torch.cuda.stream(st):
         Xd = dev(X)
         Y = w4.w4a16_gemm(Xd, packed, N, K, G, stream=st)
-        Y2 = w4.w4a16_gemm_ex(dev(np.repeat(X, 9, 0)), packed, N, K, G, stream=st)
+        Y2 = w4.w4a16_gemm(dev(np.repeat(X, 9, 0)), packed, N, K, G, stream=st)
     st.synchronize()
     assert_parity(host(Y), oracle.gemm(X, q, z, s, G), "side stream decode")
     assert_parity(host(Y2), oracle.gemm(np.repeat(X, 9, 0), q, z, s, G), "side stream prefill")

@@ -5,6 +5,7 @@ library lands next to this file, so it travels with the source tree.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -41,6 +42,11 @@ def build_library(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+    # every kernel's host launch stub must resolve: load the library once
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as exc:
+        raise RuntimeError(f"built library does not load: {exc}") from exc
     os.replace(tmp, LIB)
     return LIB
 

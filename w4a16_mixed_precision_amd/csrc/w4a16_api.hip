@@ -33,7 +33,7 @@ int fail_hip(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // M
-constexpr int64_t kMaxKN = (int64_t)1 << 24;   // K and N (32-bit buffer offsets)
+constexpr int64_t kMaxKN = (int64_t)1 << 22;   // K and N (32-bit buffer offsets)
 
 bool shape_ok(int64_t K, int64_t N, int64_t G) {
     if (K <= 0 || N <= 0 || K > kMaxKN || N > kMaxKN) return false;
@@ -125,18 +125,14 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits, 
     if (path != W4A16_PATH_AUTO && path != W4A16_PATH_DECODE && path != W4A16_PATH_PREFILL)
         return fail(W4A16_ERR_ARG, "path %d is not one of W4A16_PATH_*", path);
     if (path == W4A16_PATH_AUTO) path = M <= 32 ? W4A16_PATH_DECODE : W4A16_PATH_PREFILL;
-    if (path == W4A16_PATH_DECODE) {
-        if (M > w4a16::kDecodeMaxM)
-            return fail(W4A16_ERR_ARG, "decode path needs M <= %d (M=%lld)", w4a16::kDecodeMaxM, (long long)M);
-        const int maxs = w4a16::decode_max_splits((int)M, (int)N, (int)K);
-        if (splits < 0 || splits > maxs)
-            return fail(W4A16_ERR_ARG, "splits=%d outside 0..%d", splits, maxs);
-        if (splits == 0) splits = w4a16::decode_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus);
-    } else {
-        if (splits > 1 || splits < 0)
-            return fail(W4A16_ERR_ARG, "prefill path takes splits 0 or 1 (got %d)", splits);
-        splits = 1;
-    }
+    if (path == W4A16_PATH_DECODE && M > w4a16::kDecodeMaxM)
+        return fail(W4A16_ERR_ARG, "decode path needs M <= %d (M=%lld)", w4a16::kDecodeMaxM, (long long)M);
+    const int maxs = (int)(K / 128);
+    if (splits < 0 || splits > maxs) return fail(W4A16_ERR_ARG, "splits=%d outside 0..%d", splits, maxs);
+    if (splits == 0)
+        splits = path == W4A16_PATH_DECODE
+                     ? w4a16::decode_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus)
+                     : w4a16::prefill_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus);
     p->path = path;
     p->splits = splits;
     return W4A16_OK;
@@ -145,7 +141,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits, 
 size_t plan_workspace(const Plan &p, int64_t M, int64_t N, int64_t K, int64_t G) {
     if (p.path == W4A16_PATH_DECODE)
         return w4a16::decode_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits);
-    return 0;
+    return w4a16::prefill_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits);
 }
 
 int check_gemm_args(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
@@ -166,7 +162,8 @@ int launch(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t 
         e = w4a16::launch_decode(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, ws,
                                  p.splits, num_cus, stream);
     else
-        e = w4a16::launch_prefill(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, stream);
+        e = w4a16::launch_prefill(X, (const uint8_t *)packed, (int)M, (int)N, (int)K, (int)G, Y, ws,
+                                  p.splits, num_cus, stream);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     g_last_error[0] = 0;
     return W4A16_OK;

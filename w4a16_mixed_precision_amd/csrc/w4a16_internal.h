@@ -25,8 +25,11 @@ size_t decode_workspace_bytes(int M, int N, int K, int G, int splits);
 hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
                          uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 
-// Prefill path (any M): LDS-staged activations, MFMA tiles.
+// Prefill path (any M): LDS-staged activations, MFMA tiles, optional split
+// of K across workgroups (fp32 partials + reduce kernel) for small grids.
+int prefill_auto_splits(int M, int N, int K, int G, int num_cus);
+size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits);
 hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
-                          uint16_t *Y, hipStream_t stream);
+                          uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 
 }  // namespace w4a16

@@ -8,15 +8,16 @@
 // staging, dequantization interleaved with the math, direct matrix-core
 // execution), re-shaped for gfx950:
 //
-// * Workgroup tile BM x (64 NSW): four waves side by side along N, each
-//   owning all BM rows and NSW 16-column strips, so no two waves dequantize
-//   the same weight.
+// * Workgroup tile BM x BN with WM x WN waves; wave (wm, wn) owns MTW 16-row
+//   tiles and NSW 16-column strips. Its accumulators stay in registers for
+//   the whole K loop.
 // * Activations: the BM x 128 tile of X for the next K block is copied
 //   global -> LDS by direct 16-byte loads (no register staging) while the
 //   current block is being multiplied (two LDS stages). Inside a 256-byte
 //   LDS row the sixteen 16-byte chunks are stored XOR-swizzled by the row
 //   index, so the 16 lanes that read one k chunk from 16 consecutive rows hit
-//   16 different bank groups.
+//   16 different bank groups. A operands of the next 32-row step are read
+//   from LDS while the current step's MFMAs run.
 // * Weights: each wave loads its packed tiles straight into registers, one
 //   16-byte load per lane per strip and K block (the packed order is the
 //   operand order, so there is no run-time swizzle), one block ahead.
@@ -24,7 +25,15 @@
 //   Scale): exponent-OR gives 1024 + q, a packed fp16 add of -(1024 + z)
 //   gives q - z exactly, a packed fp16 multiply by s gives the weight
 //   rounded once to fp16. The B operand of every 16 x 16 x 32 MFMA is
-//   produced this way and reused for all BM/16 row tiles.
+//   produced this way and reused for all MTW row tiles of the wave.
+// * Split-K: when the tile grid alone cannot fill the GPU, workgroups also
+//   split K; each writes fp32 partials and a second kernel adds them in
+//   split order (the kernel boundary orders the two; no device-scope fence).
+// * Workgroups are dispatched round-robin over the eight XCDs; tile ids are
+//   remapped so that the workgroups resident on one XCD share rows of X and
+//   columns of W in that XCD's L2.
+#include <stdlib.h>
+
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -33,63 +42,103 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int MTW, int NSW, int GS>
-__global__ void __launch_bounds__(256)
+// Packed weights of one K block for the wave's NSW strips, kept raw until
+// use (combining them right after the load would make the compiler wait on
+// every load in flight, including the next block's prefetch).
+template <int NSW, int NF>
+struct WSet {
+    u32x4 w[NSW];
+    uint32_t sc[NF][NSW];  // fp16 scale bits
+    uint32_t zb[NF][NSW];  // byte holding the zero code
+};
+
+template <int MTW, int NSW, int WM, int WN, int GS, int OCC>
+__global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
-               uint16_t *__restrict__ Y, int M, int N, int K, int tiles_m) {
-    constexpr int BM = 16 * MTW;
+               uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int tiles_m,
+               int tiles_n, int S, int slice_blocks) {
+    constexpr int WAVES = WM * WN;
+    constexpr int THREADS = WAVES * 64;
+    constexpr int BM = WM * MTW * 16;
     constexpr int STAGE = BM * 256;  // BM rows x 128 k x 2 bytes
     constexpr int F = GS < 4 ? GS : 4;
     constexpr int NF = 4 / F;
-    constexpr int XLOADS = BM / 16;  // 16-byte direct loads per thread per stage
+    constexpr int XLOADS = BM * 16 / THREADS;  // 16-byte direct loads per thread per stage
+    static_assert(BM * 16 % THREADS == 0, "X tile must split evenly over the threads");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int nblk = K / kBlockK;
     const int ngrp = K / (32 * GS);
     const int nstrip = N / kStripCols;
-    const int tm = blockIdx.x % tiles_m;
-    const int tn = blockIdx.x / tiles_m;
+
+    // XCD-aware remap: dispatch order id -> logical tile id. Consecutive ids
+    // go to consecutive XCDs, so give each XCD a contiguous run of tiles;
+    // within a run M varies fastest, so neighbours share columns of W.
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
+    const int tm = tile % tiles_m;
+    const int tn = tile / tiles_m;
+    const int split = blockIdx.y;
+    const int bb = split * slice_blocks;
+    const int be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
+
     const int m0 = tm * BM;
-    const int strip_w = tn * 4 * NSW + wave * NSW;  // first strip of this wave
-    const PackedView pv = packed_view(packed, K, N, 32 * GS);
+    const int strip_w = (tn * WN + wn) * NSW;  // first strip of this wave
     const uint32_t magic = kMagic;
 
-    // Global source of this thread's X chunks (row clamped into [0, M)).
-    const uint16_t *xsrc[XLOADS];
+    // X: this thread's chunk i of a stage covers row r0(i) + lane/16 of the
+    // tile, r0(i) = 4 (i WAVES + wave). One buffer per i starts at that row
+    // group and ends at row M, so rows past M read as zeros (their results
+    // are never stored); the per-lane offset is the same for every i.
+    const int rows_here = M - m0 < BM ? M - m0 : BM;
+    __amdgpu_buffer_rsrc_t rx[XLOADS];
 #pragma unroll
     for (int i = 0; i < XLOADS; ++i) {
-        const int f = (i * 4 + wave) * 64 + lane;
-        const int row = f >> 4;
-        const int chunk = (f & 15) ^ (row & 15);
-        int grow = m0 + row;
-        grow = grow < M ? grow : M - 1;
-        xsrc[i] = X + (size_t)grow * K + chunk * 8;
+        const int r0 = 4 * (i * WAVES + wave);
+        const int nrows = rows_here - r0 > 0 ? rows_here - r0 : 0;
+        rx[i] = make_rsrc(X + (size_t)(m0 + (r0 < rows_here ? r0 : 0)) * K, (uint32_t)((size_t)nrows * K * 2));
     }
+    const int xrow = lane >> 4;
+    const uint32_t xoff = (uint32_t)(xrow * K * 2 + (((lane & 15) ^ ((4 * wave + xrow) & 15)) * 16));
+    static_assert((4 * WAVES) % 16 == 0, "chunk swizzle must not depend on the load index");
+    // W, scales, zeros: per-lane offsets shared by all strips, strip offsets
+    // in scalar registers (tail strips past N are loaded but not stored).
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed, (uint32_t)weight_bytes(K, N));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(packed + weight_bytes(K, N), (uint32_t)scale_bytes(K, N, 32 * GS));
+    const __amdgpu_buffer_rsrc_t rz =
+        make_rsrc(packed + weight_bytes(K, N) + scale_bytes(K, N, 32 * GS), (uint32_t)zero_bytes(K, N, 32 * GS));
+    const uint32_t woff = lane * 16, soff = col * 2, zoff = col >> 1;
+    int sstrip[NSW];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) sstrip[j] = strip_w + j < nstrip ? strip_w + j : nstrip - 1;
+
     auto issue_x = [&](int b, int stage) {
 #pragma unroll
         for (int i = 0; i < XLOADS; ++i) {
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(xsrc[i] + b * kBlockK),
-                (lds_void *)(lds + stage * STAGE + (i * 4 + wave) * 1024), 16, 0, 0);
+            // (a local copy: passing the array element straight to the
+            // builtin makes hipcc's host pass drop this kernel's launch stub)
+            const __amdgpu_buffer_rsrc_t r = rx[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void *)(lds + stage * STAGE + (i * WAVES + wave) * 1024), 16, xoff, b * 256, 0, 0);
         }
     };
-    auto load_w = [&](int b, u32x4 *w, uint32_t (*sz)[NSW]) {
+    typedef WSet<NSW, NF> Set;
+    auto load_w = [&](int b, Set &w) {
 #pragma unroll
         for (int j = 0; j < NSW; ++j) {
-            const int s = strip_w + j;
-            if (s < nstrip) {
-                w[j] = pv.w[((size_t)s * nblk + b) * 64 + lane];
+            w.w[j] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (sstrip[j] * nblk + b) * kTileBytes, 0));
 #pragma unroll
-                for (int f = 0; f < NF; ++f)
-                    sz[f][j] = load_scale_zero(pv, (size_t)s * ngrp + (b * 4 + f * F) / GS, col);
-            } else {
-                w[j] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int f = 0; f < NF; ++f) sz[f][j] = 0u;
+            for (int f = 0; f < NF; ++f) {
+                const int g = sstrip[j] * ngrp + (b * 4 + f * F) / GS;
+                w.sc[f][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, g * 32, 0);
+                w.zb[f][j] = __builtin_amdgcn_raw_buffer_load_b8(rz, zoff, g * 8, 0);
             }
         }
     };
@@ -100,49 +149,55 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 #pragma unroll
         for (int j = 0; j < NSW; ++j) acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 wc[NSW], wn[NSW];
-    uint32_t szc[NF][NSW], szn[NF][NSW];
-    issue_x(0, 0);
-    load_w(0, wc, szc);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // LDS byte offset of this lane's A operand for row tile mt, step t.
+    const int rbase = wm * MTW * 16;
+    auto a_off = [&](int mt, int t) { return (rbase + mt * 16 + col) * 256 + (((4 * t + kq) ^ col) * 16); };
+    const int zsh = (col & 1) * 4;
 
-    for (int b = 0; b < nblk; ++b) {
-        const int cur = b & 1;
-        if (b + 1 < nblk) {
-            issue_x(b + 1, cur ^ 1);
-            load_w(b + 1, wn, szn);
-        }
-        const uint8_t *st = lds + cur * STAGE;
+    auto compute = [&](int stage, const Set &w) {
+        const uint8_t *st = lds + stage * STAGE;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            // LDS reads first; the dequantization below covers their latency
+            half8 a[MTW];
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) a[mt] = *reinterpret_cast<const half8 *>(st + a_off(mt, t));
             const int f = t / F;
             half8 bw[NSW];
 #pragma unroll
             for (int j = 0; j < NSW; ++j) {
-                const uint32_t sz = szc[f][j];
-                const uint32_t s2 = (sz & 0xFFFFu) | (sz << 16);
-                bw[j] = dequant_w(t, wc[j], neg_bias_pair(sz), s2, magic);
+                const uint32_t h = 0xE400u | ((w.zb[f][j] >> zsh) & 15u);
+                bw[j] = dequant_w(t, w.w[j], h * 0x10001u, (w.sc[f][j] & 0xFFFFu) * 0x10001u, magic);
             }
-            const int chunk = (4 * t + kq) ^ col;
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt) {
-                const half8 a = *reinterpret_cast<const half8 *>(st + (mt * 16 + col) * 256 + chunk * 16);
+            for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-                for (int j = 0; j < NSW; ++j) acc[mt][j] = mfma16x16x32(a, bw[j], acc[mt][j]);
-            }
+                for (int j = 0; j < NSW; ++j) acc[mt][j] = mfma16x16x32(a[mt], bw[j], acc[mt][j]);
+            // keep the scheduler from hoisting the next step's LDS reads
+            // (and their registers) above these MFMAs
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    Set wc, wnext;
+    issue_x(bb, 0);
+    load_w(bb, wc);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int b = bb; b < be; ++b) {
+        const int cur = (b - bb) & 1;
+        if (b + 1 < be) {
+            issue_x(b + 1, cur ^ 1);
+            load_w(b + 1, wnext);
+        }
+        compute(cur, wc);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < NSW; ++j) {
-            wc[j] = wn[j];
-#pragma unroll
-            for (int f = 0; f < NF; ++f) szc[f][j] = szn[f][j];
-        }
+        wc = wnext;
     }
 
-    // Epilogue: fp32 -> fp16 (round to nearest even), rows beyond M dropped.
+    // Epilogue: fp32 -> fp16 (round to nearest even) or fp32 partials; rows
+    // beyond M and strips beyond N dropped.
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
@@ -152,36 +207,137 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
             const size_t n = (size_t)s * kStripCols + col;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int row = m0 + mt * 16 + 4 * kq + e;
-                if (row < M) Y[(size_t)row * N + n] = f32_to_f16_bits(acc[mt][j][e]);
+                const int row = m0 + rbase + mt * 16 + 4 * kq + e;
+                if (row >= M) continue;
+                if (S == 1)
+                    Y[(size_t)row * N + n] = f32_to_f16_bits(acc[mt][j][e]);
+                else
+                    part[((size_t)split * M + row) * N + n] = acc[mt][j][e];
             }
         }
 }
 
-template <int MTW, int NSW>
-hipError_t launch_shape(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
-                        uint16_t *Y, hipStream_t stream) {
-    constexpr int BM = 16 * MTW, BN = 64 * NSW;
+__global__ void __launch_bounds__(256)
+prefill_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ Y, int64_t MN, int S) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < MN;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float v = 0.f;
+        for (int s = 0; s < S; ++s) v += part[(size_t)s * MN + i];
+        Y[i] = f32_to_f16_bits(v);
+    }
+}
+
+// ------------------------------------------------------------- configurations
+struct Cfg {
+    int mtw, nsw, wm, wn, occ;
+};
+
+// Instantiated shapes (index = W4A16_PREFILL_CFG for tuning).
+constexpr Cfg kCfgs[] = {
+    {16, 4, 1, 4, 1},  // 0: 256 x 256, 4 waves, 1 wave/SIMD
+    {8, 4, 2, 4, 2},   // 1: 256 x 256, 8 waves, 2 waves/SIMD
+    {8, 4, 1, 4, 2},   // 2: 128 x 256, 4 waves, 2 WGs/CU
+    {4, 4, 1, 4, 2},   // 3:  64 x 256
+    {8, 2, 2, 4, 2},   // 4: 256 x 128, 8 waves
+    {4, 4, 2, 4, 2},   // 5: 128 x 256, 8 waves
+};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+template <int CI, int GS>
+hipError_t launch_cfg_g(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y,
+                        float *part, int S, int slice_blocks, hipStream_t stream) {
+    constexpr Cfg c = kCfgs[CI];
+    constexpr int BM = c.wm * c.mtw * 16, BN = c.wn * c.nsw * 16;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
+    hipLaunchKernelGGL((prefill_kernel<c.mtw, c.nsw, c.wm, c.wn, GS, c.occ>),
+                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)S), dim3(c.wm * c.wn * 64), 0, stream, X,
+                       packed, Y, part, M, N, K, tiles_m, tiles_n, S, slice_blocks);
+    return hipGetLastError();
+}
+
+template <int CI>
+hipError_t launch_cfg(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
+                      float *part, int S, int slice_blocks, hipStream_t stream) {
     switch (G) {
-        case 32: hipLaunchKernelGGL((prefill_kernel<MTW, NSW, 1>), grid, dim3(256), 0, stream, X, packed, Y, M, N, K, tiles_m); break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<MTW, NSW, 2>), grid, dim3(256), 0, stream, X, packed, Y, M, N, K, tiles_m); break;
-        case 128: hipLaunchKernelGGL((prefill_kernel<MTW, NSW, 4>), grid, dim3(256), 0, stream, X, packed, Y, M, N, K, tiles_m); break;
-        case 256: hipLaunchKernelGGL((prefill_kernel<MTW, NSW, 8>), grid, dim3(256), 0, stream, X, packed, Y, M, N, K, tiles_m); break;
+        case 32: return launch_cfg_g<CI, 1>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
+        case 64: return launch_cfg_g<CI, 2>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
+        case 128: return launch_cfg_g<CI, 4>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
+        case 256: return launch_cfg_g<CI, 8>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+}
+
+hipError_t launch_index(int ci, const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
+                        uint16_t *Y, float *part, int S, int slice_blocks, hipStream_t stream) {
+    switch (ci) {
+        case 0: return launch_cfg<0>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 1: return launch_cfg<1>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 2: return launch_cfg<2>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 3: return launch_cfg<3>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 4: return launch_cfg<4>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        default: return launch_cfg<5>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+    }
+}
+
+struct PrefillPlan {
+    int ci, splits, slice_blocks;
+};
+
+// Tile shape by M; split K when the tiles cannot fill every CU about twice.
+// W4A16_PREFILL_CFG overrides the shape (tuning).
+PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
+    PrefillPlan p;
+    p.ci = M <= 64 ? 3 : 2;
+    if (const char *e = getenv("W4A16_PREFILL_CFG")) {
+        const int v = atoi(e);
+        if (v >= 0 && v < kNumCfgs) p.ci = v;
+    }
+    const Cfg c = kCfgs[p.ci];
+    const int BM = c.wm * c.mtw * 16, BN = c.wn * c.nsw * 16;
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int nblk = K / kBlockK;
+    const int per_cu = c.occ * 4 / (c.wm * c.wn) > 0 ? c.occ * 4 / (c.wm * c.wn) : 1;  // resident WGs per CU
+    if (splits <= 0) {
+        splits = 1;
+        const int want = num_cus * per_cu;
+        if (tiles < want) splits = (want + tiles - 1) / tiles;
+        const int cap = nblk / 8 > 1 ? nblk / 8 : 1;  // keep 8+ blocks per split
+        if (splits > cap) splits = cap;
+    }
+    if (splits > nblk) splits = nblk;
+    const int unit = G > kBlockK ? G / kBlockK : 1;
+    int sb = (nblk + splits - 1) / splits;
+    sb = (sb + unit - 1) / unit * unit;
+    p.slice_blocks = sb;
+    p.splits = (nblk + sb - 1) / sb;
+    return p;
 }
 
 }  // namespace
 
+int prefill_auto_splits(int M, int N, int K, int G, int num_cus) {
+    return prefill_plan(M, N, K, G, 0, num_cus).splits;
+}
+
+size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits) {
+    const PrefillPlan p = prefill_plan(M, N, K, G, splits, 256);
+    if (p.splits <= 1) return 0;
+    return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
 hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
-                          uint16_t *Y, hipStream_t stream) {
-    if (M <= 64) return launch_shape<4, 4>(X, packed, M, N, K, G, Y, stream);
-    if (M <= 128) return launch_shape<8, 4>(X, packed, M, N, K, G, Y, stream);
-    return launch_shape<16, 4>(X, packed, M, N, K, G, Y, stream);
+                          uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream) {
+    const PrefillPlan p = prefill_plan(M, N, K, G, splits, num_cus);
+    float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    hipError_t e = launch_index(p.ci, X, packed, M, N, K, G, Y, part, p.splits, p.slice_blocks, stream);
+    if (e != hipSuccess || p.splits <= 1) return e;
+    const int64_t MN = (int64_t)M * N;
+    int64_t blocks = (MN + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, Y, MN,
+                       p.splits);
+    return hipGetLastError();
 }
 
 }  // namespace w4a16
