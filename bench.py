@@ -2,28 +2,35 @@
 """Benchmark of the W4A16 GEMM on one MI355X.
 
 One step = one W4A16 GEMM launch (through the C ABI, automatic plan) for every
-instance of the workload, e.g. for the default Llama-3-8B-shaped decode
-workload: fused QKV (K=4096, N=6144) and down-projection (K=14336, N=4096),
-each at M = 1, 8, 16 and 32, G = 128: eight launches.
+instance of the workload. For the default Llama-3-8B-shaped decode workload
+that is fused QKV (K=4096, N=6144) and down-projection (K=14336, N=4096), each
+at M = 1, 8, 16 and 32, G = 128: eight launches.
 
 Inputs are seeded synthetic tensors (synth.py) resident in HBM before the
-timed region. Every weight matrix is replicated into enough copies to cover
-``--rotate-gib`` GiB, X and Y likewise, and consecutive launches on one matrix
-use consecutive copies, so no launch finds its weights in the 256 MiB
-Infinity Cache or an L2 left warm by an earlier launch.
+timed region. Every weight matrix is replicated into C copies, C chosen so
+that the copies of the smallest matrix cover at least ``--rotate-gib`` GiB,
+and step s uses copy s mod C of every tensor, so no launch finds its weights
+in the 256 MiB Infinity Cache or a warm L2.
+
+Timing: the steps are captured into HIP graphs (the way a serving loop
+replays its decode step): one graph holding a whole rotation of C steps and
+one graph per single step. K timed steps replay the rotation graph K // C
+times and then K mod C single-step graphs, back to back between two
+synchronizations. ``--eager`` times plain Python-driven launches instead
+(host launch overhead included).
 
 Prints ONE JSON line:
   value        effective TB/s = sum of algorithmic bytes over the step / step
                time (algorithmic bytes: 4-bit weights, fp16 scales, 4-bit
-               zeros, fp16 X and Y, each once); TFLOP/s for the prefill
-               workload
+               zeros, fp16 X and Y, each once); TFLOP/s for a prefill workload
   roofline     the dominant kernel's achieved rate against the MI355X peak
-               (HBM 8 TB/s, or fp16 MFMA 2.5 PFLOP/s), from HIP events around
-               each launch in the timed region
+               (HBM 8 TB/s, or fp16 MFMA 2.5 PFLOP/s): algorithmic bytes (or
+               flops) per launch / average launch time, from HIP events around
+               per-instance graph replays in the timed phase
   cpu_baseline the CPU oracle (float64, OpenMP) timed on this host on the same
-               step, as context
-  secondary    (default run only) TFLOP/s of the Llama-3-8B-shaped prefill
-               GEMM, M=2048, K=4096, N=28672
+               step (sampled by columns where an instance is large)
+  secondary    (default run) TFLOP/s of the Llama-3-8B-shaped prefill GEMM,
+               M=2048, K=4096, N=28672
 """
 from __future__ import annotations
 
@@ -46,14 +53,17 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=0, help="timed steps (default: one rotation, at least 40)")
+    p.add_argument("--warmup", type=int, default=0, help="untimed steps (default: one rotation)")
     p.add_argument("--workload", default="llama3_8b_decode")
     p.add_argument("--rotate-gib", type=float, default=1.0,
-                   help="bytes of distinct weight copies per matrix that launches cycle through")
+                   help="minimum bytes of distinct copies per weight matrix that steps cycle through")
+    p.add_argument("--eager", action="store_true", help="time Python-driven launches, no graphs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--detail", action="store_true", help="print per-instance lines to stderr")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="before timing, run one device copy of BYTES bytes (reference for HBM counters)")
+    p.add_argument("--detail", action="store_true", help="per-instance lines to stderr")
     return p.parse_args(argv)
 
 
@@ -67,101 +77,161 @@ class Runner:
         import synth
         import w4a16_mixed_precision_amd as w4
 
+        self.torch = torch
         self.w4 = w4
         self.insts = insts
-        self.mats = {}      # matrix key -> dict(packed copies, K, N, G)
-        self.host = {}      # instance name -> (X, q, z, s) host copies (cpu baseline)
-        self.xs, self.ys, self.mat_of = [], [], []
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")  # noqa: E731
+        keys, base = [], {}
+        self.host = {}
         for inst in insts:
             key = (inst.workload, inst.matrix, inst.K, inst.N, inst.G, inst.outliers, inst.seed)
+            keys.append(key)
             X, q, z, s = synth.draw(inst)
             self.host[inst.name] = (X, q, z, s)
-            if key not in self.mats:
-                nbytes = w4.w4a16_packed_bytes(inst.K, inst.N, inst.G)
-                copies = max(2, math.ceil(rotate_bytes / nbytes))
-                base = w4.w4a16_pack(to(q), to(z), to(s), inst.G)
-                packed = [base] + [base.clone() for _ in range(copies - 1)]
-                self.mats[key] = {"packed": packed, "next": 0}
-            mat = self.mats[key]
-            n = len(mat["packed"])
-            xd = to(X)
-            self.xs.append([xd] + [xd.clone() for _ in range(n - 1)])
+            if key not in base:
+                base[key] = w4.w4a16_pack(to(q), to(z), to(s), inst.G)
+        smallest = min(b.numel() for b in base.values())
+        self.copies = max(2, math.ceil(rotate_bytes / smallest))
+        self.packed = {k: [b] + [b.clone() for _ in range(self.copies - 1)] for k, b in base.items()}
+        self.xs, self.ys, self.ws, self.mat_of = [], [], [], []
+        for inst, key in zip(insts, keys):
+            xd = to(self.host[inst.name][0])
+            self.xs.append([xd] + [xd.clone() for _ in range(self.copies - 1)])
             self.ys.append([torch.empty((inst.M, inst.N), dtype=torch.float16, device="cuda")
-                            for _ in range(n)])
+                            for _ in range(self.copies)])
+            nbytes = w4.w4a16_workspace_bytes(inst.M, inst.N, inst.K, inst.G, w4.W4A16_PATH_AUTO, 0)
+            self.ws.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda"))
             self.mat_of.append(key)
         torch.cuda.synchronize()
+        self.graphs = None
 
-    def launch(self, i):
+    def launch(self, i, c):
         inst = self.insts[i]
-        mat = self.mats[self.mat_of[i]]
-        c = mat["next"]
-        mat["next"] = (c + 1) % len(mat["packed"])
-        self.w4.w4a16_gemm(self.xs[i][c], mat["packed"][c], inst.N, inst.K, inst.G, Y=self.ys[i][c])
+        self.w4.w4a16_gemm_ex(self.xs[i][c], self.packed[self.mat_of[i]][c], inst.N, inst.K, inst.G,
+                              Y=self.ys[i][c], workspace=self.ws[i])
 
-    def step(self):
+    def step(self, c, only=None):
         for i in range(len(self.insts)):
-            self.launch(i)
+            if only is None or i == only:
+                self.launch(i, c)
 
-    def timed(self, steps, warmup):
-        """Times `steps` steps after `warmup` untimed ones. Returns
-        (ms per step, per-instance mean ms per launch)."""
-        import torch
-        for _ in range(warmup):
-            self.step()
+    def capture(self, only=None):
+        """Graphs: one holding all C steps, and one per single step."""
+        torch = self.torch
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for c in range(self.copies):  # eager pass first: plans, workspaces
+                self.step(c, only)
+            torch.cuda.synchronize()
+            rotation = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(rotation, stream=st):
+                for c in range(self.copies):
+                    self.step(c, only)
+            singles = []
+            for c in range(self.copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=st):
+                    self.step(c, only)
+                singles.append(g)
         torch.cuda.synchronize()
-        n = len(self.insts)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
+        return rotation, singles
+
+    def time_steps(self, steps, warmup, eager, only=None):
+        """Times exactly `steps` steps after `warmup` untimed ones; returns
+        ms per step."""
+        torch = self.torch
+        C = self.copies
+
+        def run(first, count):
+            if eager:
+                for s in range(first, first + count):
+                    self.step(s % C, only)
+                return
+            s = first
+            while count > 0:
+                if s % C == 0 and count >= C:
+                    rotation.replay()
+                    s, count = s + C, count - C
+                else:
+                    singles[s % C].replay()
+                    s, count = s + 1, count - 1
+
+        if not eager:
+            rotation, singles = self.capture(only)
+        run(0, warmup)
         torch.cuda.synchronize()
-        start.record()
-        for s in range(steps):
-            evs[s][0].record()
-            for i in range(n):
-                self.launch(i)
-                evs[s][i + 1].record()
-        end.record()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        start = (warmup + C - 1) // C * C  # start the timed steps on a rotation boundary
+        e0.record()
+        run(start, steps)
+        e1.record()
         torch.cuda.synchronize()
-        total_ms = start.elapsed_time(end)
-        per = [sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps for i in range(n)]
-        return total_ms / steps, per
+        return e0.elapsed_time(e1) / steps
 
 
-def decode_kernel_name(inst):
-    mt = 1 if inst.M <= 16 else (2 if inst.M <= 32 else 4)
-    return f"decode_kernel<MT={mt},G={inst.G}>"
+def recorded_traffic(workload):
+    """HBM bytes per launch of the dominant decode kernel, from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it was taken on the current
+    kernel sources (else None)."""
+    import hashlib
+    if workload != "llama3_8b_decode":
+        return None
+    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        for rel, digest in rec["sources_sha256"].items():
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        return float(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(runner, max_macs=4e9):
-    """The CPU oracle timed on the step's GEMMs. Instances larger than
-    `max_macs` multiply-adds are sampled by their leading columns (a multiple
-    of 16), and the sampled sub-problem's algorithmic bytes are credited."""
+def kernel_name(inst):
+    if inst.M > 32:
+        return "prefill_kernel"
+    return "decode_kernel"
+
+
+def cpu_baseline(runner, max_macs=4e9, repeats=3):
+    """The CPU oracle timed on the step's GEMMs (median of `repeats` passes).
+    Instances larger than `max_macs` multiply-adds are sampled by their
+    leading columns (a multiple of 16), and the sampled sub-problem's
+    algorithmic bytes are credited."""
     import dataclasses
 
     import oracle
     oracle.load()
     cores = oracle.max_threads()
-    t_total, b_total, sampled = 0.0, 0, []
-    for inst in runner.insts:
-        X, q, z, s = runner.host[inst.name]
-        cols = inst.N
-        if inst.M * inst.K * inst.N > max_macs:
-            cols = max(16, int(max_macs // (inst.M * inst.K)) // 16 * 16)
-            sampled.append(f"{inst.name}: {cols}/{inst.N} columns")
-        t0 = time.perf_counter()
-        oracle.gemm(X, q, z, s, inst.G, cols=(0, cols))
-        t_total += time.perf_counter() - t0
-        b_total += dataclasses.replace(inst, N=cols).alg_bytes()
+    times, b_total, sampled = [], 0, []
+    for rep in range(repeats):
+        t_total = 0.0
+        for inst in runner.insts:
+            X, q, z, s = runner.host[inst.name]
+            cols = inst.N
+            if inst.M * inst.K * inst.N > max_macs:
+                cols = max(16, int(max_macs // (inst.M * inst.K)) // 16 * 16)
+                if rep == 0:
+                    sampled.append(f"{inst.name}: {cols}/{inst.N} columns")
+            t0 = time.perf_counter()
+            oracle.gemm(X, q, z, s, inst.G, cols=(0, cols))
+            t_total += time.perf_counter() - t0
+            if rep == 0:
+                b_total += dataclasses.replace(inst, N=cols).alg_bytes()
+        times.append(t_total)
+    t = sorted(times)[len(times) // 2]
     what = f"one step ({len(runner.insts)} GEMMs)"
     if sampled:
         what += " with column samples [" + "; ".join(sampled) + "]"
     return {
-        "value": b_total / t_total / 1e12,
+        "value": b_total / t / 1e12,
         "unit": "TB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{what}, float64 C oracle, {t_total:.2f} s",
+        "sample": f"{what}, float64 C oracle, median of {repeats} passes, {t:.2f} s per pass",
     }
 
 
@@ -171,15 +241,15 @@ def run_prefill_secondary(args):
     import synth
     inst = synth.workload_instances("llama3_8b_prefill")[0]
     r = Runner([inst], args.rotate_gib * 2 ** 30)
-    ms, per = r.timed(max(5, args.steps // 5), max(2, args.warmup // 5))
-    tflops = inst.flops() / (per[0] * 1e-3) / 1e12
+    ms = r.time_steps(2 * r.copies, r.copies, args.eager)
+    tflops = inst.flops() / (ms * 1e-3) / 1e12
     del r
     torch.cuda.empty_cache()
     return {
         "metric": "W4A16 GEMM TFLOP/s, Llama-3-8B-shaped prefill gate_up (M=2048, K=4096, N=28672, G=128)",
         "value": tflops,
         "unit": "TFLOP/s",
-        "ms_per_launch": per[0],
+        "ms_per_launch": ms,
         "frac_of_mfma_f16_peak": tflops / MFMA_F16_PEAK_TFLOPS,
     }
 
@@ -189,8 +259,7 @@ def main(argv=None):
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported: the W4A16 GEMM here is a single-GPU kernel and no multi-GPU path exists.",
-              file=sys.stderr, flush=True)
+              "supported: this build measures the single-GPU W4A16 GEMM only.", file=sys.stderr, flush=True)
         return 2
 
     import torch
@@ -201,9 +270,22 @@ def main(argv=None):
         return 2
     torch.cuda.set_device(0)
     insts = synth.workload_instances(args.workload)
-    prefill = all(i.M >= 256 for i in insts)
+    prefill = all(i.M > 32 for i in insts)
     runner = Runner(insts, args.rotate_gib * 2 ** 30)
-    ms_step, per = runner.timed(args.steps, args.warmup)
+    steps = args.steps or max(40, runner.copies)
+    warmup = args.warmup or runner.copies
+
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_step = runner.time_steps(steps, warmup, args.eager)
+    ms_eager = ms_step if args.eager else runner.time_steps(runner.copies, 4, True)
+    # per-instance launch times: the same timed loop over one instance at a time
+    per = [runner.time_steps(2 * runner.copies, runner.copies, args.eager, only=i) for i in range(len(insts))]
 
     total_bytes = sum(i.alg_bytes() for i in insts)
     total_flops = sum(i.flops() for i in insts)
@@ -214,7 +296,7 @@ def main(argv=None):
             "us": ms * 1e3,
             "TBps": inst.alg_bytes() / (ms * 1e-3) / 1e12,
             "TFLOPs": inst.flops() / (ms * 1e-3) / 1e12,
-            "kernel": decode_kernel_name(inst) if inst.M <= 32 else "prefill_kernel",
+            "kernel": kernel_name(inst),
         })
         if args.detail:
             print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
@@ -231,14 +313,15 @@ def main(argv=None):
     else:
         value = total_bytes / (ms_step * 1e-3) / 1e12
         unit = "TB/s"
-        # dominant kernel: the M <= 16 decode instantiation (most launches, most time)
+        # dominant kernel: the decode kernel at M <= 16 (six of the eight
+        # launches, the metric's M range)
         sel = [k for k, i in enumerate(insts) if i.M <= 16] or list(range(len(insts)))
         b = sum(insts[k].alg_bytes() for k in sel)
         t = sum(per[k] for k in sel) * 1e-3
         achieved = b / t / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": decode_kernel_name(insts[sel[0]]),
+                "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload),
+                "kernel": "decode_kernel (M <= 16 launches)",
                 "launches_per_step": len(sel), "bytes_per_launch": b / len(sel),
                 "avg_launch_us": t / len(sel) * 1e6}
 
@@ -247,8 +330,8 @@ def main(argv=None):
         "value": value,
         "unit": unit,
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -260,7 +343,9 @@ def main(argv=None):
             "instances": [i.name for i in insts],
             "algorithmic_bytes_per_step": total_bytes,
             "flops_per_step": total_flops,
-            "rotation_gib_per_matrix": args.rotate_gib,
+            "rotation_copies": runner.copies,
+            "timing": "eager launches" if args.eager else "HIP graph replay, one graph per step",
+            "ms_per_step_eager": ms_eager,
             "parallelism": "single GPU",
         },
         "roofline": roof,

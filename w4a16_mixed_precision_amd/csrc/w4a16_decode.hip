@@ -111,36 +111,6 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     SZ *szl = reinterpret_cast<SZ *>(lds);
     uint8_t *xl = lds + L.sz_bytes;
 
-    // ---- stage scale/zero records of the slice: [NS][ng][16]
-    {
-        const uint16_t *sreg = reinterpret_cast<const uint16_t *>(packed + weight_bytes(K, N));
-        const uint8_t *zreg = packed + weight_bytes(K, N) + scale_bytes(K, N, G);
-        for (int e = threadIdx.x; e < NS * ng * 16; e += WK * 64) {
-            const int j = e / (ng * 16), r = e % (ng * 16);
-            const int g = g0 + r / 16, c = r % 16;
-            const int s = strip0 + j;
-            SZ v{0u, 0.f};
-            if (s < nstrip) {
-                const size_t rec = (size_t)s * ngrp + g;
-                const uint32_t z = (zreg[rec * 8 + (c >> 1)] >> ((c & 1) * 4)) & 15u;
-                const uint32_t h = 0xE400u | z;
-                v.nb = h | (h << 16);
-                v.sc = (float)__builtin_bit_cast(_Float16, sreg[rec * 16 + c]);
-            }
-            szl[e] = v;
-        }
-    }
-    // ---- stage the slice's rows of X (LDS-X mode): [M][slice k] + padding
-    if constexpr (XLDS) {
-        const int kc = (be - bb) * kBlockK / 8;  // 16-byte chunks per row
-        for (int e = threadIdx.x; e < M * kc; e += WK * 64) {
-            const int r = e / kc, c = e % kc;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(X + (size_t)r * K + (size_t)bb * kBlockK + c * 8);
-            *reinterpret_cast<u32x4 *>(xl + r * L.x_stride + c * 16) = v;
-        }
-    }
-    __syncthreads();
-
     __amdgpu_buffer_rsrc_t rw[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -256,16 +226,66 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                     b1.a[i][t][mt] = half8{0, 0, 0, 0, 0, 0, 0, 0};
                 }
     }
+    // With LDS-staged X the first two batches of weight tiles go out before
+    // the staging, so their latency overlaps it (with register X the extra
+    // live registers would cost occupancy; those waves load after staging).
     int b = wb;
-    if (b < we) load(b, b0);
-    while (b < we) {
+    if constexpr (XLDS) {
+        if (b < we) load(b, b0);
         if (b + NB < we) load(b + NB, b1);
-        compute(b, b0);
-        b += NB;
-        if (b >= we) break;
-        if (b + NB < we) load(b + NB, b0);
-        compute(b, b1);
-        b += NB;
+    }
+
+    // ---- stage scale/zero records of the slice: [NS][ng][16]
+    {
+        const uint16_t *sreg = reinterpret_cast<const uint16_t *>(packed + weight_bytes(K, N));
+        const uint8_t *zreg = packed + weight_bytes(K, N) + scale_bytes(K, N, G);
+        for (int e = threadIdx.x; e < NS * ng * 16; e += WK * 64) {
+            const int j = e / (ng * 16), r = e % (ng * 16);
+            const int g = g0 + r / 16, c = r % 16;
+            const int s = strip0 + j;
+            SZ v{0u, 0.f};
+            if (s < nstrip) {
+                const size_t rec = (size_t)s * ngrp + g;
+                const uint32_t z = (zreg[rec * 8 + (c >> 1)] >> ((c & 1) * 4)) & 15u;
+                const uint32_t h = 0xE400u | z;
+                v.nb = h | (h << 16);
+                v.sc = (float)__builtin_bit_cast(_Float16, sreg[rec * 16 + c]);
+            }
+            szl[e] = v;
+        }
+    }
+    // ---- stage the slice's rows of X (LDS-X mode): [M][slice k] + padding
+    if constexpr (XLDS) {
+        const int kc = (be - bb) * kBlockK / 8;  // 16-byte chunks per row
+        for (int e = threadIdx.x; e < M * kc; e += WK * 64) {
+            const int r = e / kc, c = e % kc;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(X + (size_t)r * K + (size_t)bb * kBlockK + c * 8);
+            *reinterpret_cast<u32x4 *>(xl + r * L.x_stride + c * 16) = v;
+        }
+    }
+    __syncthreads();
+
+    if constexpr (XLDS) {
+        while (b < we) {
+            compute(b, b0);
+            b += NB;
+            if (b + NB < we) load(b + NB, b0);
+            if (b >= we) break;
+            compute(b, b1);
+            b += NB;
+            if (b + NB < we) load(b + NB, b1);
+        }
+    } else {
+        if (b < we) load(b, b0);
+        while (b < we) {
+            if (b + NB < we) load(b + NB, b1);
+            compute(b, b0);
+            b += NB;
+            if (b >= we) break;
+            if (b + NB < we) load(b + NB, b0);
+            compute(b, b1);
+            b += NB;
+        }
     }
 
     // ---- add the WK partial tiles of each strip in LDS, run 0 first
@@ -315,6 +335,7 @@ constexpr uint32_t kLdsBudget = 64 * 1024;
 struct Plan {
     int mt, ns, wk;
     bool xlds;
+    bool fixed_splits;  // automatic plan keeps K unsplit
     int splits, slice_blocks;
 };
 
@@ -323,15 +344,31 @@ int env_int(const char *name, int dflt) {
     return v ? atoi(v) : dflt;
 }
 
-// Launch shape for M: LDS-staged X with one strip per wave for M <= 4,
-// register X shared by NS strips per wave otherwise. W4A16_DECODE_NS and
-// W4A16_DECODE_WK override NS and WK for tuning (instantiated values only).
-Plan base_plan(int M) {
+// Launch shape. LDS-staged X with one strip per wave for M <= 4; for
+// larger M register X shared by NS strips per wave, the shape picked from
+// measurements on MI355X over the Llama-3-8B/70B decode matrices: narrow N
+// with short K (QKV-like) runs best unsplit with 2 strips x 16 waves, the
+// rest with 4 strips x 8 waves and K split across workgroups where N is
+// narrow. W4A16_DECODE_NS and W4A16_DECODE_WK override NS and WK for tuning
+// (instantiated values only).
+Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
     p.xlds = M <= 4;
-    p.ns = p.xlds ? 1 : (p.mt == 4 ? 2 : 4);
-    p.wk = 8;
+    const int nstrip = N / kStripCols, nblk = K / kBlockK;
+    const bool short_narrow = nstrip <= 384 && nblk <= 64;
+    if (p.xlds) {
+        p.ns = 1;
+        p.wk = nstrip < 512 ? 16 : 8;
+    } else if (short_narrow) {
+        p.ns = 2;
+        p.wk = p.mt == 1 ? 16 : 8;
+    } else {
+        p.ns = (M <= 8 && nstrip >= 2048) ? 2 : 4;
+        p.wk = 8;
+    }
+    if (p.mt == 4) p.ns = 2;
+    p.fixed_splits = !p.xlds && short_narrow;
     const int ens = env_int("W4A16_DECODE_NS", 0), ewk = env_int("W4A16_DECODE_WK", 0);
     if (ens == 1 || ens == 2 || ens == 4) p.ns = ens;
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
@@ -357,9 +394,10 @@ bool lds_fits(const Plan &p, int M, int G, int slice_blocks) {
 }
 
 Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
-    Plan p = base_plan(M);
+    Plan p = base_plan(M, N, K);
     const int nblk = K / kBlockK;
     const int tiles = (N / kStripCols + p.ns - 1) / p.ns;
+    if (splits <= 0 && p.fixed_splits) splits = 1;
     if (splits <= 0) {
         // Narrow N: about two workgroups per CU, keeping two blocks per wave.
         splits = 1;
