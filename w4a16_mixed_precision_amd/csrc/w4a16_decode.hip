@@ -136,25 +136,27 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         for (int j = 0; j < NS; ++j) acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     typedef DecodeBatch<MT, NS, NB> Batch;
+    // Blocks at or past the end of the wave's run load from the out-of-range
+    // offset: no branch, no memory traffic, and the same instruction count
+    // on every path. X rows >= M are out of range of X's descriptor too.
     auto load = [&](int b0, Batch &bt) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NB; ++i) {
+            const bool in = b0 + i < we;
+            const uint32_t wo = in ? (uint32_t)lane * 16u : kOobOffset;
 #pragma unroll
             for (int j = 0; j < NS; ++j)
-                if (b0 + i < we)
-                    bt.w[i][j] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], lane * 16, (b0 + i) * kTileBytes, 0));
-        if constexpr (!XLDS) {
-#pragma unroll
-            for (int i = 0; i < NB; ++i)
+                bt.w[i][j] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], wo, (b0 + i) * kTileBytes, 0));
+            if constexpr (!XLDS) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        if (b0 + i < we && mt * 16 + col < M)
-                            bt.a[i][t][mt] = __builtin_bit_cast(
-                                half8, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rx, xoff[mt], ((b0 + i) * kBlockK + t * 32) * 2, 0));
+                        bt.a[i][t][mt] = __builtin_bit_cast(
+                            half8, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rx, in ? xoff[mt] : kOobOffset, ((b0 + i) * kBlockK + t * 32) * 2, 0));
+            }
         }
     };
     auto compute = [&](int b0, const Batch &bt) {
@@ -214,78 +216,116 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         }
     };
 
+    // The first two batches go out before the staging so that their latency
+    // overlaps it.
     Batch b0, b1;
-    if constexpr (!XLDS) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    b0.a[i][t][mt] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-                    b1.a[i][t][mt] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-                }
-    }
-    // With LDS-staged X the first two batches of weight tiles go out before
-    // the staging, so their latency overlaps it (with register X the extra
-    // live registers would cost occupancy; those waves load after staging).
     int b = wb;
-    if constexpr (XLDS) {
-        if (b < we) load(b, b0);
-        if (b + NB < we) load(b + NB, b1);
-    }
+    if (b < we) load(b, b0);
+    if (b + NB < we) load(b + NB, b1);
 
-    // ---- stage scale/zero records of the slice: [NS][ng][16]
+    // ---- staging: the scale/zero records of the slice, [NS][ng][16], and in
+    // LDS-X mode the slice's rows of X. A record unit is half a group record
+    // (8 columns: 16 bytes of scales and 4 bytes of zero codes), an X unit 16
+    // bytes of one row. One round issues the loads of up to SU record units
+    // and XU X units per thread (whole waves past the end skip theirs), waits
+    // once for everything issued so far, the weight batches included (vector
+    // loads complete in order, so that costs nothing extra), and writes them
+    // to LDS; units beyond that round (long slices only) follow one by one.
     {
-        const uint16_t *sreg = reinterpret_cast<const uint16_t *>(packed + weight_bytes(K, N));
-        const uint8_t *zreg = packed + weight_bytes(K, N) + scale_bytes(K, N, G);
-        for (int e = threadIdx.x; e < NS * ng * 16; e += WK * 64) {
-            const int j = e / (ng * 16), r = e % (ng * 16);
-            const int g = g0 + r / 16, c = r % 16;
-            const int s = strip0 + j;
-            SZ v{0u, 0.f};
-            if (s < nstrip) {
-                const size_t rec = (size_t)s * ngrp + g;
-                const uint32_t z = (zreg[rec * 8 + (c >> 1)] >> ((c & 1) * 4)) & 15u;
-                const uint32_t h = 0xE400u | z;
-                v.nb = h | (h << 16);
-                v.sc = (float)__builtin_bit_cast(_Float16, sreg[rec * 16 + c]);
+        constexpr int T = WK * 64, SU = 1, XU = XLDS ? 2 : 1;
+        const int tid = (int)threadIdx.x;
+        const int nsv = nstrip - strip0 < NS ? nstrip - strip0 : NS;  // strips that exist
+        const uint8_t *srec = packed + weight_bytes(K, N) + (size_t)strip0 * ngrp * 32;
+        const uint8_t *zrec = packed + weight_bytes(K, N) + scale_bytes(K, N, G) + (size_t)strip0 * ngrp * 8;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(srec, (uint32_t)(nsv * ngrp * 32));
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(zrec, (uint32_t)(nsv * ngrp * 8));
+        const int units = NS * ng * 2;
+        const int kc = (be - bb) * kBlockK / 8;  // X units per row
+        const int xunits = XLDS ? M * kc : 0;
+
+        auto sz_load = [&](int u, u32x4 &sv, uint32_t &zv) {
+            const int j = u / (ng * 2), r = u % (ng * 2);
+            const bool ok = u < units && j < nsv;
+            const uint32_t rec = (uint32_t)(j * ngrp + g0 + (r >> 1));
+            sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rs, ok ? rec * 32u + (r & 1) * 16u : kOobOffset, 0, 0));
+            zv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz, ok ? rec * 8u + (r & 1) * 4u : kOobOffset,
+                                                               0, 0);
+        };
+        auto sz_store = [&](int u, const u32x4 &sv, uint32_t zv) {
+            u32x4 *dst = reinterpret_cast<u32x4 *>(szl + (u >> 1) * 16 + (u & 1) * 8);
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2) {
+                u32x4 rec2;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t hz = 0xE400u | ((zv >> (4 * (2 * c2 + h))) & 15u);
+                    rec2[2 * h] = hz | (hz << 16);
+                    rec2[2 * h + 1] = __builtin_bit_cast(
+                        uint32_t, (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[c2] >> (16 * h))));
+                }
+                dst[c2] = rec2;
             }
-            szl[e] = v;
-        }
-    }
-    // ---- stage the slice's rows of X (LDS-X mode): [M][slice k] + padding
-    if constexpr (XLDS) {
-        const int kc = (be - bb) * kBlockK / 8;  // 16-byte chunks per row
-        for (int e = threadIdx.x; e < M * kc; e += WK * 64) {
+        };
+        auto x_load = [&](int e) {
             const int r = e / kc, c = e % kc;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(X + (size_t)r * K + (size_t)bb * kBlockK + c * 8);
+            const uint32_t off = e < xunits ? (uint32_t)(r * K * 2 + bb * kBlockK * 2 + c * 16) : kOobOffset;
+            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        };
+        auto x_store = [&](int e, const u32x4 &v) {
+            const int r = e / kc, c = e % kc;
             *reinterpret_cast<u32x4 *>(xl + r * L.x_stride + c * 16) = v;
+        };
+
+        u32x4 sv[SU], xv[XU];
+        uint32_t zv[SU];
+#pragma unroll
+        for (int i = 0; i < SU; ++i)
+            if (i * T + wk * 64 < units) sz_load(i * T + tid, sv[i], zv[i]);
+        if constexpr (XLDS) {
+#pragma unroll
+            for (int i = 0; i < XU; ++i)
+                if (i * T + wk * 64 < xunits) xv[i] = x_load(i * T + tid);
+        }
+        asm volatile("" ::: "memory");       // no load sinks below this point
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+        for (int i = 0; i < SU; ++i)
+            if (i * T + tid < units) sz_store(i * T + tid, sv[i], zv[i]);
+        if constexpr (XLDS) {
+#pragma unroll
+            for (int i = 0; i < XU; ++i)
+                if (i * T + tid < xunits) x_store(i * T + tid, xv[i]);
+        }
+        for (int u = SU * T + tid; u < units; u += T) {
+            u32x4 a;
+            uint32_t z;
+            sz_load(u, a, z);
+            sz_store(u, a, z);
+        }
+        if constexpr (XLDS) {
+            for (int e = XU * T + tid; e < xunits; e += T) x_store(e, x_load(e));
         }
     }
+    // Nothing is outstanding from here on but the weight batches of the
+    // main loop.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    if constexpr (XLDS) {
-        while (b < we) {
+    // Two batches in flight: consume one, refill it two batches ahead. All
+    // rounds but the last refill unconditionally (only the final refill can
+    // reach past the run, and those blocks are out of range); the last round
+    // only consumes.
+    if (b < we) {
+        const int rounds = (we - b + 2 * NB - 1) / (2 * NB);
+        for (int r = 1; r < rounds; ++r, b += 2 * NB) {
             compute(b, b0);
-            b += NB;
-            if (b + NB < we) load(b + NB, b0);
-            if (b >= we) break;
-            compute(b, b1);
-            b += NB;
-            if (b + NB < we) load(b + NB, b1);
+            load(b + 2 * NB, b0);
+            compute(b + NB, b1);
+            load(b + 3 * NB, b1);
         }
-    } else {
-        if (b < we) load(b, b0);
-        while (b < we) {
-            if (b + NB < we) load(b + NB, b1);
-            compute(b, b0);
-            b += NB;
-            if (b >= we) break;
-            if (b + NB < we) load(b + NB, b0);
-            compute(b, b1);
-            b += NB;
-        }
+        compute(b, b0);
+        compute(b + NB, b1);
     }
 
     // ---- add the WK partial tiles of each strip in LDS, run 0 first

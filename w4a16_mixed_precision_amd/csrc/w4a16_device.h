@@ -154,6 +154,13 @@ __device__ inline uint16_t f32_to_f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// A raw buffer load whose offset reaches past the descriptor's byte count
+// returns zeros and makes no memory request. Kernels point loads they do not
+// need at this offset instead of branching around them, so every path
+// through a loop issues the same loads and the compiler can wait for exactly
+// the batch it consumes.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
 // Buffer resource over [base, base + bytes) for raw buffer loads (gfx9
 // descriptor: stride 0, 32-bit data format word).
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
