@@ -61,24 +61,40 @@ struct DecodeBatch {
     half8 a[NB][4][MT];  // register-X mode only
 };
 
-// Dynamic LDS layout: [ sz records | X rows (LDS-X mode) or reduction ].
+// Dynamic LDS: one private region per wave, back to back, holding the
+// records of the wave's groups, [NS][ngw][16], and in LDS-X mode the rows of
+// X over the wave's run of blocks, [M][x_stride]. X arrives by direct
+// buffer-to-LDS loads of 1 KiB (4 blocks of one row) per instruction, so a
+// row slot holds whole KiB chunks, plus 16 bytes that put consecutive rows in
+// different banks. After the main loop the same memory holds the cross-wave
+// reduction buffer [WK][NS][MT][64] of float4.
 struct DecodeLds {
-    uint32_t sz_bytes, x_bytes, red_bytes, x_stride;
-    __host__ __device__ uint32_t total() const {
-        return sz_bytes + (x_bytes > red_bytes ? x_bytes : red_bytes);
-    }
+    uint32_t ngw;         // record groups per wave region
+    uint32_t sz_bytes;    // records per wave region
+    uint32_t x_stride;    // bytes per staged row of X
+    uint32_t wave_bytes;  // one wave region
+    uint32_t red_bytes;
+    uint32_t regions;     // WK * wave_bytes
+    __host__ __device__ uint32_t total() const { return regions > red_bytes ? regions : red_bytes; }
 };
 
 __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, int slice_blocks, int G,
                                                  bool xlds) {
     DecodeLds l;
-    const int groups = (slice_blocks * kBlockK + G - 1) / G;
-    l.sz_bytes = (uint32_t)(NS * groups * 16 * sizeof(SZ));
-    l.x_stride = (uint32_t)(slice_blocks * kBlockK * 2 + 16);  // +16 B: rows in different banks
-    l.x_bytes = xlds ? (uint32_t)M * l.x_stride : 0u;
+    const int per = (slice_blocks + WK - 1) / WK;
+    // a run that starts inside a group (G > 128) touches one group more
+    l.ngw = (uint32_t)((per * kBlockK + G - 1) / G + (G > kBlockK ? 1 : 0));
+    l.sz_bytes = (uint32_t)(NS * l.ngw * 16 * sizeof(SZ));
+    l.x_stride = (uint32_t)((per + 3) / 4 * 1024 + 16);
+    l.wave_bytes = l.sz_bytes + (xlds ? (uint32_t)M * l.x_stride : 0u);
     l.red_bytes = (uint32_t)(WK * NS * MT * 64 * 16);
+    l.regions = (uint32_t)WK * l.wave_bytes;
     return l;
 }
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
 template <int MT, int NS, int WK, int NB, int GS, bool XLDS>
 __global__ void __launch_bounds__(WK * 64)
@@ -88,6 +104,9 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     constexpr int F = GS < 4 ? GS : 4;  // 32-row k-steps per scale group inside a block
     constexpr int NF = 4 / F;            // scale groups per 128-row block
     constexpr int G = 32 * GS;
+    // loads of one batch and of the two batches issued ahead of the loop
+    constexpr int kBatchLoads = NB * (NS + (XLDS ? 0 : 4 * MT));
+    static_assert(2 * kBatchLoads <= 63, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int lane = threadIdx.x & 63;
@@ -101,15 +120,15 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     const int split = blockIdx.y;
     const int bb = split * slice_blocks;
     const int be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
-    const int per = (be - bb + WK - 1) / WK;
-    const int wb = bb + wk * per;
+    const int per = (slice_blocks + WK - 1) / WK;
+    const int wb = bb + wk * per < be ? bb + wk * per : be;
     const int we = wb + per < be ? wb + per : be;
-    const int g0 = bb * kBlockK / G;  // slices start on a group boundary
-    const int ng = ((be - bb) * kBlockK + G - 1) / G;
+    const int gw0 = wb * kBlockK / G;  // groups overlapping the wave's run
+    const int ngw = (we * kBlockK + G - 1) / G - gw0;
 
     const DecodeLds L = decode_lds(M, MT, NS, WK, slice_blocks, G, XLDS);
-    SZ *szl = reinterpret_cast<SZ *>(lds);
-    uint8_t *xl = lds + L.sz_bytes;
+    SZ *szl = reinterpret_cast<SZ *>(lds + wk * L.wave_bytes);
+    uint8_t *xl = lds + wk * L.wave_bytes + L.sz_bytes;
 
     __amdgpu_buffer_rsrc_t rw[NS];
 #pragma unroll
@@ -171,7 +190,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                 for (int mt = 0; mt < MT; ++mt) {
                     if constexpr (XLDS)
                         a[t][mt] = *reinterpret_cast<const half8 *>(
-                            xl + xoff[mt] + ((b - bb) * kBlockK + t * 32) * 2);
+                            xl + xoff[mt] + ((b - wb) * kBlockK + t * 32) * 2);
                     else
                         a[t][mt] = bt.a[i][t][mt];
                 }
@@ -183,7 +202,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 #pragma unroll
                 for (int f = 0; f < NF; ++f) {
                     const int g = (b * 4 + f * F) / GS;
-                    const SZ sz = szl[(j * ng + (g - g0)) * 16 + col];
+                    const SZ sz = szl[(j * (int)L.ngw + (g - gw0)) * 16 + col];
                     const uint32_t nb_lo = sz.nb;
                     const uint32_t nb_hi = ((nb_lo & 0x000F000Fu) << 4) | 0xE400E400u;
                     floatx4 acc_lo[MT], acc_hi[MT];
@@ -216,44 +235,34 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         }
     };
 
-    // The first two batches go out before the staging so that their latency
-    // overlaps it.
-    Batch b0, b1;
-    int b = wb;
-    if (b < we) load(b, b0);
-    if (b + NB < we) load(b + NB, b1);
-
-    // ---- staging: the scale/zero records of the slice, [NS][ng][16], and in
-    // LDS-X mode the slice's rows of X. A record unit is half a group record
-    // (8 columns: 16 bytes of scales and 4 bytes of zero codes), an X unit 16
-    // bytes of one row. One round issues the loads of up to SU record units
-    // and XU X units per thread (whole waves past the end skip theirs), waits
-    // once for everything issued so far, the weight batches included (vector
-    // loads complete in order, so that costs nothing extra), and writes them
-    // to LDS; units beyond that round (long slices only) follow one by one.
-    {
-        constexpr int T = WK * 64, SU = 1, XU = XLDS ? 2 : 1;
-        const int tid = (int)threadIdx.x;
+    if (wb < we) {  // uniform per wave; waves without blocks only join the reduction
+        // ---- staging into the wave's own LDS region: the records of its
+        // groups and (LDS-X mode) its rows of X. These loads go out before the
+        // first two weight batches, so waiting for them leaves the weight
+        // loads in flight (vector loads complete in order). A record unit is
+        // half a group record (8 columns: 16 bytes of scales, 4 bytes of zero
+        // codes), one per lane; units past the first 64 (long runs only)
+        // follow after a full wait.
         const int nsv = nstrip - strip0 < NS ? nstrip - strip0 : NS;  // strips that exist
         const uint8_t *srec = packed + weight_bytes(K, N) + (size_t)strip0 * ngrp * 32;
         const uint8_t *zrec = packed + weight_bytes(K, N) + scale_bytes(K, N, G) + (size_t)strip0 * ngrp * 8;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(srec, (uint32_t)(nsv * ngrp * 32));
         const __amdgpu_buffer_rsrc_t rz = make_rsrc(zrec, (uint32_t)(nsv * ngrp * 8));
-        const int units = NS * ng * 2;
-        const int kc = (be - bb) * kBlockK / 8;  // X units per row
-        const int xunits = XLDS ? M * kc : 0;
+        const int su_n = NS * ngw * 2;
 
         auto sz_load = [&](int u, u32x4 &sv, uint32_t &zv) {
-            const int j = u / (ng * 2), r = u % (ng * 2);
-            const bool ok = u < units && j < nsv;
-            const uint32_t rec = (uint32_t)(j * ngrp + g0 + (r >> 1));
+            const int j = u / (ngw * 2), r = u % (ngw * 2);
+            const bool ok = u < su_n && j < nsv;
+            const uint32_t rec = (uint32_t)(j * ngrp + gw0 + (r >> 1));
             sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                rs, ok ? rec * 32u + (r & 1) * 16u : kOobOffset, 0, 0));
             zv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz, ok ? rec * 8u + (r & 1) * 4u : kOobOffset,
                                                                0, 0);
         };
         auto sz_store = [&](int u, const u32x4 &sv, uint32_t zv) {
-            u32x4 *dst = reinterpret_cast<u32x4 *>(szl + (u >> 1) * 16 + (u & 1) * 8);
+            if (u >= su_n) return;
+            const int j = u / (ngw * 2), r = u % (ngw * 2);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(szl + (j * (int)L.ngw + (r >> 1)) * 16 + (r & 1) * 8);
 #pragma unroll
             for (int c2 = 0; c2 < 4; ++c2) {
                 u32x4 rec2;
@@ -267,56 +276,47 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                 dst[c2] = rec2;
             }
         };
-        auto x_load = [&](int e) {
-            const int r = e / kc, c = e % kc;
-            const uint32_t off = e < xunits ? (uint32_t)(r * K * 2 + bb * kBlockK * 2 + c * 16) : kOobOffset;
-            return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
-        };
-        auto x_store = [&](int e, const u32x4 &v) {
-            const int r = e / kc, c = e % kc;
-            *reinterpret_cast<u32x4 *>(xl + r * L.x_stride + c * 16) = v;
-        };
 
-        u32x4 sv[SU], xv[XU];
-        uint32_t zv[SU];
-#pragma unroll
-        for (int i = 0; i < SU; ++i)
-            if (i * T + wk * 64 < units) sz_load(i * T + tid, sv[i], zv[i]);
+        u32x4 sv0;
+        uint32_t zv0;
+        sz_load(lane, sv0, zv0);
         if constexpr (XLDS) {
-#pragma unroll
-            for (int i = 0; i < XU; ++i)
-                if (i * T + wk * 64 < xunits) xv[i] = x_load(i * T + tid);
+            // row r, chunk c: blocks [wb + 4c, wb + 4c + 4) of row r; lanes
+            // past the run read zeros into the slot's spare bytes
+            const int run = we - wb, nch = (run + 3) / 4;
+            for (int r = 0; r < M; ++r)
+                for (int c = 0; c < nch; ++c) {
+                    const bool ok = c * 64 + lane < run * 16;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rx, (lds_void *)(xl + r * L.x_stride + c * 1024), 16,
+                        ok ? (uint32_t)(r * K * 2 + lane * 16) : kOobOffset, (wb * kBlockK + c * 512) * 2, 0, 0);
+                }
         }
-        asm volatile("" ::: "memory");       // no load sinks below this point
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-#pragma unroll
-        for (int i = 0; i < SU; ++i)
-            if (i * T + tid < units) sz_store(i * T + tid, sv[i], zv[i]);
-        if constexpr (XLDS) {
-#pragma unroll
-            for (int i = 0; i < XU; ++i)
-                if (i * T + tid < xunits) x_store(i * T + tid, xv[i]);
-        }
-        for (int u = SU * T + tid; u < units; u += T) {
+        asm volatile("" ::: "memory");  // staging loads go out first
+        Batch b0, b1;
+        int b = wb;
+        load(b, b0);
+        asm volatile("" ::: "memory");  // keep the two batches apart in issue order
+        load(b + NB, b1);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBatchLoads));  // staging loads landed
+
+        sz_store(lane, sv0, zv0);
+        for (int u = 64 + lane; u - lane < su_n; u += 64) {
             u32x4 a;
             uint32_t z;
             sz_load(u, a, z);
             sz_store(u, a, z);
         }
-        if constexpr (XLDS) {
-            for (int e = XU * T + tid; e < xunits; e += T) x_store(e, x_load(e));
-        }
-    }
-    // Nothing is outstanding from here on but the weight batches of the
-    // main loop.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+        // the region is private to the wave: order its writes before its reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // Two batches in flight: consume one, refill it two batches ahead. All
-    // rounds but the last refill unconditionally (only the final refill can
-    // reach past the run, and those blocks are out of range); the last round
-    // only consumes.
-    if (b < we) {
+        // Two batches in flight: consume one, refill it two batches ahead.
+        // All rounds but the last refill unconditionally (only the final
+        // refill can reach past the run, and those blocks are out of range);
+        // the last round only consumes.
         const int rounds = (we - b + 2 * NB - 1) / (2 * NB);
         for (int r = 1; r < rounds; ++r, b += 2 * NB) {
             compute(b, b0);
@@ -329,8 +329,8 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     }
 
     // ---- add the WK partial tiles of each strip in LDS, run 0 first
-    __syncthreads();  // every wave is done with the staged X
-    floatx4 *red = reinterpret_cast<floatx4 *>(xl);  // [WK][NS][MT][64]
+    __syncthreads();  // every wave is done with its region
+    floatx4 *red = reinterpret_cast<floatx4 *>(lds);  // [WK][NS][MT][64]
 #pragma unroll
     for (int j = 0; j < NS; ++j)
 #pragma unroll
@@ -356,14 +356,32 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     }
 }
 
-// Y = sum over s of part[s] (split order), fp32 -> fp16.
-__global__ void __launch_bounds__(256)
+// Y = sum over s of part[s] in split order, fp32 -> fp16. Each thread owns
+// four consecutive outputs and loads up to eight partials before adding any,
+// so the reduction costs one memory round trip per eight splits instead of
+// one per split; the additions still run in split order (bitwise equal to a
+// plain loop).
+__global__ void __launch_bounds__(64)
 splitk_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ Y, int64_t MN, int S) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < MN;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        float v = 0.f;
-        for (int s = 0; s < S; ++s) v += part[(size_t)s * MN + i];
-        Y[i] = f32_to_f16_bits(v);
+    typedef float floatx4_t __attribute__((ext_vector_type(4)));
+    const int64_t n4 = MN / 4;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const floatx4_t *p = reinterpret_cast<const floatx4_t *>(part) + i;
+        floatx4_t v = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < S; s0 += 8) {
+            floatx4_t t[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) t[u] = p[(s0 + u) * n4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) v += t[u];
+        }
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f32_to_f16_bits(v[e]);
+        reinterpret_cast<uint2 *>(Y)[i] = uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                               (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
     }
 }
 
@@ -413,6 +431,8 @@ Plan base_plan(int M, int N, int K) {
     if (ens == 1 || ens == 2 || ens == 4) p.ns = ens;
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
     if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1)) p.wk = ewk;
+    // no more waves than blocks of K (idle waves would still hold LDS)
+    while (p.wk > 4 && p.wk > nblk) p.wk /= 2;
     // the cross-wave reduction buffer must leave room for the staged records
     while (p.wk * p.ns * p.mt * 64 * 16 > 32 * 1024 && p.wk > 4) p.wk /= 2;
     while (p.wk * p.ns * p.mt * 64 * 16 > 32 * 1024 && p.ns > 1) p.ns /= 2;
@@ -545,10 +565,10 @@ hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N,
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e = launch_plan(X, packed, M, N, K, G, Y, part, p, stream);
     if (e != hipSuccess || p.splits <= 1) return e;
-    const int64_t MN = (int64_t)M * N;
-    int64_t blocks = (MN + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, Y, MN,
+    const int64_t MN = (int64_t)M * N;  // a multiple of 16
+    int64_t blocks = (MN / 4 + 63) / 64;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, part, Y, MN,
                        p.splits);
     return hipGetLastError();
 }

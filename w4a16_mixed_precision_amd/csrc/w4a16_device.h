@@ -12,6 +12,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;  // LDS pointer for direct buffer loads
 
 // Geometry of the packed weight tiles: 16 output columns ("strip") by 128
 // rows of K ("block") = 1024 bytes, read by one wave64 as 16 bytes per lane.

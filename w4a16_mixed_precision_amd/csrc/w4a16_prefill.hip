@@ -40,7 +40,6 @@
 namespace w4a16 {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Packed weights of one K block for the wave's NSW strips, kept raw until
 // use (combining them right after the load would make the compiler wait on
