@@ -173,8 +173,8 @@ def w4a16_gemm(X, packed, N: int, K: int, G: int, Y=None, stream=None):
 
 def w4a16_gemm_ex(X, packed, N: int, K: int, G: int, Y=None, workspace=None,
                   path: int = W4A16_PATH_AUTO, splits: int = 0, stream=None):
-    """w4a16_gemm with an explicit plan and caller-owned workspace (a zeroed
-    uint8 device tensor of at least w4a16_workspace_bytes(...) bytes)."""
+    """w4a16_gemm with an explicit plan and caller-owned workspace (a uint8
+    device tensor of at least w4a16_workspace_bytes(...) bytes, any contents)."""
     import torch
     M = X.shape[0]
     if X.dim() != 2 or X.shape[1] != K:

@@ -24,15 +24,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libw4a16.so)")
 
 
-def build_library(verbose: bool = False, extra_flags=None) -> str:
-    # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU instructions.
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(HERE, "..", "include")]
-    cmd += list(extra_flags or [])
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd += ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,6 +34,25 @@ def build_library(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build_library(verbose: bool = False, extra_flags=None) -> str:
+    # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU instructions.
+    flags = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(HERE, "..", "include")] + list(extra_flags or [])
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+    # one hipcc per source, in parallel (the decode kernels dominate)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        futs = [ex.submit(_run, [hipcc()] + flags + ["-c", os.path.join(CSRC, s), "-o", o], verbose)
+                for s, o in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     # every kernel's host launch stub must resolve: load the library once
     try:
         ctypes.CDLL(tmp)

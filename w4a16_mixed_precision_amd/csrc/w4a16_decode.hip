@@ -96,13 +96,79 @@ __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, i
 // are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
+// One 128-row block of NS strips: for each of the block's scale groups the
+// matrix instruction runs over its 32-row steps with exact integer weights
+// (q - z, or 16 (q - z) for the high-nibble steps), and the group's partial
+// products are scaled into acc in fp32. rec points at the records of the
+// first strip; strip j's records start rec_stride groups later, and gbase is
+// the group index of the first record.
+template <int MT, int NS, int GS>
+__device__ __forceinline__ void block_mma(const half8 (&a)[4][MT], const u32x4 (&w)[NS], const SZ *rec,
+                                          int rec_stride, int b, int gbase, int col, uint32_t magic,
+                                          floatx4 (&acc)[MT][NS]) {
+    constexpr int F = GS < 4 ? GS : 4;  // 32-row k-steps per scale group inside a block
+    constexpr int NF = 4 / F;            // scale groups per 128-row block
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        u32x4 w8;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) w8[v] = w[j][v] >> 8;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int g = (b * 4 + f * F) / GS;
+            const SZ sz = rec[(j * rec_stride + (g - gbase)) * 16 + col];
+            const uint32_t nb_lo = sz.nb;
+            const uint32_t nb_hi = ((nb_lo & 0x000F000Fu) << 4) | 0xE400E400u;
+            floatx4 acc_lo[MT], acc_hi[MT];
+            bool lo_used = false, hi_used = false;
+#pragma unroll
+            for (int tt = 0; tt < F; ++tt) {
+                const int t = f * F + tt;
+                const half8 bq = dequant_qz(t, w[j], w8, nb_lo, nb_hi, magic);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (t < 2)
+                        acc_lo[mt] = mfma16x16x32(a[t][mt], bq, lo_used ? acc_lo[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
+                    else
+                        acc_hi[mt] = mfma16x16x32(a[t][mt], bq, hi_used ? acc_hi[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
+                }
+                if (t < 2) lo_used = true; else hi_used = true;
+            }
+            const float sc = sz.sc, sc16 = sz.sc * 0.0625f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (lo_used) acc[mt][j][e] = __builtin_fmaf(sc, acc_lo[mt][e], acc[mt][j][e]);
+                    if (hi_used) acc[mt][j][e] = __builtin_fmaf(sc16, acc_hi[mt][e], acc[mt][j][e]);
+                }
+        }
+    }
+}
+
+// Converts half a group record (8 columns: 8 fp16 scales, 8 four-bit zero
+// codes) into 8 LDS records.
+__device__ __forceinline__ void store_records(SZ *dst, const u32x4 &sv, uint32_t zv) {
+    u32x4 *d = reinterpret_cast<u32x4 *>(dst);
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+        u32x4 rec2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t hz = 0xE400u | ((zv >> (4 * (2 * c2 + h))) & 15u);
+            rec2[2 * h] = hz | (hz << 16);
+            rec2[2 * h + 1] =
+                __builtin_bit_cast(uint32_t, (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[c2] >> (16 * h))));
+        }
+        d[c2] = rec2;
+    }
+}
+
 template <int MT, int NS, int WK, int NB, int GS, bool XLDS>
 __global__ void __launch_bounds__(WK * 64)
 decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
               uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int S,
               int slice_blocks) {
-    constexpr int F = GS < 4 ? GS : 4;  // 32-row k-steps per scale group inside a block
-    constexpr int NF = 4 / F;            // scale groups per 128-row block
     constexpr int G = 32 * GS;
     // loads of one batch and of the two batches issued ahead of the loop
     constexpr int kBatchLoads = NB * (NS + (XLDS ? 0 : 4 * MT));
@@ -194,44 +260,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                     else
                         a[t][mt] = bt.a[i][t][mt];
                 }
-#pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                u32x4 w8;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) w8[v] = bt.w[i][j][v] >> 8;
-#pragma unroll
-                for (int f = 0; f < NF; ++f) {
-                    const int g = (b * 4 + f * F) / GS;
-                    const SZ sz = szl[(j * (int)L.ngw + (g - gw0)) * 16 + col];
-                    const uint32_t nb_lo = sz.nb;
-                    const uint32_t nb_hi = ((nb_lo & 0x000F000Fu) << 4) | 0xE400E400u;
-                    floatx4 acc_lo[MT], acc_hi[MT];
-                    bool lo_used = false, hi_used = false;
-#pragma unroll
-                    for (int tt = 0; tt < F; ++tt) {
-                        const int t = f * F + tt;
-                        const half8 bq = dequant_qz(t, bt.w[i][j], w8, nb_lo, nb_hi, magic);
-#pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            if (t < 2)
-                                acc_lo[mt] = mfma16x16x32(a[t][mt], bq,
-                                                          lo_used ? acc_lo[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
-                            else
-                                acc_hi[mt] = mfma16x16x32(a[t][mt], bq,
-                                                          hi_used ? acc_hi[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
-                        }
-                        if (t < 2) lo_used = true; else hi_used = true;
-                    }
-                    const float sc = sz.sc, sc16 = sz.sc * 0.0625f;
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (lo_used) acc[mt][j][e] = __builtin_fmaf(sc, acc_lo[mt][e], acc[mt][j][e]);
-                            if (hi_used) acc[mt][j][e] = __builtin_fmaf(sc16, acc_hi[mt][e], acc[mt][j][e]);
-                        }
-                }
-            }
+            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngw, b, gw0, col, magic, acc);
         }
     };
 
@@ -262,19 +291,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         auto sz_store = [&](int u, const u32x4 &sv, uint32_t zv) {
             if (u >= su_n) return;
             const int j = u / (ngw * 2), r = u % (ngw * 2);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(szl + (j * (int)L.ngw + (r >> 1)) * 16 + (r & 1) * 8);
-#pragma unroll
-            for (int c2 = 0; c2 < 4; ++c2) {
-                u32x4 rec2;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t hz = 0xE400u | ((zv >> (4 * (2 * c2 + h))) & 15u);
-                    rec2[2 * h] = hz | (hz << 16);
-                    rec2[2 * h + 1] = __builtin_bit_cast(
-                        uint32_t, (float)__builtin_bit_cast(_Float16, (uint16_t)(sv[c2] >> (16 * h))));
-                }
-                dst[c2] = rec2;
-            }
+            store_records(szl + (j * (int)L.ngw + (r >> 1)) * 16 + (r & 1) * 8, sv, zv);
         };
 
         u32x4 sv0;
@@ -356,6 +373,194 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     }
 }
 
+// LDS of the strip-parallel kernel: the slice's rows of X, shared by all
+// waves, [M][xs] (whole KiB chunks per row plus 16 bytes of bank padding),
+// then one record region per wave, [NS][ngc][16].
+struct SpLds {
+    uint32_t xs, x_bytes, ngc, rec_bytes, total;
+};
+
+__host__ __device__ inline SpLds sp_lds(int M, int NS, int WK, int slice_blocks, int G) {
+    SpLds l;
+    l.xs = (uint32_t)((slice_blocks + 3) / 4 * 1024 + 16);
+    l.x_bytes = (uint32_t)M * l.xs;
+    l.ngc = (uint32_t)((slice_blocks * kBlockK + G - 1) / G);  // slices start on a group boundary
+    l.rec_bytes = (uint32_t)(NS * l.ngc * 16 * sizeof(SZ));
+    l.total = l.x_bytes + (uint32_t)WK * l.rec_bytes;
+    return l;
+}
+
+// Strip-parallel decode kernel: the WK waves of a workgroup take different
+// strips (NS each) over the same slice of K, so the slice's rows of X are
+// staged in LDS once and feed WK x NS strips, and no cross-wave reduction is
+// needed. Each wave streams its strips' tiles of the slice with two batches
+// in flight, as in decode_kernel; with S > 1 slices the fp32 partials go to
+// the workspace for splitk_reduce_kernel.
+template <int MT, int NS, int WK, int NB, int GS>
+__global__ void __launch_bounds__(WK * 64)
+decode_sp_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
+                 uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int S,
+                 int slice_blocks) {
+    constexpr int G = 32 * GS;
+    constexpr int kBatchLoads = NB * NS;
+    static_assert(2 * kBatchLoads <= 63, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int nblk = K / kBlockK;
+    const int ngrp = K / G;
+    const int nstrip = N / kStripCols;
+    const int strip0 = (blockIdx.x * WK + wk) * NS;  // this wave's first strip
+    const int split = blockIdx.y;
+    const int bb = split * slice_blocks;
+    const int be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
+    const int g0 = bb * kBlockK / G;
+    const int ng = (be * kBlockK + G - 1) / G - g0;
+
+    const SpLds L = sp_lds(M, NS, WK, slice_blocks, G);
+    uint8_t *xl = lds;
+    SZ *szl = reinterpret_cast<SZ *>(lds + L.x_bytes + wk * L.rec_bytes);
+
+    bool valid[NS];
+    __amdgpu_buffer_rsrc_t rw[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        valid[j] = strip0 + j < nstrip;
+        const int s = valid[j] ? strip0 + j : 0;
+        rw[j] = make_rsrc(packed + (size_t)s * nblk * kTileBytes, (uint32_t)nblk * kTileBytes);
+    }
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
+    uint32_t xoff[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 16 + col;  // rows >= M read row M-1: never stored
+        xoff[mt] = (uint32_t)((row < M ? row : M - 1) * L.xs + kq * 16);
+    }
+    const uint32_t magic = kMagic;
+
+    floatx4 acc[MT][NS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    struct Batch {
+        u32x4 w[NB][NS];
+    };
+    // blocks past the slice and strips past N load from the out-of-range offset
+    auto load = [&](int b0, Batch &bt) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                bt.w[i][j] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rw[j], (b0 + i < be && valid[j]) ? (uint32_t)lane * 16u : kOobOffset,
+                               (b0 + i) * kTileBytes, 0));
+    };
+    auto compute = [&](int b0, const Batch &bt) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int b = b0 + i;
+            if (b >= be) break;
+            half8 a[4][MT];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    a[t][mt] = *reinterpret_cast<const half8 *>(xl + xoff[mt] + ((b - bb) * kBlockK + t * 32) * 2);
+            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngc, b, g0, col, magic, acc);
+        }
+    };
+
+    // ---- staging. X rows of the slice, cooperatively: instruction i moves
+    // chunk i % nch (blocks 4c..4c+3 of the slice) of row i / nch, lanes past
+    // the slice reading zeros into the row's spare bytes. Records of the
+    // wave's own strips: one unit (half a group record) per lane, units past
+    // the first 64 after a full wait. All of it is issued before the first two
+    // weight batches, and the wave waits for it alone.
+    const int run = be - bb, nch = (run + 3) / 4;
+    for (int i = wk; i < M * nch; i += WK) {
+        const int r = i / nch, c = i % nch;
+        const bool ok = c * 64 + lane < run * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xl + r * L.xs + c * 1024), 16,
+                                                 ok ? (uint32_t)(r * K * 2 + lane * 16) : kOobOffset,
+                                                 (bb * kBlockK + c * 512) * 2, 0, 0);
+    }
+    const int nsv = strip0 >= nstrip ? 0 : (nstrip - strip0 < NS ? nstrip - strip0 : NS);
+    const int s0 = strip0 < nstrip ? strip0 : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(packed + weight_bytes(K, N) + (size_t)s0 * ngrp * 32, (uint32_t)(nsv * ngrp * 32));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(
+        packed + weight_bytes(K, N) + scale_bytes(K, N, G) + (size_t)s0 * ngrp * 8, (uint32_t)(nsv * ngrp * 8));
+    const int su_n = NS * ng * 2;
+    auto sz_load = [&](int u, u32x4 &sv, uint32_t &zv) {
+        const int j = u / (ng * 2), r = u % (ng * 2);
+        const bool ok = u < su_n && j < nsv;
+        const uint32_t rec = (uint32_t)(j * ngrp + g0 + (r >> 1));
+        sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, ok ? rec * 32u + (r & 1) * 16u : kOobOffset, 0, 0));
+        zv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz, ok ? rec * 8u + (r & 1) * 4u : kOobOffset, 0, 0);
+    };
+    auto sz_store = [&](int u, const u32x4 &sv, uint32_t zv) {
+        if (u >= su_n) return;
+        const int j = u / (ng * 2), r = u % (ng * 2);
+        store_records(szl + (j * (int)L.ngc + (r >> 1)) * 16 + (r & 1) * 8, sv, zv);
+    };
+    u32x4 sv0;
+    uint32_t zv0;
+    sz_load(lane, sv0, zv0);
+    asm volatile("" ::: "memory");  // staging loads go out first
+    Batch b0, b1;
+    int b = bb;
+    load(b, b0);
+    asm volatile("" ::: "memory");  // keep the two batches apart in issue order
+    load(b + NB, b1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBatchLoads));  // staging loads landed
+    sz_store(lane, sv0, zv0);
+    for (int u = 64 + lane; u - lane < su_n; u += 64) {
+        u32x4 sa;
+        uint32_t za;
+        sz_load(u, sa, za);
+        sz_store(u, sa, za);
+    }
+    __syncthreads();  // X is shared by the workgroup
+
+    if (nsv > 0) {
+        const int rounds = (be - b + 2 * NB - 1) / (2 * NB);
+        for (int r = 1; r < rounds; ++r, b += 2 * NB) {
+            compute(b, b0);
+            load(b + 2 * NB, b0);
+            compute(b + NB, b1);
+            load(b + 3 * NB, b1);
+        }
+        compute(b, b0);
+        compute(b + NB, b1);
+
+        // lane (col, kq) holds rows 4 kq + e of column col of every strip
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if (!valid[j]) continue;
+            const size_t n = (size_t)(strip0 + j) * kStripCols + col;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = mt * 16 + kq * 4 + e;
+                    if (r >= M) continue;
+                    if (S == 1)
+                        Y[(size_t)r * N + n] = f32_to_f16_bits(acc[mt][j][e]);
+                    else
+                        part[((size_t)split * M + r) * N + n] = acc[mt][j][e];
+                }
+        }
+    }
+}
+
 // Y = sum over s of part[s] in split order, fp32 -> fp16. Each thread owns
 // four consecutive outputs and loads up to eight partials before adding any,
 // so the reduction costs one memory round trip per eight splits instead of
@@ -392,7 +597,8 @@ constexpr uint32_t kLdsBudget = 64 * 1024;
 
 struct Plan {
     int mt, ns, wk;
-    bool xlds;
+    bool sp;    // strip-parallel kernel
+    bool xlds;  // decode_kernel with LDS-staged X
     bool fixed_splits;  // automatic plan keeps K unsplit
     int splits, slice_blocks;
 };
@@ -402,42 +608,55 @@ int env_int(const char *name, int dflt) {
     return v ? atoi(v) : dflt;
 }
 
-// Launch shape. LDS-staged X with one strip per wave for M <= 4; for
-// larger M register X shared by NS strips per wave, the shape picked from
-// measurements on MI355X over the Llama-3-8B/70B decode matrices: narrow N
-// with short K (QKV-like) runs best unsplit with 2 strips x 16 waves, the
-// rest with 4 strips x 8 waves and K split across workgroups where N is
-// narrow. W4A16_DECODE_NS and W4A16_DECODE_WK override NS and WK for tuning
+// Launch shape, picked from graph-timed sweeps on MI355X over the decode
+// matrices of Llama-3-8B (QKV 4096 x 6144, down 14336 x 4096) and Llama-3-70B
+// (gate/up 8192 x 57344, down 28672 x 8192):
+// * M <= 4: LDS-staged X, 8 waves per workgroup, one strip per wave (two
+//   where N is very wide);
+// * short K with narrow N (QKV-like): K unsplit, 2 strips x 8 waves, and for
+//   17 <= M <= 32 the strip-parallel kernel (X staged once per workgroup);
+// * otherwise register X shared by 2 (M <= 8) or 4 strips per wave, K split
+//   across workgroups until there is about one workgroup per CU.
+// W4A16_DECODE_SP, _NS and _WK override the kernel, NS and WK for tuning
 // (instantiated values only).
 Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
     p.xlds = M <= 4;
+    p.sp = false;
     const int nstrip = N / kStripCols, nblk = K / kBlockK;
     const bool short_narrow = nstrip <= 384 && nblk <= 64;
     if (p.xlds) {
-        p.ns = 1;
-        p.wk = nstrip < 512 ? 16 : 8;
-    } else if (short_narrow) {
-        p.ns = 2;
-        p.wk = p.mt == 1 ? 16 : 8;
-    } else {
-        p.ns = (M <= 8 && nstrip >= 2048) ? 2 : 4;
+        p.ns = nstrip >= 2048 ? 2 : 1;
         p.wk = 8;
+    } else if (short_narrow) {
+        p.sp = p.mt == 2;
+        p.ns = 2;
+        p.wk = 8;
+    } else {
+        p.ns = M <= 8 ? 2 : 4;
+        p.wk = p.mt == 1 ? 8 : 4;
     }
     if (p.mt == 4) p.ns = 2;
     p.fixed_splits = !p.xlds && short_narrow;
+    const int esp = env_int("W4A16_DECODE_SP", -1);
+    if (esp == 0 || esp == 1) p.sp = esp == 1 && p.mt <= 2;
+    if (p.sp) p.xlds = false;
     const int ens = env_int("W4A16_DECODE_NS", 0), ewk = env_int("W4A16_DECODE_WK", 0);
     if (ens == 1 || ens == 2 || ens == 4) p.ns = ens;
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
-    if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1)) p.wk = ewk;
+    if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1 && !p.sp)) p.wk = ewk;
+    p.splits = 1;
+    p.slice_blocks = 0;
+    if (p.sp) {
+        if (p.wk == 16) p.wk = 8;
+        return p;
+    }
     // no more waves than blocks of K (idle waves would still hold LDS)
     while (p.wk > 4 && p.wk > nblk) p.wk /= 2;
     // the cross-wave reduction buffer must leave room for the staged records
     while (p.wk * p.ns * p.mt * 64 * 16 > 32 * 1024 && p.wk > 4) p.wk /= 2;
     while (p.wk * p.ns * p.mt * 64 * 16 > 32 * 1024 && p.ns > 1) p.ns /= 2;
-    p.splits = 1;
-    p.slice_blocks = 0;
     return p;
 }
 
@@ -449,21 +668,25 @@ int slice_for(int K, int G, int splits) {
     return (sb + unit - 1) / unit * unit;
 }
 
-bool lds_fits(const Plan &p, int M, int G, int slice_blocks) {
-    return decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xlds).total() <= kLdsBudget;
+uint32_t plan_lds(const Plan &p, int M, int G, int slice_blocks) {
+    return p.sp ? sp_lds(M, p.ns, p.wk, slice_blocks, G).total
+                : decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xlds).total();
 }
+
+bool lds_fits(const Plan &p, int M, int G, int slice_blocks) { return plan_lds(p, M, G, slice_blocks) <= kLdsBudget; }
 
 Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     Plan p = base_plan(M, N, K);
     const int nblk = K / kBlockK;
-    const int tiles = (N / kStripCols + p.ns - 1) / p.ns;
+    const int tiles = (N / kStripCols + p.ns * (p.sp ? p.wk : 1) - 1) / (p.ns * (p.sp ? p.wk : 1));
     if (splits <= 0 && p.fixed_splits) splits = 1;
     if (splits <= 0) {
-        // Narrow N: about two workgroups per CU, keeping two blocks per wave.
+        // Narrow N: about one workgroup per CU, keeping at least two blocks
+        // per wave (decode_kernel) or per slice (strip-parallel kernel).
         splits = 1;
         if (tiles < num_cus) {
-            splits = (2 * num_cus + tiles - 1) / tiles;
-            int cap = nblk / (2 * p.wk);
+            splits = (num_cus + tiles - 1) / tiles;
+            int cap = p.sp ? nblk / 2 : nblk / (2 * p.wk);
             if (cap < 1) cap = 1;
             if (splits > cap) splits = cap;
         }
@@ -473,6 +696,59 @@ Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     p.slice_blocks = slice_for(K, G, splits);
     p.splits = (nblk + p.slice_blocks - 1) / p.slice_blocks;
     return p;
+}
+
+template <int MT, int NS, int WK, int GS>
+hipError_t launch_sp_one(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y,
+                         float *part, const Plan &p, hipStream_t stream) {
+    constexpr int NB = (MT == 1 && NS == 1) ? 2 : 1;
+    const SpLds L = sp_lds(M, NS, WK, p.slice_blocks, 32 * GS);
+    const int tiles = (N / kStripCols + WK * NS - 1) / (WK * NS);
+    hipLaunchKernelGGL((decode_sp_kernel<MT, NS, WK, NB, GS>), dim3(tiles, p.splits), dim3(WK * 64), L.total,
+                       stream, X, packed, Y, part, M, N, K, p.splits, p.slice_blocks);
+    return hipGetLastError();
+}
+
+template <int MT, int NS, int WK>
+hipError_t launch_sp_g(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
+                       float *part, const Plan &p, hipStream_t stream) {
+    switch (G) {
+        case 32: return launch_sp_one<MT, NS, WK, 1>(X, packed, M, N, K, Y, part, p, stream);
+        case 64: return launch_sp_one<MT, NS, WK, 2>(X, packed, M, N, K, Y, part, p, stream);
+        case 128: return launch_sp_one<MT, NS, WK, 4>(X, packed, M, N, K, Y, part, p, stream);
+        case 256: return launch_sp_one<MT, NS, WK, 8>(X, packed, M, N, K, Y, part, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int MT, int NS>
+hipError_t launch_sp_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
+                        float *part, const Plan &p, hipStream_t stream) {
+    if (p.wk == 8) return launch_sp_g<MT, NS, 8>(X, packed, M, N, K, G, Y, part, p, stream);
+    return launch_sp_g<MT, NS, 4>(X, packed, M, N, K, G, Y, part, p, stream);
+}
+
+hipError_t launch_sp(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
+                     float *part, const Plan &p, hipStream_t stream) {
+    switch (p.mt) {
+        case 1:
+            switch (p.ns) {
+                case 1: return launch_sp_wk<1, 1>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_sp_wk<1, 2>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_sp_wk<1, 4>(X, packed, M, N, K, G, Y, part, p, stream);
+            }
+        case 2:
+            switch (p.ns) {
+                case 1: return launch_sp_wk<2, 1>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_sp_wk<2, 2>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_sp_wk<2, 4>(X, packed, M, N, K, G, Y, part, p, stream);
+            }
+        default:
+            switch (p.ns) {
+                case 1: return launch_sp_wk<4, 1>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_sp_wk<4, 2>(X, packed, M, N, K, G, Y, part, p, stream);
+            }
+    }
 }
 
 template <int MT, int NS, int WK, int GS, bool XLDS>
@@ -510,6 +786,7 @@ hipError_t launch_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int
 
 hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                        float *part, const Plan &p, hipStream_t stream) {
+    if (p.sp) return launch_sp(X, packed, M, N, K, G, Y, part, p, stream);
     if (p.xlds) {  // M <= 4
         switch (p.ns) {
             case 1: return launch_wk<1, 1, true>(X, packed, M, N, K, G, Y, part, p, stream);
