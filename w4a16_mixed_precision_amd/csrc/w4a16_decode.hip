@@ -92,6 +92,11 @@ __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, i
     return l;
 }
 
+// Cache policy of the weight loads: non-temporal. Every weight byte is read
+// once per call, so the stream should not evict the kernel's code, X, the
+// scale records or split-K partials from L2.
+constexpr int kWeightLoadPolicy = 2;  // nt
+
 // s_waitcnt immediate that waits until at most n vector memory operations
 // are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
@@ -232,7 +237,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 #pragma unroll
             for (int j = 0; j < NS; ++j)
                 bt.w[i][j] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], wo, (b0 + i) * kTileBytes, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], wo, (b0 + i) * kTileBytes, kWeightLoadPolicy));
             if constexpr (!XLDS) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
@@ -459,7 +464,7 @@ decode_sp_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ pac
                 bt.w[i][j] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                rw[j], (b0 + i < be && valid[j]) ? (uint32_t)lane * 16u : kOobOffset,
-                               (b0 + i) * kTileBytes, 0));
+                               (b0 + i) * kTileBytes, kWeightLoadPolicy));
     };
     auto compute = [&](int b0, const Batch &bt) {
 #pragma unroll
