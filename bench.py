@@ -193,7 +193,7 @@ def recorded_traffic(workload):
 def kernel_name(inst):
     if inst.M > 32:
         return "prefill_kernel"
-    return "decode_kernel"
+    return "decode path"
 
 
 def cpu_baseline(runner, max_macs=4e9, repeats=3):
