@@ -138,6 +138,35 @@ def test_parity_small(M, K, N, G, path, splits):
     assert_parity(Y, oracle.gemm(X, q, z, s, G), f"M={M} K={K} N={N} G={G}")
 
 
+# Decode kernel shapes for 5 <= M <= 16: both ways of feeding X (register
+# A operands, LDS ring) under several workgroup shapes, ragged M, every group
+# size, split and unsplit K. The plan knobs are read at every call.
+DECODE_X = [
+    # (M, K, N, G, splits)
+    (5, 1152, 272, 64, 1),
+    (8, 2048, 1040, 128, 1),
+    (8, 4096, 512, 128, 3),
+    (12, 1024, 400, 32, 2),
+    (13, 640, 336, 64, 0),
+    (16, 2304, 784, 256, 1),
+    (16, 29568, 64, 64, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,G,splits", DECODE_X)
+@pytest.mark.parametrize("xm", [0, 2])
+@pytest.mark.parametrize("ns,wk", [(1, 8), (2, 16), (4, 4)])
+def test_decode_x_modes(monkeypatch, M, K, N, G, splits, xm, ns, wk):
+    monkeypatch.setenv("W4A16_DECODE_XM", str(xm))
+    monkeypatch.setenv("W4A16_DECODE_NS", str(ns))
+    monkeypatch.setenv("W4A16_DECODE_WK", str(wk))
+    say(f"decode X mode {xm} ns={ns} wk={wk}: M={M} K={K} N={N} G={G} splits={splits}")
+    q, z, s, rng = _weights(K, N, G, seed=M * 5 + K + N + G)
+    X = synth.draw_x(rng, M, K)
+    Y = run_gemm(X, pack_dev(q, z, s, G), N, K, G, path=DECODE, splits=splits)
+    assert_parity(Y, oracle.gemm(X, q, z, s, G), f"xm={xm} ns={ns} wk={wk} M={M} K={K} N={N} G={G}")
+
+
 def test_parity_with_activation_outliers_both_paths():
     K, N, G, M = 2048, 512, 128, 48
     q, z, s, idx, rng = synth.draw_weights(K, N, G, seed=5, outliers=True)

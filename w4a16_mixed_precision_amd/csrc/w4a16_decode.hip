@@ -17,12 +17,16 @@
 // * Scales and zeros of the workgroup's strips and slice are staged in LDS
 //   once, already turned into the fp16 pair -(1024 + z) and the fp32 scale,
 //   so the main loop reads them with one LDS load per group and strip.
-// * Activations: for M <= 4 the rows of X in the slice are staged in LDS too
-//   (a few KiB) and every lane reads its A operand from there; for larger M
-//   each wave loads its A operands from global memory once per 32-row step
-//   and uses them for all NS strips, so X costs 4/NS loads per tile.
-//   Rows >= M of the 16-row MFMA tile are padding: their results are never
-//   stored.
+// * Activations, three modes. M <= 4: the rows of X over the wave's run are
+//   staged in LDS before the main loop (a few KiB). M <= 16: each batch of
+//   weight tiles travels with the X rows of its blocks, copied straight into
+//   a two-slot LDS ring by 16-byte buffer->LDS loads that each move four
+//   rows x 256 bytes (whole 128-byte lines). Larger M: each wave loads its A
+//   operands into registers once per 32-row step and uses them for all NS
+//   strips. The per-CU cost of X is the number of cache lines it pulls into
+//   the CU; register A operands use half of each line they touch, the ring
+//   all of it. Rows >= M of the 16-row MFMA tile are padding: their results
+//   are never stored.
 // * Dequantization ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
 //   Engine", section 3, FP16 = (INT4 - ZeroPoint) x Scale): one v_and_or_b32
 //   per pair of codes sets the fp16 exponent field and yields 1024 + q (or
@@ -78,15 +82,20 @@ struct DecodeLds {
     __host__ __device__ uint32_t total() const { return regions > red_bytes ? regions : red_bytes; }
 };
 
+// X modes of decode_kernel
+constexpr int kXReg = 0;  // A operands loaded into registers
+constexpr int kXRun = 1;  // the wave's run of X staged in LDS up front
+// 8 or 16: the X rows of each batch's blocks in an LDS ring of that many rows
+
 __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, int slice_blocks, int G,
-                                                 bool xlds) {
+                                                 int xm) {
     DecodeLds l;
     const int per = (slice_blocks + WK - 1) / WK;
     // a run that starts inside a group (G > 128) touches one group more
     l.ngw = (uint32_t)((per * kBlockK + G - 1) / G + (G > kBlockK ? 1 : 0));
     l.sz_bytes = (uint32_t)(NS * l.ngw * 16 * sizeof(SZ));
     l.x_stride = (uint32_t)((per + 3) / 4 * 1024 + 16);
-    l.wave_bytes = l.sz_bytes + (xlds ? (uint32_t)M * l.x_stride : 0u);
+    l.wave_bytes = l.sz_bytes + (xm == kXRun ? (uint32_t)M * l.x_stride : 0u);
     l.red_bytes = (uint32_t)(WK * NS * MT * 64 * 16);
     l.regions = (uint32_t)WK * l.wave_bytes;
     return l;
@@ -100,6 +109,8 @@ constexpr int kWeightLoadPolicy = 2;  // nt
 // s_waitcnt immediate that waits until at most n vector memory operations
 // are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate that waits for all LDS (and scalar memory) operations
+constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 
 // One 128-row block of NS strips: for each of the block's scale groups the
 // matrix instruction runs over its 32-row steps with exact integer weights
@@ -169,16 +180,30 @@ __device__ __forceinline__ void store_records(SZ *dst, const u32x4 &sv, uint32_t
     }
 }
 
-template <int MT, int NS, int WK, int NB, int GS, bool XLDS>
+template <int MT, int NS, int WK, int NB, int GS, int XM>
 __global__ void __launch_bounds__(WK * 64)
 decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
               uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int S,
               int slice_blocks) {
     constexpr int G = 32 * GS;
+    constexpr bool kRun = XM == kXRun;
+    constexpr bool kRing = XM >= 8;
+    static_assert(!kRing || (MT == 1 && (XM == 8 || XM == 16)), "ring: 8 or 16 rows");
+    // X loads per block: 4 MT register loads, or one ring load per 4 rows
+    constexpr int kXLoads = XM == kXReg ? 4 * MT : (kRing ? XM / 4 : 0);
     // loads of one batch and of the two batches issued ahead of the loop
-    constexpr int kBatchLoads = NB * (NS + (XLDS ? 0 : 4 * MT));
+    constexpr int kBatchLoads = NB * (NS + kXLoads);
     static_assert(2 * kBatchLoads <= 63, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    // Ring mode: slot i of ring0 (ring1) holds X rows [0, XM) of block i of
+    // the batch in flight in b0 (b1), [row][256 bytes] with the sixteen
+    // 16-byte chunks of row r stored at position chunk ^ (r & 15), so the 16
+    // lanes that read one chunk of 16 rows hit 16 different bank groups. Two
+    // arrays, so that the compiler sees that a batch's reads and the other
+    // batch's copies touch different memory.
+    constexpr int kSlot = kRing ? XM * kBlockK * 2 : 16;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kRing ? WK * NB * kSlot : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kRing ? WK * NB * kSlot : 16];
 
     const int lane = threadIdx.x & 63;
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -197,9 +222,11 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     const int gw0 = wb * kBlockK / G;  // groups overlapping the wave's run
     const int ngw = (we * kBlockK + G - 1) / G - gw0;
 
-    const DecodeLds L = decode_lds(M, MT, NS, WK, slice_blocks, G, XLDS);
+    const DecodeLds L = decode_lds(M, MT, NS, WK, slice_blocks, G, XM);
     SZ *szl = reinterpret_cast<SZ *>(lds + wk * L.wave_bytes);
     uint8_t *xl = lds + wk * L.wave_bytes + L.sz_bytes;
+    uint8_t *xr0 = ring0 + wk * NB * kSlot;
+    uint8_t *xr1 = ring1 + wk * NB * kSlot;
 
     __amdgpu_buffer_rsrc_t rw[NS];
 #pragma unroll
@@ -212,10 +239,20 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int row = mt * 16 + col;
-        if constexpr (XLDS)  // rows >= M read row M-1: padding rows are never stored
+        if constexpr (kRun)  // rows >= M read row M-1: padding rows are never stored
             xoff[mt] = (uint32_t)((row < M ? row : M - 1) * L.x_stride + kq * 16);
+        else if constexpr (kRing)  // ring rows >= M hold zeros; rows >= XM repeat rows < XM
+            xoff[mt] = (uint32_t)((row & (XM - 1)) * kBlockK * 2);
         else
             xoff[mt] = (uint32_t)((row * K + kq * 8) * 2);
+    }
+    // ring copies: lane -> row xi * 4 + lane / 16 of a block, 16-byte chunk
+    // (lane & 15) ^ row, written to LDS position lane
+    uint32_t xsrc[4];  // (a size that depends on XM keeps hipcc from emitting the host stub)
+#pragma unroll
+    for (int xi = 0; xi < (kRing ? XM / 4 : 1); ++xi) {
+        const int r = xi * 4 + (lane >> 4);
+        xsrc[xi] = r < M ? (uint32_t)(r * K * 2 + (((lane & 15) ^ (r & 15)) * 16)) : kOobOffset;
     }
     const uint32_t magic = kMagic;
 
@@ -229,16 +266,26 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     // Blocks at or past the end of the wave's run load from the out-of-range
     // offset: no branch, no memory traffic, and the same instruction count
     // on every path. X rows >= M are out of range of X's descriptor too.
-    auto load = [&](int b0, Batch &bt) {
+    auto load = [&](int b0, Batch &bt, uint8_t *xr) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const bool in = b0 + i < we;
             const uint32_t wo = in ? (uint32_t)lane * 16u : kOobOffset;
+            if constexpr (kRing) {
+                // the slots being refilled were read by the previous
+                // compute: those LDS reads complete before the copies start
+                if (i == 0) __builtin_amdgcn_s_waitcnt(kLgkmZero);
+#pragma unroll
+                for (int xi = 0; xi < XM / 4; ++xi)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xr + i * kSlot + xi * 1024), 16,
+                                                             in ? xsrc[xi] : kOobOffset,
+                                                             (b0 + i) * kBlockK * 2, 0, 0);
+            }
 #pragma unroll
             for (int j = 0; j < NS; ++j)
                 bt.w[i][j] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], wo, (b0 + i) * kTileBytes, kWeightLoadPolicy));
-            if constexpr (!XLDS) {
+            if constexpr (XM == kXReg) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -249,7 +296,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
             }
         }
     };
-    auto compute = [&](int b0, const Batch &bt) {
+    auto compute = [&](int b0, const Batch &bt, const uint8_t *xr) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int b = b0 + i;
@@ -259,9 +306,12 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    if constexpr (XLDS)
+                    if constexpr (kRun)
                         a[t][mt] = *reinterpret_cast<const half8 *>(
                             xl + xoff[mt] + ((b - wb) * kBlockK + t * 32) * 2);
+                    else if constexpr (kRing)
+                        a[t][mt] = *reinterpret_cast<const half8 *>(
+                            xr + i * kSlot + xoff[mt] + (((4 * t + kq) ^ col) * 16));
                     else
                         a[t][mt] = bt.a[i][t][mt];
                 }
@@ -302,7 +352,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         u32x4 sv0;
         uint32_t zv0;
         sz_load(lane, sv0, zv0);
-        if constexpr (XLDS) {
+        if constexpr (kRun) {
             // row r, chunk c: blocks [wb + 4c, wb + 4c + 4) of row r; lanes
             // past the run read zeros into the slot's spare bytes
             const int run = we - wb, nch = (run + 3) / 4;
@@ -317,9 +367,9 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         asm volatile("" ::: "memory");  // staging loads go out first
         Batch b0, b1;
         int b = wb;
-        load(b, b0);
+        load(b, b0, xr0);
         asm volatile("" ::: "memory");  // keep the two batches apart in issue order
-        load(b + NB, b1);
+        load(b + NB, b1, xr1);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBatchLoads));  // staging loads landed
 
@@ -341,13 +391,13 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         // the last round only consumes.
         const int rounds = (we - b + 2 * NB - 1) / (2 * NB);
         for (int r = 1; r < rounds; ++r, b += 2 * NB) {
-            compute(b, b0);
-            load(b + 2 * NB, b0);
-            compute(b + NB, b1);
-            load(b + 3 * NB, b1);
+            compute(b, b0, xr0);
+            load(b + 2 * NB, b0, xr0);
+            compute(b + NB, b1, xr1);
+            load(b + 3 * NB, b1, xr1);
         }
-        compute(b, b0);
-        compute(b + NB, b1);
+        compute(b, b0, xr0);
+        compute(b + NB, b1, xr1);
     }
 
     // ---- add the WK partial tiles of each strip in LDS, run 0 first
@@ -599,11 +649,12 @@ inline int decode_mt(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 // ---------------------------------------------------------------- planning
 constexpr uint32_t kLdsBudget = 64 * 1024;
+constexpr uint32_t kLdsMax = 160 * 1024;  // per CU on gfx950
 
 struct Plan {
     int mt, ns, wk;
     bool sp;    // strip-parallel kernel
-    bool xlds;  // decode_kernel with LDS-staged X
+    int xm;     // decode_kernel X mode: kXReg, kXRun, or ring rows (8, 16)
     bool fixed_splits;  // automatic plan keeps K unsplit
     int splits, slice_blocks;
 };
@@ -616,24 +667,41 @@ int env_int(const char *name, int dflt) {
 // Launch shape, picked from graph-timed sweeps on MI355X over the decode
 // matrices of Llama-3-8B (QKV 4096 x 6144, down 14336 x 4096) and Llama-3-70B
 // (gate/up 8192 x 57344, down 28672 x 8192):
-// * M <= 4: LDS-staged X, 8 waves per workgroup, one strip per wave (two
-//   where N is very wide);
-// * short K with narrow N (QKV-like): K unsplit, 2 strips x 8 waves, and for
-//   17 <= M <= 32 the strip-parallel kernel (X staged once per workgroup);
+// * M <= 4: X staged per run in LDS, 8 waves per workgroup, one strip per
+//   wave (two where N is very wide);
+// * 5 <= M <= 16: X through the LDS ring. Short K with narrow N (QKV-like):
+//   K unsplit, 2 strips x 16 waves. Very wide N: 2 strips x 4 waves, plenty
+//   of workgroups. Otherwise about one workgroup per CU with K unsplit for
+//   M <= 8 (16 waves); for larger M twice the strips per workgroup and K
+//   split in two, which halves the X each CU has to read;
+// * 17 <= M <= 32 on QKV-like matrices: the strip-parallel kernel;
 // * otherwise register X shared by 2 (M <= 8) or 4 strips per wave, K split
 //   across workgroups until there is about one workgroup per CU.
-// W4A16_DECODE_SP, _NS and _WK override the kernel, NS and WK for tuning
-// (instantiated values only).
+// W4A16_DECODE_SP, _XM (0: register X, 2: ring), _NS and _WK override the
+// kernel, X mode, NS and WK for tuning (instantiated values only).
 Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
-    p.xlds = M <= 4;
+    p.xm = M <= 4 ? kXRun : (M <= 16 ? (M <= 8 ? 8 : 16) : kXReg);
     p.sp = false;
     const int nstrip = N / kStripCols, nblk = K / kBlockK;
     const bool short_narrow = nstrip <= 384 && nblk <= 64;
-    if (p.xlds) {
+    if (p.xm == kXRun) {
         p.ns = nstrip >= 2048 ? 2 : 1;
         p.wk = 8;
+    } else if (p.xm != kXReg) {
+        if (short_narrow) {
+            p.ns = 2;
+            p.wk = 16;
+        } else if (nstrip >= 1024) {
+            p.ns = 2;
+            p.wk = 4;
+        } else {
+            int ns = nstrip / 256;
+            ns = ns < 1 ? 1 : (ns > 2 ? 2 : ns);
+            p.ns = M <= 8 ? ns : 2 * ns;
+            p.wk = M <= 8 ? 16 : 8;
+        }
     } else if (short_narrow) {
         p.sp = p.mt == 2;
         p.ns = 2;
@@ -643,10 +711,14 @@ Plan base_plan(int M, int N, int K) {
         p.wk = p.mt == 1 ? 8 : 4;
     }
     if (p.mt == 4) p.ns = 2;
-    p.fixed_splits = !p.xlds && short_narrow;
+    p.fixed_splits = p.xm != kXRun && short_narrow;
     const int esp = env_int("W4A16_DECODE_SP", -1);
     if (esp == 0 || esp == 1) p.sp = esp == 1 && p.mt <= 2;
-    if (p.sp) p.xlds = false;
+    if (p.sp) p.xm = kXReg;
+    const int exm = env_int("W4A16_DECODE_XM", -1);
+    if (exm == 0 && p.xm != kXRun) p.xm = kXReg;
+    if (exm == 2 && !p.sp && M > 4 && p.mt == 1) p.xm = M <= 8 ? 8 : 16;
+    if (p.sp) p.xm = kXReg;
     const int ens = env_int("W4A16_DECODE_NS", 0), ewk = env_int("W4A16_DECODE_WK", 0);
     if (ens == 1 || ens == 2 || ens == 4) p.ns = ens;
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
@@ -673,12 +745,25 @@ int slice_for(int K, int G, int splits) {
     return (sb + unit - 1) / unit * unit;
 }
 
-uint32_t plan_lds(const Plan &p, int M, int G, int slice_blocks) {
-    return p.sp ? sp_lds(M, p.ns, p.wk, slice_blocks, G).total
-                : decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xlds).total();
+// Batches of 2 tiles per wave only for single-strip single-tile waves
+// without an LDS ring (the ring holds one block per batch).
+constexpr int decode_nb(int MT, int NS, int XM) { return (NS == 1 && MT == 1 && XM <= kXRun) ? 2 : 1; }
+
+// Static LDS of the ring mode: two rings of WK x NB slots of XM rows.
+uint32_t ring_lds(const Plan &p) {
+    return p.xm >= 8 ? (uint32_t)(2 * p.wk * decode_nb(p.mt, p.ns, p.xm) * p.xm * kBlockK * 2) : 0u;
 }
 
-bool lds_fits(const Plan &p, int M, int G, int slice_blocks) { return plan_lds(p, M, G, slice_blocks) <= kLdsBudget; }
+uint32_t plan_lds(const Plan &p, int M, int G, int slice_blocks) {
+    return p.sp ? sp_lds(M, p.ns, p.wk, slice_blocks, G).total
+                : decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xm).total() + ring_lds(p);
+}
+
+// Plans with an LDS ring run one workgroup per CU and may use all of its
+// LDS; the others keep to a budget that leaves room for two.
+bool lds_fits(const Plan &p, int M, int G, int slice_blocks) {
+    return plan_lds(p, M, G, slice_blocks) <= (p.xm >= 8 ? kLdsMax : kLdsBudget);
+}
 
 Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     Plan p = base_plan(M, N, K);
@@ -756,66 +841,77 @@ hipError_t launch_sp(const uint16_t *X, const uint8_t *packed, int M, int N, int
     }
 }
 
-template <int MT, int NS, int WK, int GS, bool XLDS>
+template <int MT, int NS, int WK, int GS, int XM>
 hipError_t launch_one(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y,
                       float *part, const Plan &p, hipStream_t stream) {
-    constexpr int NB = (NS == 1 && MT == 1) ? 2 : 1;
-    const DecodeLds L = decode_lds(M, MT, NS, WK, p.slice_blocks, 32 * GS, XLDS);
+    constexpr int NB = decode_nb(MT, NS, XM);
+    const DecodeLds L = decode_lds(M, MT, NS, WK, p.slice_blocks, 32 * GS, XM);
     const int tiles = (N / kStripCols + NS - 1) / NS;
-    hipLaunchKernelGGL((decode_kernel<MT, NS, WK, NB, GS, XLDS>), dim3(tiles, p.splits), dim3(WK * 64),
+    hipLaunchKernelGGL((decode_kernel<MT, NS, WK, NB, GS, XM>), dim3(tiles, p.splits), dim3(WK * 64),
                        L.total(), stream, X, packed, Y, part, M, N, K, p.splits, p.slice_blocks);
     return hipGetLastError();
 }
 
-template <int MT, int NS, int WK, bool XLDS>
+template <int MT, int NS, int WK, int XM>
 hipError_t launch_g(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                     float *part, const Plan &p, hipStream_t stream) {
     switch (G) {
-        case 32: return launch_one<MT, NS, WK, 1, XLDS>(X, packed, M, N, K, Y, part, p, stream);
-        case 64: return launch_one<MT, NS, WK, 2, XLDS>(X, packed, M, N, K, Y, part, p, stream);
-        case 128: return launch_one<MT, NS, WK, 4, XLDS>(X, packed, M, N, K, Y, part, p, stream);
-        case 256: return launch_one<MT, NS, WK, 8, XLDS>(X, packed, M, N, K, Y, part, p, stream);
+        case 32: return launch_one<MT, NS, WK, 1, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 64: return launch_one<MT, NS, WK, 2, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 128: return launch_one<MT, NS, WK, 4, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 256: return launch_one<MT, NS, WK, 8, XM>(X, packed, M, N, K, Y, part, p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int MT, int NS, bool XLDS>
+template <int MT, int NS, int XM>
 hipError_t launch_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                      float *part, const Plan &p, hipStream_t stream) {
     if constexpr (MT == 1) {
-        if (p.wk == 16) return launch_g<MT, NS, 16, XLDS>(X, packed, M, N, K, G, Y, part, p, stream);
+        if (p.wk == 16) return launch_g<MT, NS, 16, XM>(X, packed, M, N, K, G, Y, part, p, stream);
     }
-    if (p.wk == 4) return launch_g<MT, NS, 4, XLDS>(X, packed, M, N, K, G, Y, part, p, stream);
-    return launch_g<MT, NS, 8, XLDS>(X, packed, M, N, K, G, Y, part, p, stream);
+    if (p.wk == 4) return launch_g<MT, NS, 4, XM>(X, packed, M, N, K, G, Y, part, p, stream);
+    return launch_g<MT, NS, 8, XM>(X, packed, M, N, K, G, Y, part, p, stream);
 }
 
 hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                        float *part, const Plan &p, hipStream_t stream) {
     if (p.sp) return launch_sp(X, packed, M, N, K, G, Y, part, p, stream);
-    if (p.xlds) {  // M <= 4
+    if (p.xm == kXRun) {  // M <= 4
         switch (p.ns) {
-            case 1: return launch_wk<1, 1, true>(X, packed, M, N, K, G, Y, part, p, stream);
-            case 2: return launch_wk<1, 2, true>(X, packed, M, N, K, G, Y, part, p, stream);
-            default: return launch_wk<1, 4, true>(X, packed, M, N, K, G, Y, part, p, stream);
+            case 1: return launch_wk<1, 1, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
+            case 2: return launch_wk<1, 2, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
+            default: return launch_wk<1, 4, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
+        }
+    }
+    if (p.xm == 8 || p.xm == 16) {  // 5 <= M <= 16
+        const bool r8 = p.xm == 8;
+        switch (p.ns) {
+            case 1: return r8 ? launch_wk<1, 1, 8>(X, packed, M, N, K, G, Y, part, p, stream)
+                              : launch_wk<1, 1, 16>(X, packed, M, N, K, G, Y, part, p, stream);
+            case 2: return r8 ? launch_wk<1, 2, 8>(X, packed, M, N, K, G, Y, part, p, stream)
+                              : launch_wk<1, 2, 16>(X, packed, M, N, K, G, Y, part, p, stream);
+            default: return r8 ? launch_wk<1, 4, 8>(X, packed, M, N, K, G, Y, part, p, stream)
+                               : launch_wk<1, 4, 16>(X, packed, M, N, K, G, Y, part, p, stream);
         }
     }
     switch (p.mt) {
         case 1:
             switch (p.ns) {
-                case 1: return launch_wk<1, 1, false>(X, packed, M, N, K, G, Y, part, p, stream);
-                case 2: return launch_wk<1, 2, false>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_wk<1, 4, false>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 1: return launch_wk<1, 1, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_wk<1, 2, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<1, 4, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
             }
         case 2:
             switch (p.ns) {
-                case 1: return launch_wk<2, 1, false>(X, packed, M, N, K, G, Y, part, p, stream);
-                case 2: return launch_wk<2, 2, false>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_wk<2, 4, false>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 1: return launch_wk<2, 1, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_wk<2, 2, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<2, 4, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
             }
         default:
             switch (p.ns) {
-                case 1: return launch_wk<4, 1, false>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_wk<4, 2, false>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 1: return launch_wk<4, 1, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<4, 2, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
             }
     }
 }
