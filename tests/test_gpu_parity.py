@@ -138,9 +138,10 @@ def test_parity_small(M, K, N, G, path, splits):
     assert_parity(Y, oracle.gemm(X, q, z, s, G), f"M={M} K={K} N={N} G={G}")
 
 
-# Decode kernel shapes for 5 <= M <= 16: both ways of feeding X (register
-# A operands, LDS ring) under several workgroup shapes, ragged M, every group
-# size, split and unsplit K. The plan knobs are read at every call.
+# Decode kernel shapes for 5 <= M <= 32: every way of feeding X (register A
+# operands, LDS ring, strip-parallel kernel) under several workgroup shapes,
+# ragged M, every group size, split and unsplit K. The plan knobs are read at
+# every call.
 DECODE_X = [
     # (M, K, N, G, splits)
     (5, 1152, 272, 64, 1),
@@ -150,14 +151,21 @@ DECODE_X = [
     (13, 640, 336, 64, 0),
     (16, 2304, 784, 256, 1),
     (16, 29568, 64, 64, 0),
+    (20, 1024, 400, 32, 2),
+    (25, 1152, 272, 64, 3),
+    (32, 2304, 784, 256, 1),
+    (32, 4096, 512, 128, 0),
 ]
 
 
 @pytest.mark.parametrize("M,K,N,G,splits", DECODE_X)
-@pytest.mark.parametrize("xm", [0, 2])
+@pytest.mark.parametrize("xm", [0, 2, "sp"])
 @pytest.mark.parametrize("ns,wk", [(1, 8), (2, 16), (4, 4)])
 def test_decode_x_modes(monkeypatch, M, K, N, G, splits, xm, ns, wk):
-    monkeypatch.setenv("W4A16_DECODE_XM", str(xm))
+    if xm == "sp":  # strip-parallel kernel: X of the slice staged once per workgroup
+        monkeypatch.setenv("W4A16_DECODE_SP", "1")
+    else:
+        monkeypatch.setenv("W4A16_DECODE_XM", str(xm))
     monkeypatch.setenv("W4A16_DECODE_NS", str(ns))
     monkeypatch.setenv("W4A16_DECODE_WK", str(wk))
     say(f"decode X mode {xm} ns={ns} wk={wk}: M={M} K={K} N={N} G={G} splits={splits}")

@@ -188,7 +188,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     constexpr int G = 32 * GS;
     constexpr bool kRun = XM == kXRun;
     constexpr bool kRing = XM >= 8;
-    static_assert(!kRing || (MT == 1 && (XM == 8 || XM == 16)), "ring: 8 or 16 rows");
+    static_assert(!kRing || (MT == 1 && XM == 8) || XM == 16 * MT, "ring rows: 8, or 16 per row tile");
     // X loads per block: 4 MT register loads, or one ring load per 4 rows
     constexpr int kXLoads = XM == kXReg ? 4 * MT : (kRing ? XM / 4 : 0);
     // loads of one batch and of the two batches issued ahead of the loop
@@ -241,14 +241,14 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         const int row = mt * 16 + col;
         if constexpr (kRun)  // rows >= M read row M-1: padding rows are never stored
             xoff[mt] = (uint32_t)((row < M ? row : M - 1) * L.x_stride + kq * 16);
-        else if constexpr (kRing)  // ring rows >= M hold zeros; rows >= XM repeat rows < XM
+        else if constexpr (kRing)  // ring rows >= M hold zeros; rows >= XM (M <= 8) repeat rows < 8
             xoff[mt] = (uint32_t)((row & (XM - 1)) * kBlockK * 2);
         else
             xoff[mt] = (uint32_t)((row * K + kq * 8) * 2);
     }
     // ring copies: lane -> row xi * 4 + lane / 16 of a block, 16-byte chunk
     // (lane & 15) ^ row, written to LDS position lane
-    uint32_t xsrc[4];  // (a size that depends on XM keeps hipcc from emitting the host stub)
+    uint32_t xsrc[8];  // (a size that depends on XM keeps hipcc from emitting the host stub)
 #pragma unroll
     for (int xi = 0; xi < (kRing ? XM / 4 : 1); ++xi) {
         const int r = xi * 4 + (lane >> 4);
@@ -669,20 +669,21 @@ int env_int(const char *name, int dflt) {
 // (gate/up 8192 x 57344, down 28672 x 8192):
 // * M <= 4: X staged per run in LDS, 8 waves per workgroup, one strip per
 //   wave (two where N is very wide);
-// * 5 <= M <= 16: X through the LDS ring. Short K with narrow N (QKV-like):
-//   K unsplit, 2 strips x 16 waves. Very wide N: 2 strips x 4 waves, plenty
-//   of workgroups. Otherwise about one workgroup per CU with K unsplit for
-//   M <= 8 (16 waves); for larger M twice the strips per workgroup and K
-//   split in two, which halves the X each CU has to read;
-// * 17 <= M <= 32 on QKV-like matrices: the strip-parallel kernel;
-// * otherwise register X shared by 2 (M <= 8) or 4 strips per wave, K split
-//   across workgroups until there is about one workgroup per CU.
+// * 5 <= M <= 32: X through the LDS ring. Short K with narrow N (QKV-like):
+//   K unsplit, 2 strips x 16 waves (x 4 waves for M > 16). Very wide N: 2
+//   strips x 4 waves, plenty of workgroups. Otherwise about one workgroup
+//   per CU with K unsplit for M <= 8 (16 waves); for larger M twice the
+//   strips per workgroup and K split in two, which halves the X each CU has
+//   to read (4 strips x 4 waves for M > 16);
+// * M > 32: register X shared by 2 strips per wave, K split across
+//   workgroups until there is about one workgroup per CU. The strip-parallel
+//   kernel and register X for smaller M remain available for tuning.
 // W4A16_DECODE_SP, _XM (0: register X, 2: ring), _NS and _WK override the
 // kernel, X mode, NS and WK for tuning (instantiated values only).
 Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
-    p.xm = M <= 4 ? kXRun : (M <= 16 ? (M <= 8 ? 8 : 16) : kXReg);
+    p.xm = M <= 4 ? kXRun : (M <= 16 ? (M <= 8 ? 8 : 16) : (M <= 32 ? 32 : kXReg));
     p.sp = false;
     const int nstrip = N / kStripCols, nblk = K / kBlockK;
     const bool short_narrow = nstrip <= 384 && nblk <= 64;
@@ -690,17 +691,17 @@ Plan base_plan(int M, int N, int K) {
         p.ns = nstrip >= 2048 ? 2 : 1;
         p.wk = 8;
     } else if (p.xm != kXReg) {
-        if (short_narrow) {
+        if (short_narrow || nstrip >= 1024) {
             p.ns = 2;
-            p.wk = 16;
-        } else if (nstrip >= 1024) {
-            p.ns = 2;
-            p.wk = 4;
-        } else {
+            p.wk = short_narrow && p.mt == 1 ? 16 : 4;
+        } else if (p.mt == 1) {
             int ns = nstrip / 256;
             ns = ns < 1 ? 1 : (ns > 2 ? 2 : ns);
             p.ns = M <= 8 ? ns : 2 * ns;
             p.wk = M <= 8 ? 16 : 8;
+        } else {
+            p.ns = 4;
+            p.wk = 4;
         }
     } else if (short_narrow) {
         p.sp = p.mt == 2;
@@ -717,12 +718,16 @@ Plan base_plan(int M, int N, int K) {
     if (p.sp) p.xm = kXReg;
     const int exm = env_int("W4A16_DECODE_XM", -1);
     if (exm == 0 && p.xm != kXRun) p.xm = kXReg;
-    if (exm == 2 && !p.sp && M > 4 && p.mt == 1) p.xm = M <= 8 ? 8 : 16;
+    if (exm == 2 && M > 4 && p.mt <= 2) {
+        p.sp = false;
+        p.xm = M <= 8 ? 8 : 16 * p.mt;
+    }
     if (p.sp) p.xm = kXReg;
     const int ens = env_int("W4A16_DECODE_NS", 0), ewk = env_int("W4A16_DECODE_WK", 0);
     if (ens == 1 || ens == 2 || ens == 4) p.ns = ens;
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
     if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1 && !p.sp)) p.wk = ewk;
+    if (p.mt > 1 && p.wk > 8) p.wk = 8;
     p.splits = 1;
     p.slice_blocks = 0;
     if (p.sp) {
@@ -882,6 +887,13 @@ hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, i
             case 1: return launch_wk<1, 1, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
             case 2: return launch_wk<1, 2, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
             default: return launch_wk<1, 4, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
+        }
+    }
+    if (p.xm == 32) {  // 17 <= M <= 32
+        switch (p.ns) {
+            case 1: return launch_wk<2, 1, 32>(X, packed, M, N, K, G, Y, part, p, stream);
+            case 2: return launch_wk<2, 2, 32>(X, packed, M, N, K, G, Y, part, p, stream);
+            default: return launch_wk<2, 4, 32>(X, packed, M, N, K, G, Y, part, p, stream);
         }
     }
     if (p.xm == 8 || p.xm == 16) {  // 5 <= M <= 16
