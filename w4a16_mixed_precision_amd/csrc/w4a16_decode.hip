@@ -29,12 +29,11 @@
 //   are never stored.
 // * Dequantization ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
 //   Engine", section 3, FP16 = (INT4 - ZeroPoint) x Scale): one v_and_or_b32
-//   per pair of codes sets the fp16 exponent field and yields 1024 + q (or
-//   1024 + 16 q for the two steps stored in the high nibbles); a packed fp16
-//   add of -(1024 + z) (or -(1024 + 16 z)) leaves the exact integer q - z (or
-//   16 (q - z)), which the matrix instruction multiplies with X. The scale
-//   (and the 1/16) is applied in fp32 once per group and column to the
-//   group's partial sum. The integer work of one tile is independent of the
+//   per pair of codes sets the fp16 exponent field and yields 1024 + q (low
+//   nibbles) or 64 + q (high nibbles, no shift needed); a packed fp16 add of
+//   -(1024 + z) or -(64 + z) leaves the exact integer q - z, which the matrix
+//   instruction multiplies with X. The scale is applied in fp32 once per
+//   group and column to the group's partial sum. The integer work of one tile is independent of the
 //   other tiles in flight, so it interleaves with the matrix instructions and
 //   the loads (the pages' ILP point).
 // * Reduction: the WK partial tiles of each strip are added in LDS in fixed
@@ -113,15 +112,15 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 <
 constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 
 // One 128-row block of NS strips: for each of the block's scale groups the
-// matrix instruction runs over its 32-row steps with exact integer weights
-// (q - z, or 16 (q - z) for the high-nibble steps), and the group's partial
-// products are scaled into acc in fp32. rec points at the records of the
-// first strip; strip j's records start rec_stride groups later, and gbase is
-// the group index of the first record.
+// matrix instruction runs over its 32-row steps with the exact integer
+// weights q - z, and the group's partial products are scaled into acc in
+// fp32. rec points at the records of the first strip; strip j's records
+// start rec_stride groups later, and gbase is the group index of the first
+// record.
 template <int MT, int NS, int GS>
 __device__ __forceinline__ void block_mma(const half8 (&a)[4][MT], const u32x4 (&w)[NS], const SZ *rec,
-                                          int rec_stride, int b, int gbase, int col, uint32_t magic,
-                                          floatx4 (&acc)[MT][NS]) {
+                                          int rec_stride, int b, int gbase, int col, uint32_t m_lo,
+                                          uint32_t m_hi, floatx4 (&acc)[MT][NS]) {
     constexpr int F = GS < 4 ? GS : 4;  // 32-row k-steps per scale group inside a block
     constexpr int NF = 4 / F;            // scale groups per 128-row block
 #pragma unroll
@@ -133,31 +132,20 @@ __device__ __forceinline__ void block_mma(const half8 (&a)[4][MT], const u32x4 (
         for (int f = 0; f < NF; ++f) {
             const int g = (b * 4 + f * F) / GS;
             const SZ sz = rec[(j * rec_stride + (g - gbase)) * 16 + col];
-            const uint32_t nb_lo = sz.nb;
-            const uint32_t nb_hi = ((nb_lo & 0x000F000Fu) << 4) | 0xE400E400u;
-            floatx4 acc_lo[MT], acc_hi[MT];
-            bool lo_used = false, hi_used = false;
+            const DequantConsts dc{sz.nb, neg_bias64_from_1024(sz.nb), m_lo, m_hi};
+            floatx4 part[MT];
 #pragma unroll
             for (int tt = 0; tt < F; ++tt) {
                 const int t = f * F + tt;
-                const half8 bq = dequant_qz(t, w[j], w8, nb_lo, nb_hi, magic);
+                const half8 bq = dequant_qz(t, w[j], w8, dc);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    if (t < 2)
-                        acc_lo[mt] = mfma16x16x32(a[t][mt], bq, lo_used ? acc_lo[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
-                    else
-                        acc_hi[mt] = mfma16x16x32(a[t][mt], bq, hi_used ? acc_hi[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
-                }
-                if (t < 2) lo_used = true; else hi_used = true;
+                for (int mt = 0; mt < MT; ++mt)
+                    part[mt] = mfma16x16x32(a[t][mt], bq, tt ? part[mt] : floatx4{0.f, 0.f, 0.f, 0.f});
             }
-            const float sc = sz.sc, sc16 = sz.sc * 0.0625f;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (lo_used) acc[mt][j][e] = __builtin_fmaf(sc, acc_lo[mt][e], acc[mt][j][e]);
-                    if (hi_used) acc[mt][j][e] = __builtin_fmaf(sc16, acc_hi[mt][e], acc[mt][j][e]);
-                }
+                for (int e = 0; e < 4; ++e) acc[mt][j][e] = __builtin_fmaf(sz.sc, part[mt][e], acc[mt][j][e]);
         }
     }
 }
@@ -254,7 +242,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         const int r = xi * 4 + (lane >> 4);
         xsrc[xi] = r < M ? (uint32_t)(r * K * 2 + (((lane & 15) ^ (r & 15)) * 16)) : kOobOffset;
     }
-    const uint32_t magic = kMagic;
+    const uint32_t m_lo = kMagic, m_hi = kMagic64;
 
     floatx4 acc[MT][NS];
 #pragma unroll
@@ -315,7 +303,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                     else
                         a[t][mt] = bt.a[i][t][mt];
                 }
-            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngw, b, gw0, col, magic, acc);
+            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngw, b, gw0, col, m_lo, m_hi, acc);
         }
     };
 
@@ -494,7 +482,7 @@ decode_sp_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ pac
         const int row = mt * 16 + col;  // rows >= M read row M-1: never stored
         xoff[mt] = (uint32_t)((row < M ? row : M - 1) * L.xs + kq * 16);
     }
-    const uint32_t magic = kMagic;
+    const uint32_t m_lo = kMagic, m_hi = kMagic64;
 
     floatx4 acc[MT][NS];
 #pragma unroll
@@ -527,7 +515,7 @@ decode_sp_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ pac
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     a[t][mt] = *reinterpret_cast<const half8 *>(xl + xoff[mt] + ((b - bb) * kBlockK + t * 32) * 2);
-            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngc, b, g0, col, magic, acc);
+            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngc, b, g0, col, m_lo, m_hi, acc);
         }
     };
 

@@ -20,48 +20,9 @@ constexpr int kStripCols = 16;
 constexpr int kBlockK = 128;
 constexpr int kTileBytes = 1024;
 
-// Offsets of the three regions of a packed buffer.
-struct PackedView {
-    const u32x4 *w;       // [N/16][K/128][64 lanes] of 16 bytes
-    const uint16_t *s;    // [N/16][K/G][16] fp16 scales
-    const uint8_t *z;     // [N/16][K/G][8] two 4-bit zeros per byte
-};
-
 __host__ __device__ inline size_t weight_bytes(int64_t K, int64_t N) { return (size_t)(K * N / 2); }
 __host__ __device__ inline size_t scale_bytes(int64_t K, int64_t N, int64_t G) { return (size_t)(2 * N * (K / G)); }
 __host__ __device__ inline size_t zero_bytes(int64_t K, int64_t N, int64_t G) { return (size_t)(N * (K / G) / 2); }
-
-__device__ inline PackedView packed_view(const uint8_t *p, int K, int N, int G) {
-    PackedView v;
-    v.w = reinterpret_cast<const u32x4 *>(p);
-    v.s = reinterpret_cast<const uint16_t *>(p + weight_bytes(K, N));
-    v.z = p + weight_bytes(K, N) + scale_bytes(K, N, G);
-    return v;
-}
-
-// Scale bits and zero code of (strip, group) for column `col` of the strip,
-// combined into one word: bits 0..15 fp16 scale, bits 16..19 zero code.
-__device__ inline uint32_t load_scale_zero(const PackedView &pv, size_t rec, int col) {
-    uint32_t sc = pv.s[rec * 16 + col];
-    uint32_t zc = (pv.z[rec * 8 + (col >> 1)] >> ((col & 1) * 4)) & 15u;
-    return sc | (zc << 16);
-}
-
-// -(1024 + z) and -(1024 + 16 z) as fp16 pairs: 1024 + z is exponent 10
-// with z in the low mantissa bits (0x6400 | z), 1024 + 16 z puts z four bits
-// higher; the sign bit makes them negative.
-__device__ inline uint32_t neg_bias_pair(uint32_t sz) {
-    uint32_t h = 0xE400u | (sz >> 16);
-    return h | (h << 16);
-}
-__device__ inline uint32_t neg_bias16_pair(uint32_t sz) {
-    uint32_t h = 0xE400u | ((sz >> 16) << 4);
-    return h | (h << 16);
-}
-
-__device__ inline float scale_of(uint32_t sz) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
-}
 
 // (x & mask) | magic in one VALU op. gfx9 VOP3 reads at most one scalar
 // operand, so the mask goes in an SGPR and the magic number in a VGPR.
@@ -71,13 +32,22 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
     return r;
 }
 
-// Exponent-OR conversion: a half with exponent field 10 (0x6400) and a code
-// c in its low mantissa bits is exactly 1024 + c, so OR-ing the code into
-// 0x6400 converts it to fp16 without an integer-to-float instruction. Codes
-// sitting four bits higher give 1024 + 16 c, also exact.
+// Exponent-OR conversion: a half with exponent field 10 (0x6400, the value
+// 1024) has a mantissa unit of 1, so OR-ing a code c into its low four bits
+// gives exactly 1024 + c without an integer-to-float instruction. With
+// exponent 6 (0x5400, the value 64) the unit is 1/16, so a code sitting in
+// bits 4..7 gives exactly 64 + c: the high nibble of a byte converts without
+// a shift.
 constexpr uint32_t kMagic = 0x64006400u;
+constexpr uint32_t kMagic64 = 0x54005400u;
 constexpr uint32_t kLoMask = 0x000F000Fu;
 constexpr uint32_t kHiMask = 0x00F000F0u;
+
+// -(64 + z) as an fp16 pair, from the pair -(1024 + z) (0xE400 | z): the z
+// bits move up by four and the exponent becomes that of 64.
+__device__ inline uint32_t neg_bias64_from_1024(uint32_t nb_lo) {
+    return ((nb_lo & kLoMask) << 4) | 0xD400D400u;
+}
 
 __device__ inline half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
 
@@ -91,56 +61,56 @@ __device__ inline half8 pack_h8(half2v r0, half2v r1, half2v r2, half2v r3) {
 // One lane's 16-byte slice of a packed tile holds four words; word v carries
 // the k pair (2v, 2v+1) of each of the four 32-row steps of the tile: steps
 // 0 and 1 in the low nibble of bytes 0/2 and 1/3, steps 2 and 3 in their high
-// nibble (see the layout in include/w4a16.h).
+// nibble (see the layout in include/w4a16.h). With w8[v] = w[v] >> 8 (once
+// per word), step T reads its codes from (T odd ? w8 : w) under the low
+// (T < 2) or high (T >= 2) nibble mask: one shift per word for all four
+// steps.
 //
-// B operand of exact integers for step T: (q - z) for T = 0, 1 and 16 (q - z)
-// for T = 2, 3 (the caller folds the 1/16 into the scale). (1024 + q) -
-// (1024 + z) and (1024 + 16 q) - (1024 + 16 z) are exact in fp16 (all
-// operands in [1024, 1264]). w8[v] = w[v] >> 8, computed once per word.
+// B operand of exact integers q - z for step T: (1024 + q) - (1024 + z) for
+// the low nibbles, (64 + q) - (64 + z) for the high ones; both are exact in
+// fp16 (operands in [1024, 1039] and [64, 79]).
+struct DequantConsts {
+    uint32_t nb_lo;  // -(1024 + z) pair
+    uint32_t nb_hi;  // -(64 + z) pair
+    uint32_t m_lo;   // kMagic, in a VGPR (gfx9 VOP3 reads one scalar operand)
+    uint32_t m_hi;   // kMagic64, likewise
+};
+
 template <int T>
-__device__ inline half8 dequant_qz_step(const u32x4 &w, const u32x4 &w8, uint32_t nb_lo,
-                                        uint32_t nb_hi, uint32_t magic) {
-    const uint32_t mask = (T < 2) ? kLoMask : kHiMask;
-    const uint32_t nb = (T < 2) ? nb_lo : nb_hi;
-    half2v r[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const uint32_t src = (T & 1) ? w8[v] : w[v];
-        r[v] = as_h2(and_or(src, mask, magic)) + as_h2(nb);
-    }
-    return pack_h8(r[0], r[1], r[2], r[3]);
+__device__ inline half2v dequant_pair(const u32x4 &w, const u32x4 &w8, int v, const DequantConsts &c) {
+    const uint32_t src = (T & 1) ? w8[v] : w[v];
+    return as_h2(and_or(src, T < 2 ? kLoMask : kHiMask, T < 2 ? c.m_lo : c.m_hi)) + as_h2(T < 2 ? c.nb_lo : c.nb_hi);
 }
 
-// B operand of fp16 weights for step T: ((1024 + q) - (1024 + z)) * s, the
-// exact q - z rounded once to fp16 by the multiply with s.
 template <int T>
-__device__ inline half8 dequant_w_step(const u32x4 &w, uint32_t nb_lo, uint32_t s2, uint32_t magic) {
-    constexpr int shift = T == 0 ? 0 : (T == 1 ? 8 : (T == 2 ? 4 : 12));
-    half2v r[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const uint32_t src = shift ? (w[v] >> shift) : w[v];
-        r[v] = (as_h2(and_or(src, kLoMask, magic)) + as_h2(nb_lo)) * as_h2(s2);
-    }
-    return pack_h8(r[0], r[1], r[2], r[3]);
+__device__ inline half8 dequant_qz_step(const u32x4 &w, const u32x4 &w8, const DequantConsts &c) {
+    return pack_h8(dequant_pair<T>(w, w8, 0, c), dequant_pair<T>(w, w8, 1, c), dequant_pair<T>(w, w8, 2, c),
+                   dequant_pair<T>(w, w8, 3, c));
+}
+
+// B operand of fp16 weights for step T: the exact q - z rounded once to fp16
+// by the multiply with the scale pair s2.
+template <int T>
+__device__ inline half8 dequant_w_step(const u32x4 &w, const u32x4 &w8, const DequantConsts &c, uint32_t s2) {
+    return pack_h8(dequant_pair<T>(w, w8, 0, c) * as_h2(s2), dequant_pair<T>(w, w8, 1, c) * as_h2(s2),
+                   dequant_pair<T>(w, w8, 2, c) * as_h2(s2), dequant_pair<T>(w, w8, 3, c) * as_h2(s2));
 }
 
 // Runtime-step dispatch for code that loops over steps.
-__device__ inline half8 dequant_w(int t, const u32x4 &w, uint32_t nb_lo, uint32_t s2, uint32_t magic) {
+__device__ inline half8 dequant_w(int t, const u32x4 &w, const u32x4 &w8, const DequantConsts &c, uint32_t s2) {
     switch (t) {
-        case 0: return dequant_w_step<0>(w, nb_lo, s2, magic);
-        case 1: return dequant_w_step<1>(w, nb_lo, s2, magic);
-        case 2: return dequant_w_step<2>(w, nb_lo, s2, magic);
-        default: return dequant_w_step<3>(w, nb_lo, s2, magic);
+        case 0: return dequant_w_step<0>(w, w8, c, s2);
+        case 1: return dequant_w_step<1>(w, w8, c, s2);
+        case 2: return dequant_w_step<2>(w, w8, c, s2);
+        default: return dequant_w_step<3>(w, w8, c, s2);
     }
 }
-__device__ inline half8 dequant_qz(int t, const u32x4 &w, const u32x4 &w8, uint32_t nb_lo,
-                                   uint32_t nb_hi, uint32_t magic) {
+__device__ inline half8 dequant_qz(int t, const u32x4 &w, const u32x4 &w8, const DequantConsts &c) {
     switch (t) {
-        case 0: return dequant_qz_step<0>(w, w8, nb_lo, nb_hi, magic);
-        case 1: return dequant_qz_step<1>(w, w8, nb_lo, nb_hi, magic);
-        case 2: return dequant_qz_step<2>(w, w8, nb_lo, nb_hi, magic);
-        default: return dequant_qz_step<3>(w, w8, nb_lo, nb_hi, magic);
+        case 0: return dequant_qz_step<0>(w, w8, c);
+        case 1: return dequant_qz_step<1>(w, w8, c);
+        case 2: return dequant_qz_step<2>(w, w8, c);
+        default: return dequant_qz_step<3>(w, w8, c);
     }
 }
 

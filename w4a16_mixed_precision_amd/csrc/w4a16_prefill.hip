@@ -22,8 +22,9 @@
 //   16-byte load per lane per strip and K block (the packed order is the
 //   operand order, so there is no run-time swizzle), one block ahead.
 // * Dequantization (section 3 of the same page, FP16 = (INT4 - ZeroPoint) x
-//   Scale): exponent-OR gives 1024 + q, a packed fp16 add of -(1024 + z)
-//   gives q - z exactly, a packed fp16 multiply by s gives the weight
+//   Scale): exponent-OR gives 1024 + q (low nibbles) or 64 + q (high
+//   nibbles, unshifted), a packed fp16 add of -(1024 + z) or -(64 + z) gives
+//   q - z exactly, a packed fp16 multiply by s gives the weight
 //   rounded once to fp16. The B operand of every 16 x 16 x 32 MFMA is
 //   produced this way and reused for all MTW row tiles of the wave.
 // * Split-K: when the tile grid alone cannot fill the GPU, workgroups also
@@ -89,7 +90,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 
     const int m0 = tm * BM;
     const int strip_w = (tn * WN + wn) * NSW;  // first strip of this wave
-    const uint32_t magic = kMagic;
+    const uint32_t m_lo = kMagic, m_hi = kMagic64;
 
     // X: this thread's chunk i of a stage covers row r0(i) + lane/16 of the
     // tile, r0(i) = 4 (i WAVES + wave). One buffer per i starts at that row
@@ -155,6 +156,11 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 
     auto compute = [&](int stage, const Set &w) {
         const uint8_t *st = lds + stage * STAGE;
+        u32x4 w8[NSW];
+#pragma unroll
+        for (int j = 0; j < NSW; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) w8[j][v] = w.w[j][v] >> 8;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             // LDS reads first; the dequantization below covers their latency
@@ -166,7 +172,9 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 #pragma unroll
             for (int j = 0; j < NSW; ++j) {
                 const uint32_t h = 0xE400u | ((w.zb[f][j] >> zsh) & 15u);
-                bw[j] = dequant_w(t, w.w[j], h * 0x10001u, (w.sc[f][j] & 0xFFFFu) * 0x10001u, magic);
+                const uint32_t nb = h * 0x10001u;
+                const DequantConsts dc{nb, neg_bias64_from_1024(nb), m_lo, m_hi};
+                bw[j] = dequant_w(t, w.w[j], w8[j], dc, (w.sc[f][j] & 0xFFFFu) * 0x10001u);
             }
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt)
