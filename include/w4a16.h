@@ -126,7 +126,8 @@ int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int6
  * Workspace bytes w4a16_gemm_ex needs for this shape and plan (`path` one of
  * W4A16_PATH_*, `splits` 0 = automatic, else the number of K splits across
  * workgroups). 0 means the plan needs none. Host-only apart from reading the
- * current device's CU count when `splits` is 0.
+ * current device's CU count (the plan depends on it; without a device the
+ * size is for 256 CUs).
  */
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits);
 

@@ -138,12 +138,14 @@ def test_parity_small(M, K, N, G, path, splits):
     assert_parity(Y, oracle.gemm(X, q, z, s, G), f"M={M} K={K} N={N} G={G}")
 
 
-# Decode kernel shapes for 5 <= M <= 32: every way of feeding X (register A
-# operands, LDS ring, strip-parallel kernel) under several workgroup shapes,
-# ragged M, every group size, split and unsplit K. The plan knobs are read at
-# every call.
+# Decode kernel shapes for 2 <= M <= 32: every way of feeding X (register A
+# operands, run of X staged in LDS, LDS ring, strip-parallel kernel) under
+# several workgroup shapes, ragged M, every group size, split and unsplit K.
+# The plan knobs are read at every call.
 DECODE_X = [
     # (M, K, N, G, splits)
+    (2, 4096, 512, 128, 0),
+    (3, 29568, 64, 64, 0),
     (5, 1152, 272, 64, 1),
     (8, 2048, 1040, 128, 1),
     (8, 4096, 512, 128, 3),
@@ -158,8 +160,11 @@ DECODE_X = [
 ]
 
 
-@pytest.mark.parametrize("M,K,N,G,splits", DECODE_X)
-@pytest.mark.parametrize("xm", [0, 2, "sp"])
+# the staged run holds all of a wave's X rows at once: M <= 8 only
+X_MODES = [(c, xm) for c in DECODE_X for xm in (0, 1, 2, "sp") if xm != 1 or c[0] <= 8]
+
+
+@pytest.mark.parametrize("M,K,N,G,splits,xm", [c + (xm,) for c, xm in X_MODES])
 @pytest.mark.parametrize("ns,wk", [(1, 8), (2, 16), (4, 4)])
 def test_decode_x_modes(monkeypatch, M, K, N, G, splits, xm, ns, wk):
     if xm == "sp":  # strip-parallel kernel: X of the slice staged once per workgroup

@@ -138,9 +138,9 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits, 
     return W4A16_OK;
 }
 
-size_t plan_workspace(const Plan &p, int64_t M, int64_t N, int64_t K, int64_t G) {
+size_t plan_workspace(const Plan &p, int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
     if (p.path == W4A16_PATH_DECODE)
-        return w4a16::decode_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits);
+        return w4a16::decode_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits, num_cus);
     return w4a16::prefill_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits);
 }
 
@@ -223,16 +223,16 @@ int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G, uint8_t *q
 
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits) {
     if (M < 1 || M > kMaxDim || !shape_ok(K, N, G)) return 0;
-    // The automatic split count depends on the device's CU count; size for
-    // the current device when one is available, else for 256 CUs.
+    // The plan depends on the device's CU count; size for the current device
+    // when one is available, else for 256 CUs.
     int cus = 256, dev = 0;
-    if (splits == 0 && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
         int v = 0;
         if (device_cus(dev, &v) == W4A16_OK) cus = v;
     }
     Plan p;
     if (make_plan(M, N, K, G, path, splits, cus, &p) != W4A16_OK) return 0;
-    return plan_workspace(p, M, N, K, G);
+    return plan_workspace(p, M, N, K, G, cus);
 }
 
 int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
@@ -244,7 +244,7 @@ int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int6
     Plan p;
     if ((rc = make_plan(M, N, K, G, W4A16_PATH_AUTO, 0, cus, &p))) return rc;
     void *ws = nullptr;
-    const size_t need = plan_workspace(p, M, N, K, G);
+    const size_t need = plan_workspace(p, M, N, K, G, cus);
     if (need && (rc = device_workspace(dev, need, &ws))) return rc;
     return launch(X, packed, M, N, K, G, Y, ws, p, cus, (hipStream_t)stream);
 }
@@ -258,7 +258,7 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
     Plan p;
     if (splits != 0) {
         if ((rc = make_plan(M, N, K, G, path, splits, 256, &p))) return rc;
-        const size_t need = plan_workspace(p, M, N, K, G);
+        const size_t need = plan_workspace(p, M, N, K, G, 256);
         if (need && (!workspace || workspace_bytes < need))
             return fail(W4A16_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need,
                         workspace ? workspace_bytes : (size_t)0);
@@ -266,7 +266,7 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
     int dev, cus;
     if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
     if ((rc = make_plan(M, N, K, G, path, splits, cus, &p))) return rc;
-    const size_t need = plan_workspace(p, M, N, K, G);
+    const size_t need = plan_workspace(p, M, N, K, G, cus);
     if (need && (!workspace || workspace_bytes < need))
         return fail(W4A16_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need,
                     workspace ? workspace_bytes : (size_t)0);

@@ -17,10 +17,10 @@
 // * Scales and zeros of the workgroup's strips and slice are staged in LDS
 //   once, already turned into the fp16 pair -(1024 + z) and the fp32 scale,
 //   so the main loop reads them with one LDS load per group and strip.
-// * Activations, three modes. M <= 4: the rows of X over the wave's run are
-//   staged in LDS before the main loop (a few KiB). M <= 16: each batch of
-//   weight tiles travels with the X rows of its blocks, copied straight into
-//   a two-slot LDS ring by 16-byte buffer->LDS loads that each move four
+// * Activations, three modes. M = 1: the row of X over the wave's run is
+//   staged in LDS before the main loop (a few KiB). 2 <= M <= 32: each batch
+//   of weight tiles travels with the X rows of its blocks, copied straight
+//   into a two-slot LDS ring by 16-byte buffer->LDS loads that each move four
 //   rows x 256 bytes (whole 128-byte lines). Larger M: each wave loads its A
 //   operands into registers once per 32-row step and uses them for all NS
 //   strips. The per-CU cost of X is the number of cache lines it pulls into
@@ -655,9 +655,9 @@ int env_int(const char *name, int dflt) {
 // Launch shape, picked from graph-timed sweeps on MI355X over the decode
 // matrices of Llama-3-8B (QKV 4096 x 6144, down 14336 x 4096) and Llama-3-70B
 // (gate/up 8192 x 57344, down 28672 x 8192):
-// * M <= 4: X staged per run in LDS, 8 waves per workgroup, one strip per
+// * M = 1: X staged per run in LDS, 8 waves per workgroup, one strip per
 //   wave (two where N is very wide);
-// * 5 <= M <= 32: X through the LDS ring. Short K with narrow N (QKV-like):
+// * 2 <= M <= 32: X through the LDS ring. Short K with narrow N (QKV-like):
 //   K unsplit, 2 strips x 16 waves (x 4 waves for M > 16). Very wide N: 2
 //   strips x 4 waves, plenty of workgroups. Otherwise about one workgroup
 //   per CU with K unsplit for M <= 8 (16 waves); for larger M twice the
@@ -666,12 +666,12 @@ int env_int(const char *name, int dflt) {
 // * M > 32: register X shared by 2 strips per wave, K split across
 //   workgroups until there is about one workgroup per CU. The strip-parallel
 //   kernel and register X for smaller M remain available for tuning.
-// W4A16_DECODE_SP, _XM (0: register X, 2: ring), _NS and _WK override the
+// W4A16_DECODE_SP, _XM (0: register X, 1: staged run, 2: ring), _NS and _WK override the
 // kernel, X mode, NS and WK for tuning (instantiated values only).
 Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
-    p.xm = M <= 4 ? kXRun : (M <= 16 ? (M <= 8 ? 8 : 16) : (M <= 32 ? 32 : kXReg));
+    p.xm = M == 1 ? kXRun : (M <= 16 ? (M <= 8 ? 8 : 16) : (M <= 32 ? 32 : kXReg));
     p.sp = false;
     const int nstrip = N / kStripCols, nblk = K / kBlockK;
     const bool short_narrow = nstrip <= 384 && nblk <= 64;
@@ -706,7 +706,11 @@ Plan base_plan(int M, int N, int K) {
     if (p.sp) p.xm = kXReg;
     const int exm = env_int("W4A16_DECODE_XM", -1);
     if (exm == 0 && p.xm != kXRun) p.xm = kXReg;
-    if (exm == 2 && M > 4 && p.mt <= 2) {
+    if (exm == 1 && p.mt == 1) {
+        p.sp = false;
+        p.xm = kXRun;
+    }
+    if (exm == 2 && M > 1 && p.mt <= 2) {
         p.sp = false;
         p.xm = M <= 8 ? 8 : 16 * p.mt;
     }
@@ -752,16 +756,23 @@ uint32_t plan_lds(const Plan &p, int M, int G, int slice_blocks) {
                 : decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xm).total() + ring_lds(p);
 }
 
-// Plans with an LDS ring run one workgroup per CU and may use all of its
-// LDS; the others keep to a budget that leaves room for two.
-bool lds_fits(const Plan &p, int M, int G, int slice_blocks) {
-    return plan_lds(p, M, G, slice_blocks) <= (p.xm >= 8 ? kLdsMax : kLdsBudget);
+// A plan may use all of a CU's LDS when it runs one workgroup per CU (the
+// ring plans, or at most one workgroup per CU in all); the others keep to a
+// budget that leaves room for two.
+bool lds_fits(const Plan &p, int M, int G, int slice_blocks, long workgroups, int num_cus) {
+    const bool one_per_cu = p.xm >= 8 || workgroups <= num_cus;
+    return plan_lds(p, M, G, slice_blocks) <= (one_per_cu ? kLdsMax : kLdsBudget);
+}
+
+int plan_tiles(const Plan &p, int N) {
+    const int per = p.ns * (p.sp ? p.wk : 1);
+    return (N / kStripCols + per - 1) / per;
 }
 
 Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     Plan p = base_plan(M, N, K);
     const int nblk = K / kBlockK;
-    const int tiles = (N / kStripCols + p.ns * (p.sp ? p.wk : 1) - 1) / (p.ns * (p.sp ? p.wk : 1));
+    const int tiles = plan_tiles(p, N);
     if (splits <= 0 && p.fixed_splits) splits = 1;
     if (splits <= 0) {
         // Narrow N: about one workgroup per CU, keeping at least two blocks
@@ -775,7 +786,11 @@ Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
         }
     }
     // enough splits for the LDS budget (also raises a requested count)
-    while (splits < nblk && !lds_fits(p, M, G, slice_for(K, G, splits))) ++splits;
+    auto fits = [&](int sp) {
+        const int sb = slice_for(K, G, sp);
+        return lds_fits(p, M, G, sb, (long)tiles * ((nblk + sb - 1) / sb), num_cus);
+    };
+    while (splits < nblk && !fits(splits)) ++splits;
     p.slice_blocks = slice_for(K, G, splits);
     p.splits = (nblk + p.slice_blocks - 1) / p.slice_blocks;
     return p;
@@ -870,7 +885,7 @@ hipError_t launch_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int
 hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                        float *part, const Plan &p, hipStream_t stream) {
     if (p.sp) return launch_sp(X, packed, M, N, K, G, Y, part, p, stream);
-    if (p.xm == kXRun) {  // M <= 4
+    if (p.xm == kXRun) {  // M = 1 (M <= 16 when tuning)
         switch (p.ns) {
             case 1: return launch_wk<1, 1, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
             case 2: return launch_wk<1, 2, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
@@ -884,7 +899,7 @@ hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, i
             default: return launch_wk<2, 4, 32>(X, packed, M, N, K, G, Y, part, p, stream);
         }
     }
-    if (p.xm == 8 || p.xm == 16) {  // 5 <= M <= 16
+    if (p.xm == 8 || p.xm == 16) {  // 2 <= M <= 16
         const bool r8 = p.xm == 8;
         switch (p.ns) {
             case 1: return r8 ? launch_wk<1, 1, 8>(X, packed, M, N, K, G, Y, part, p, stream)
@@ -928,10 +943,10 @@ int decode_auto_splits(int M, int N, int K, int G, int num_cus) {
     return make_plan(M, N, K, G, 0, num_cus).splits;
 }
 
-size_t decode_workspace_bytes(int M, int N, int K, int G, int splits) {
+size_t decode_workspace_bytes(int M, int N, int K, int G, int splits, int num_cus) {
     // a requested split count is rounded to whole groups per slice and
     // raised until the slice fits the LDS budget
-    const Plan p = make_plan(M, N, K, G, splits, 256);
+    const Plan p = make_plan(M, N, K, G, splits, num_cus);
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -939,7 +954,8 @@ size_t decode_workspace_bytes(int M, int N, int K, int G, int splits) {
 hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
                          uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream) {
     const Plan p = make_plan(M, N, K, G, splits, num_cus);
-    if (!lds_fits(p, M, G, p.slice_blocks)) return hipErrorInvalidConfiguration;
+    if (!lds_fits(p, M, G, p.slice_blocks, (long)plan_tiles(p, N) * p.splits, num_cus))
+        return hipErrorInvalidConfiguration;
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e = launch_plan(X, packed, M, N, K, G, Y, part, p, stream);
     if (e != hipSuccess || p.splits <= 1) return e;

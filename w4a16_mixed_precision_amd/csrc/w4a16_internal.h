@@ -21,7 +21,8 @@ hipError_t launch_unpack(const uint8_t *packed, int K, int N, int G, uint8_t *q,
 constexpr int kDecodeMaxM = 64;
 int decode_auto_splits(int M, int N, int K, int G, int num_cus);
 int decode_max_splits(int M, int N, int K);
-size_t decode_workspace_bytes(int M, int N, int K, int G, int splits);
+// (the plan, and so the workspace, can depend on the CU count of the device)
+size_t decode_workspace_bytes(int M, int N, int K, int G, int splits, int num_cus);
 hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
                          uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 
