@@ -65,6 +65,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     constexpr int NF = 4 / F;
     constexpr int XLOADS = BM * 16 / THREADS;  // 16-byte direct loads per thread per stage
     static_assert(BM * 16 % THREADS == 0, "X tile must split evenly over the threads");
+    static_assert(MTW == 4 || MTW == 8 || MTW == 16, "row tiles per wave");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
     const int lane = threadIdx.x & 63;
@@ -154,35 +155,64 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     auto a_off = [&](int mt, int t) { return (rbase + mt * 16 + col) * 256 + (((4 * t + kq) ^ col) * 16); };
     const int zsh = (col & 1) * 4;
 
+    // One K block: four 32-row steps x NSW strips = 4 NSW strip groups of MTW
+    // MFMAs each. The B operand of a strip for the next step is dequantized
+    // during the following strip group, two 32-bit words (four fp16 weights)
+    // after every fourth MFMA, into the registers the strip's own MFMAs have
+    // finished reading;
+    // after the last strip of a step, each row tile's A operand for the next
+    // step is read from LDS right behind that row tile's MFMA. The matrix
+    // unit thus runs while the VALU converts weights and the LDS serves reads.
     auto compute = [&](int stage, const Set &w) {
         const uint8_t *st = lds + stage * STAGE;
-        u32x4 w8[NSW];
+        uint32_t nbl[NF][NSW], nbh[NF][NSW], s2[NF][NSW];
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int j = 0; j < NSW; ++j) {
+                nbl[f][j] = (0xE400u | ((w.zb[f][j] >> zsh) & 15u)) * 0x10001u;
+                nbh[f][j] = neg_bias64_from_1024(nbl[f][j]);
+                s2[f][j] = (w.sc[f][j] & 0xFFFFu) * 0x10001u;
+            }
+        // word v of strip j's B operand for step t: two fp16 weights
+        auto bword = [&](int t, int j, int v) -> uint32_t {
+            const int f = t / F;
+            const uint32_t src = (t & 1) ? (w.w[j][v] >> 8) : w.w[j][v];
+            const half2v r = (as_h2(and_or(src, t < 2 ? kLoMask : kHiMask, t < 2 ? m_lo : m_hi)) +
+                              as_h2(t < 2 ? nbl[f][j] : nbh[f][j])) *
+                             as_h2(s2[f][j]);
+            return __builtin_bit_cast(uint32_t, r);
+        };
+        half8 a[MTW];
+        u32x4 bw[NSW];
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) a[mt] = *reinterpret_cast<const half8 *>(st + a_off(mt, 0));
 #pragma unroll
         for (int j = 0; j < NSW; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) w8[j][v] = w.w[j][v] >> 8;
+            for (int v = 0; v < 4; ++v) bw[j][v] = bword(0, j, v);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            // LDS reads first; the dequantization below covers their latency
-            half8 a[MTW];
+        for (int g = 0; g < 4 * NSW; ++g) {
+            const int t = g / NSW, j = g % NSW;
+            const int pg = g - 1;                      // previous strip group
+            const int pt = pg / NSW + 1, pj = pg % NSW;  // its strip's next step
+            const bool pending = g > 0 && pt < 4;
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt) a[mt] = *reinterpret_cast<const half8 *>(st + a_off(mt, t));
-            const int f = t / F;
-            half8 bw[NSW];
+            for (int mt = 0; mt < MTW; ++mt) {
+                acc[mt][j] = mfma16x16x32(a[mt], __builtin_bit_cast(half8, bw[j]), acc[mt][j]);
+                if (t < 3 && j == NSW - 1) a[mt] = *reinterpret_cast<const half8 *>(st + a_off(mt, t + 1));
+                // two independent words at a time (their dependent op chains
+                // interleave), after every fourth MFMA (every second for MTW 4)
+                constexpr int kSlots = MTW >= 8 ? MTW / 4 : MTW / 2;  // dequant slots per group
+                constexpr int kEvery = MTW / kSlots;
+                if (pending && mt % kEvery == kEvery - 1) {
+                    const int slot = mt / kEvery;
 #pragma unroll
-            for (int j = 0; j < NSW; ++j) {
-                const uint32_t h = 0xE400u | ((w.zb[f][j] >> zsh) & 15u);
-                const uint32_t nb = h * 0x10001u;
-                const DequantConsts dc{nb, neg_bias64_from_1024(nb), m_lo, m_hi};
-                bw[j] = dequant_w(t, w.w[j], w8[j], dc, (w.sc[f][j] & 0xFFFFu) * 0x10001u);
+                    for (int v = slot * 4 / kSlots; v < (slot + 1) * 4 / kSlots; ++v) bw[pj][v] = bword(pt, pj, v);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-                for (int j = 0; j < NSW; ++j) acc[mt][j] = mfma16x16x32(a[mt], bw[j], acc[mt][j]);
-            // keep the scheduler from hoisting the next step's LDS reads
-            // (and their registers) above these MFMAs
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
