@@ -105,11 +105,6 @@ __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, i
 // scale records or split-K partials from L2.
 constexpr int kWeightLoadPolicy = 2;  // nt
 
-// s_waitcnt immediate that waits until at most n vector memory operations
-// are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
-// s_waitcnt immediate that waits for all LDS (and scalar memory) operations
-constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 
 // One 128-row block of NS strips: for each of the block's scale groups the
 // matrix instruction runs over its 32-row steps with the exact integer

@@ -125,6 +125,12 @@ __device__ inline uint16_t f32_to_f16_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate that waits for all LDS (and scalar memory) operations
+constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
+
 // A raw buffer load whose offset reaches past the descriptor's byte count
 // returns zeros and makes no memory request. Kernels point loads they do not
 // need at this offset instead of branching around them, so every path
