@@ -191,7 +191,8 @@ def recorded_traffic(workload):
 
 
 def kernel_name(inst):
-    if inst.M > 32:
+    import w4a16_mixed_precision_amd as w4
+    if w4.w4a16_auto_path(inst.M, inst.N, inst.K, inst.G) == w4.W4A16_PATH_PREFILL:
         return "prefill_kernel"
     return "decode path"
 

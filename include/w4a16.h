@@ -72,7 +72,7 @@ extern "C" {
 #define W4A16_ERR_ARG (-7)       /* path or split selector out of range */
 
 /* Execution paths for w4a16_gemm_ex. */
-#define W4A16_PATH_AUTO 0
+#define W4A16_PATH_AUTO 0    /* see w4a16_auto_path */
 #define W4A16_PATH_DECODE 1  /* weight-streaming, HBM-bound; M <= 64 */
 #define W4A16_PATH_PREFILL 2 /* LDS-tiled MFMA, compute-bound; any M */
 
@@ -157,6 +157,15 @@ const char *w4a16_last_error(void);
 
 /* W4A16_LAYOUT_VERSION of the compiled library. */
 int w4a16_layout_version(void);
+
+/*
+ * The path W4A16_PATH_AUTO takes for this shape: W4A16_PATH_DECODE for
+ * M <= 32, and for M <= 64 when N <= 6144 (narrow matrices, where the
+ * weight-streaming kernel measured faster than the tiled one); otherwise
+ * W4A16_PATH_PREFILL. Host-only. Returns W4A16_ERR_SHAPE for an
+ * unsupported shape.
+ */
+int w4a16_auto_path(int64_t M, int64_t N, int64_t K, int64_t G);
 
 #ifdef __cplusplus
 }

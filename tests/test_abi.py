@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
               "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
-              "w4a16_layout_version"):
+              "w4a16_layout_version", "w4a16_auto_path"):
         assert n in names
 
 
@@ -44,6 +44,17 @@ def test_packed_bytes_matches_layout_spec():
 
 def test_layout_version():
     assert w4.w4a16_layout_version() == 2
+
+
+def test_auto_path_rule():
+    D, P = w4.W4A16_PATH_DECODE, w4.W4A16_PATH_PREFILL
+    assert w4.w4a16_auto_path(1, 6144, 4096, 128) == D
+    assert w4.w4a16_auto_path(32, 57344, 8192, 128) == D
+    assert w4.w4a16_auto_path(33, 57344, 8192, 128) == P
+    assert w4.w4a16_auto_path(64, 6144, 4096, 128) == D
+    assert w4.w4a16_auto_path(64, 8192, 28672, 128) == P
+    assert w4.w4a16_auto_path(65, 4096, 14336, 128) == P
+    assert w4.lib().w4a16_auto_path(1, 6144, 100, 128) == w4.W4A16_ERR_SHAPE
 
 
 def test_gemm_validation_before_any_hip_call():

@@ -138,7 +138,7 @@ def test_parity_small(M, K, N, G, path, splits):
     assert_parity(Y, oracle.gemm(X, q, z, s, G), f"M={M} K={K} N={N} G={G}")
 
 
-# Decode kernel shapes for 2 <= M <= 32: every way of feeding X (register A
+# Decode kernel shapes for 2 <= M <= 64: every way of feeding X (register A
 # operands, run of X staged in LDS, LDS ring, strip-parallel kernel) under
 # several workgroup shapes, ragged M, every group size, split and unsplit K.
 # The plan knobs are read at every call.
@@ -157,6 +157,8 @@ DECODE_X = [
     (25, 1152, 272, 64, 3),
     (32, 2304, 784, 256, 1),
     (32, 4096, 512, 128, 0),
+    (48, 1024, 400, 32, 2),
+    (64, 2304, 784, 256, 1),
 ]
 
 

@@ -20,7 +20,7 @@ __all__ = [
     "W4A16_PATH_AUTO", "W4A16_PATH_DECODE", "W4A16_PATH_PREFILL",
     "w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
-    "w4a16_layout_version",
+    "w4a16_layout_version", "w4a16_auto_path",
 ]
 
 W4A16_OK = 0
@@ -73,6 +73,8 @@ def lib():
     L.w4a16_last_error.restype = ctypes.c_char_p
     L.w4a16_layout_version.argtypes = []
     L.w4a16_layout_version.restype = I
+    L.w4a16_auto_path.argtypes = [I64, I64, I64, I64]
+    L.w4a16_auto_path.restype = I
     _lib = L
     return L
 
@@ -117,6 +119,14 @@ def w4a16_last_error() -> str:
 
 def w4a16_layout_version() -> int:
     return int(lib().w4a16_layout_version())
+
+
+def w4a16_auto_path(M: int, N: int, K: int, G: int) -> int:
+    """Path the automatic plan takes for this shape (W4A16_PATH_DECODE or
+    W4A16_PATH_PREFILL)."""
+    rc = int(lib().w4a16_auto_path(M, N, K, G))
+    _check(rc if rc < 0 else 0)
+    return rc
 
 
 def w4a16_packed_bytes(K: int, N: int, G: int) -> int:

@@ -185,6 +185,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     // arrays, so that the compiler sees that a batch's reads and the other
     // batch's copies touch different memory.
     constexpr int kSlot = kRing ? XM * kBlockK * 2 : 16;
+    static_assert(!kRing || 2 * WK * NB * kSlot <= 160 * 1024, "ring exceeds the LDS");
     __shared__ __attribute__((aligned(16))) uint8_t ring0[kRing ? WK * NB * kSlot : 16];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[kRing ? WK * NB * kSlot : 16];
 
@@ -229,13 +230,17 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         else
             xoff[mt] = (uint32_t)((row * K + kq * 8) * 2);
     }
-    // ring copies: lane -> row xi * 4 + lane / 16 of a block, 16-byte chunk
-    // (lane & 15) ^ row, written to LDS position lane
-    uint32_t xsrc[8];  // (a size that depends on XM keeps hipcc from emitting the host stub)
+    // ring copies: copy xi moves rows 4 xi .. 4 xi + 3 of a block, lane ->
+    // row 4 xi + lane / 16, 16-byte chunk (lane & 15) ^ row, written to LDS
+    // position lane. Copies xi and xi + 4 share the chunk order (rows 16
+    // apart), so the per-lane offsets repeat with period 4 and the 16-row
+    // step goes into the scalar offset. Rows >= M lie past the end of X's
+    // descriptor and read as zeros.
+    uint32_t xsrc[4];
 #pragma unroll
-    for (int xi = 0; xi < (kRing ? XM / 4 : 1); ++xi) {
+    for (int xi = 0; xi < 4; ++xi) {
         const int r = xi * 4 + (lane >> 4);
-        xsrc[xi] = r < M ? (uint32_t)(r * K * 2 + (((lane & 15) ^ (r & 15)) * 16)) : kOobOffset;
+        xsrc[xi] = (uint32_t)(r * K * 2 + (((lane & 15) ^ (r & 15)) * 16));
     }
     const uint32_t m_lo = kMagic, m_hi = kMagic64;
 
@@ -261,8 +266,8 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 #pragma unroll
                 for (int xi = 0; xi < XM / 4; ++xi)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xr + i * kSlot + xi * 1024), 16,
-                                                             in ? xsrc[xi] : kOobOffset,
-                                                             (b0 + i) * kBlockK * 2, 0, 0);
+                                                             in ? xsrc[xi & 3] : kOobOffset,
+                                                             (b0 + i) * kBlockK * 2 + (xi >> 2) * 32 * K, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < NS; ++j)
@@ -666,7 +671,7 @@ int env_int(const char *name, int dflt) {
 Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
-    p.xm = M == 1 ? kXRun : (M <= 16 ? (M <= 8 ? 8 : 16) : (M <= 32 ? 32 : kXReg));
+    p.xm = M == 1 ? kXRun : (M <= 8 ? 8 : 16 * p.mt);
     p.sp = false;
     const int nstrip = N / kStripCols, nblk = K / kBlockK;
     const bool short_narrow = nstrip <= 384 && nblk <= 64;
@@ -683,7 +688,7 @@ Plan base_plan(int M, int N, int K) {
             p.ns = M <= 8 ? ns : 2 * ns;
             p.wk = M <= 8 ? 16 : 8;
         } else {
-            p.ns = 4;
+            p.ns = p.mt == 2 ? 4 : 2;
             p.wk = 4;
         }
     } else if (short_narrow) {
@@ -705,7 +710,7 @@ Plan base_plan(int M, int N, int K) {
         p.sp = false;
         p.xm = kXRun;
     }
-    if (exm == 2 && M > 1 && p.mt <= 2) {
+    if (exm == 2 && M > 1) {
         p.sp = false;
         p.xm = M <= 8 ? 8 : 16 * p.mt;
     }
@@ -715,6 +720,7 @@ Plan base_plan(int M, int N, int K) {
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
     if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1 && !p.sp)) p.wk = ewk;
     if (p.mt > 1 && p.wk > 8) p.wk = 8;
+    if (p.xm == 64) p.wk = 4;  // two 64-row slots per wave: 128 KiB of LDS at 4 waves
     p.splits = 1;
     p.slice_blocks = 0;
     if (p.sp) {
@@ -870,11 +876,15 @@ hipError_t launch_g(const uint16_t *X, const uint8_t *packed, int M, int N, int 
 template <int MT, int NS, int XM>
 hipError_t launch_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                      float *part, const Plan &p, hipStream_t stream) {
-    if constexpr (MT == 1) {
-        if (p.wk == 16) return launch_g<MT, NS, 16, XM>(X, packed, M, N, K, G, Y, part, p, stream);
+    if constexpr (XM == 64) {  // two 64-row ring slots per wave: 4 waves only
+        return launch_g<MT, NS, 4, XM>(X, packed, M, N, K, G, Y, part, p, stream);
+    } else {
+        if constexpr (MT == 1) {
+            if (p.wk == 16) return launch_g<MT, NS, 16, XM>(X, packed, M, N, K, G, Y, part, p, stream);
+        }
+        if (p.wk == 4) return launch_g<MT, NS, 4, XM>(X, packed, M, N, K, G, Y, part, p, stream);
+        return launch_g<MT, NS, 8, XM>(X, packed, M, N, K, G, Y, part, p, stream);
     }
-    if (p.wk == 4) return launch_g<MT, NS, 4, XM>(X, packed, M, N, K, G, Y, part, p, stream);
-    return launch_g<MT, NS, 8, XM>(X, packed, M, N, K, G, Y, part, p, stream);
 }
 
 hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
@@ -886,6 +896,10 @@ hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, i
             case 2: return launch_wk<1, 2, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
             default: return launch_wk<1, 4, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
         }
+    }
+    if (p.xm == 64) {  // 33 <= M <= 64
+        if (p.ns == 1) return launch_wk<4, 1, 64>(X, packed, M, N, K, G, Y, part, p, stream);
+        return launch_wk<4, 2, 64>(X, packed, M, N, K, G, Y, part, p, stream);
     }
     if (p.xm == 32) {  // 17 <= M <= 32
         switch (p.ns) {
