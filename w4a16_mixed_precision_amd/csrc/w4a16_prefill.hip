@@ -321,11 +321,17 @@ struct PrefillPlan {
     int ci, splits, slice_blocks;
 };
 
-// Tile shape by M; split K when the tiles cannot fill every CU about twice.
+// Tile shape by M (64-row tiles up to M = 128, 128-row tiles above); split
+// K so that one round of resident workgroups covers the GPU: the largest
+// split count whose tiles x splits still fit in one round. (A count that
+// spills into a second, mostly empty round costs more than it gains:
+// graph-timed on MI355X, 8192 x 10240 at M = 512 took 125 us with 3 splits
+// of its 160 tiles and 150 us with 4; 8192 x 57344 at M = 256 took 241 us
+// unsplit and 297 us with 2 splits of its 448 tiles.)
 // W4A16_PREFILL_CFG overrides the shape (tuning).
 PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
     PrefillPlan p;
-    p.ci = M <= 64 ? 3 : 2;
+    p.ci = M <= 128 ? 3 : 2;
     if (const char *e = getenv("W4A16_PREFILL_CFG")) {
         const int v = atoi(e);
         if (v >= 0 && v < kNumCfgs) p.ci = v;
@@ -336,9 +342,8 @@ PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
     const int nblk = K / kBlockK;
     const int per_cu = c.occ * 4 / (c.wm * c.wn) > 0 ? c.occ * 4 / (c.wm * c.wn) : 1;  // resident WGs per CU
     if (splits <= 0) {
-        splits = 1;
-        const int want = num_cus * per_cu;
-        if (tiles < want) splits = (want + tiles - 1) / tiles;
+        const int slots = num_cus * per_cu;
+        splits = tiles >= slots ? 1 : slots / tiles;
         const int cap = nblk / 8 > 1 ? nblk / 8 : 1;  // keep 8+ blocks per split
         if (splits > cap) splits = cap;
     }
