@@ -4,38 +4,37 @@
 // GEMM is limited by memory bandwidth, not arithmetic ("LMDeploy" interview
 // notes, answer to why W4A16 raises throughput although FLOPs do not change;
 // "LMDeploy, in depth", section "Quantization: AWQ weights and KV cache").
-// The kernel is built so that streaming the weights costs as few vector
-// memory instructions as possible: on gfx950 the per-CU address unit, not
-// DRAM, is what runs out first when every 1 KiB weight tile also drags in
-// activation and scale loads.
+// The kernel is built around what runs out first on gfx950 when every 1 KiB
+// weight tile also needs activations and scales: not DRAM bandwidth but the
+// rate at which a CU can pull cache lines into its L1 (about one 128-byte
+// line per 1.1 ns) and its VALU time for the dequantization.
 //
 // * Work unit: one 1 KiB packed tile (16 columns x 128 rows of K), read by
 //   one wave64 with one 16-byte buffer load per lane. A workgroup owns NS
 //   adjacent 16-column strips and one of S slices of K; its WK waves split
 //   the slice into contiguous runs of 128-row blocks and each wave streams
 //   all NS strips of its run, two batches of tiles in flight.
-// * Scales and zeros of the workgroup's strips and slice are staged in LDS
-//   once, already turned into the fp16 pair -(1024 + z) and the fp32 scale,
-//   so the main loop reads them with one LDS load per group and strip.
-// * Activations, three modes. M = 1: the row of X over the wave's run is
-//   staged in LDS before the main loop (a few KiB). 2 <= M <= 32: each batch
-//   of weight tiles travels with the X rows of its blocks, copied straight
-//   into a two-slot LDS ring by 16-byte buffer->LDS loads that each move four
-//   rows x 256 bytes (whole 128-byte lines). Larger M: each wave loads its A
-//   operands into registers once per 32-row step and uses them for all NS
-//   strips. The per-CU cost of X is the number of cache lines it pulls into
-//   the CU; register A operands use half of each line they touch, the ring
-//   all of it. Rows >= M of the 16-row MFMA tile are padding: their results
-//   are never stored.
+// * Scales and zeros of a wave's strips and run are staged in its own LDS
+//   region once, already turned into the fp16 pair -(1024 + z) and the fp32
+//   scale, so the main loop reads them with one LDS load per group and strip.
+// * Activations. M = 1: the row of X over the wave's run is staged in LDS
+//   before the main loop (a few KiB). 2 <= M <= 64: each batch of weight
+//   tiles travels with the X rows of its blocks, copied straight into a
+//   two-slot LDS ring by 16-byte buffer->LDS loads that each move four rows
+//   x 256 bytes (whole 128-byte lines). The per-CU cost of X is the number of
+//   cache lines it pulls in; A operands loaded into registers (kept as a
+//   tuning alternative) use half of each line they touch, the ring all of it.
+//   Rows >= M of the 16-row MFMA tiles are padding: their results are never
+//   stored.
 // * Dequantization ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
 //   Engine", section 3, FP16 = (INT4 - ZeroPoint) x Scale): one v_and_or_b32
 //   per pair of codes sets the fp16 exponent field and yields 1024 + q (low
 //   nibbles) or 64 + q (high nibbles, no shift needed); a packed fp16 add of
 //   -(1024 + z) or -(64 + z) leaves the exact integer q - z, which the matrix
 //   instruction multiplies with X. The scale is applied in fp32 once per
-//   group and column to the group's partial sum. The integer work of one tile is independent of the
-//   other tiles in flight, so it interleaves with the matrix instructions and
-//   the loads (the pages' ILP point).
+//   group and column to the group's partial sum. The integer work of one
+//   tile is independent of the other tiles in flight, so it interleaves with
+//   the matrix instructions and the loads (the pages' ILP point).
 // * Reduction: the WK partial tiles of each strip are added in LDS in fixed
 //   order. With S == 1 the workgroup writes fp16 Y directly. With S > 1 each
 //   workgroup writes its fp32 partial to a workspace and a second small
@@ -65,8 +64,8 @@ struct DecodeBatch {
 };
 
 // Dynamic LDS: one private region per wave, back to back, holding the
-// records of the wave's groups, [NS][ngw][16], and in LDS-X mode the rows of
-// X over the wave's run of blocks, [M][x_stride]. X arrives by direct
+// records of the wave's groups, [NS][ngw][16], and in staged-run mode the
+// rows of X over the wave's run of blocks, [M][x_stride]. X arrives by direct
 // buffer-to-LDS loads of 1 KiB (4 blocks of one row) per instruction, so a
 // row slot holds whole KiB chunks, plus 16 bytes that put consecutive rows in
 // different banks. After the main loop the same memory holds the cross-wave
@@ -84,7 +83,8 @@ struct DecodeLds {
 // X modes of decode_kernel
 constexpr int kXReg = 0;  // A operands loaded into registers
 constexpr int kXRun = 1;  // the wave's run of X staged in LDS up front
-// 8 or 16: the X rows of each batch's blocks in an LDS ring of that many rows
+// 8, 16, 32 or 64: the X rows of each batch's blocks in an LDS ring of that
+// many rows (8 for M <= 8, else 16 per 16-row MFMA tile)
 
 __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, int slice_blocks, int G,
                                                  int xm) {
@@ -104,7 +104,6 @@ __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, i
 // once per call, so the stream should not evict the kernel's code, X, the
 // scale records or split-K partials from L2.
 constexpr int kWeightLoadPolicy = 2;  // nt
-
 
 // One 128-row block of NS strips: for each of the block's scale groups the
 // matrix instruction runs over its 32-row steps with the exact integer
