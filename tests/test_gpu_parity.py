@@ -219,35 +219,42 @@ def test_results_are_reproducible_and_workspace_is_reusable():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-def test_split_k_graph_replays_match_eager():
-    # A split plan captured in a HIP graph (GEMM kernel plus the reduction
-    # of its partials) gives the eager result on every replay, with eager
-    # calls on the same workspace in between.
+@pytest.mark.parametrize("M,splits,path", [
+    (12, 8, DECODE),    # LDS ring (16 rows), K split + reduce kernel
+    (1, 1, DECODE),     # staged run of X
+    (5, 1, DECODE),     # LDS ring (8 rows)
+    (40, 0, DECODE),    # LDS ring (64 rows), automatic plan
+    (300, 0, PREFILL),  # tiled path, automatic plan (K split + reduce)
+])
+def test_graph_replays_match_eager(M, splits, path):
+    # A plan captured in a HIP graph (GEMM kernel, plus the reduction of its
+    # partials where K is split) gives the eager result on every replay, with
+    # eager calls on the same workspace in between.
     import torch
-    K, N, G, M = 4096, 512, 128, 12
-    q, z, s, rng = _weights(K, N, G, seed=21)
+    K, N, G = 4096, 512, 128
+    say(f"graph replay M={M} splits={splits} path={path}")
+    q, z, s, rng = _weights(K, N, G, seed=21 + M)
     X = dev(synth.draw_x(rng, M, K))
     packed = pack_dev(q, z, s, G)
-    splits = 8
-    nbytes = w4.w4a16_workspace_bytes(M, N, K, G, DECODE, splits)
-    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
-    ref = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=DECODE, splits=splits))
+    nbytes = w4.w4a16_workspace_bytes(M, N, K, G, path, splits)
+    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda") if nbytes else None
+    ref = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=path, splits=splits))
     torch.cuda.synchronize()
-    assert_parity(ref, oracle.gemm(host(X), q, z, s, G), "eager split")
+    assert_parity(ref, oracle.gemm(host(X), q, z, s, G), "eager")
     Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     st = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(st):
-        w4.w4a16_gemm_ex(X, packed, N, K, G, Y=Y, workspace=ws, path=DECODE, splits=splits, stream=st)
+        w4.w4a16_gemm_ex(X, packed, N, K, G, Y=Y, workspace=ws, path=path, splits=splits, stream=st)
         st.synchronize()
         with torch.cuda.graph(g, stream=st):
-            w4.w4a16_gemm_ex(X, packed, N, K, G, Y=Y, workspace=ws, path=DECODE, splits=splits, stream=st)
+            w4.w4a16_gemm_ex(X, packed, N, K, G, Y=Y, workspace=ws, path=path, splits=splits, stream=st)
     for i in range(4):
         Y.fill_(0)
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(Y).view(np.uint16), ref.view(np.uint16)), f"replay {i}"
-        eager = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=DECODE, splits=splits))
+        eager = host(w4.w4a16_gemm_ex(X, packed, N, K, G, workspace=ws, path=path, splits=splits))
         torch.cuda.synchronize()
         assert np.array_equal(eager.view(np.uint16), ref.view(np.uint16)), f"eager after replay {i}"
 
