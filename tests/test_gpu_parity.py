@@ -138,10 +138,9 @@ def test_parity_small(M, K, N, G, path, splits):
     assert_parity(Y, oracle.gemm(X, q, z, s, G), f"M={M} K={K} N={N} G={G}")
 
 
-# Decode kernel shapes for 2 <= M <= 64: every way of feeding X (register A
-# operands, run of X staged in LDS, LDS ring, strip-parallel kernel) under
-# several workgroup shapes, ragged M, every group size, split and unsplit K.
-# The plan knobs are read at every call.
+# Decode kernel shapes for 2 <= M <= 64: both ways of feeding X (run of X
+# staged in LDS, LDS ring) under several workgroup shapes, ragged M, every
+# group size, split and unsplit K. The plan knobs are read at every call.
 DECODE_X = [
     # (M, K, N, G, splits)
     (2, 4096, 512, 128, 0),
@@ -163,16 +162,13 @@ DECODE_X = [
 
 
 # the staged run holds all of a wave's X rows at once: M <= 8 only
-X_MODES = [(c, xm) for c in DECODE_X for xm in (0, 1, 2, "sp") if xm != 1 or c[0] <= 8]
+X_MODES = [(c, xm) for c in DECODE_X for xm in (1, 2) if xm != 1 or c[0] <= 8]
 
 
 @pytest.mark.parametrize("M,K,N,G,splits,xm", [c + (xm,) for c, xm in X_MODES])
 @pytest.mark.parametrize("ns,wk", [(1, 8), (2, 16), (4, 4)])
 def test_decode_x_modes(monkeypatch, M, K, N, G, splits, xm, ns, wk):
-    if xm == "sp":  # strip-parallel kernel: X of the slice staged once per workgroup
-        monkeypatch.setenv("W4A16_DECODE_SP", "1")
-    else:
-        monkeypatch.setenv("W4A16_DECODE_XM", str(xm))
+    monkeypatch.setenv("W4A16_DECODE_XM", str(xm))
     monkeypatch.setenv("W4A16_DECODE_NS", str(ns))
     monkeypatch.setenv("W4A16_DECODE_WK", str(wk))
     say(f"decode X mode {xm} ns={ns} wk={wk}: M={M} K={K} N={N} G={G} splits={splits}")

@@ -22,10 +22,10 @@
 //   tiles travels with the X rows of its blocks, copied straight into a
 //   two-slot LDS ring by 16-byte buffer->LDS loads that each move four rows
 //   x 256 bytes (whole 128-byte lines). The per-CU cost of X is the number of
-//   cache lines it pulls in; A operands loaded into registers (kept as a
-//   tuning alternative) use half of each line they touch, the ring all of it.
-//   Rows >= M of the 16-row MFMA tiles are padding: their results are never
-//   stored.
+//   cache lines it pulls in; A operands loaded straight into registers (16
+//   rows x 64 bytes per instruction) would use half of each line they touch,
+//   the ring uses all of it. Rows >= M of the 16-row MFMA tiles are padding:
+//   their results are never stored.
 // * Dequantization ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
 //   Engine", section 3, FP16 = (INT4 - ZeroPoint) x Scale): one v_and_or_b32
 //   per pair of codes sets the fp16 exponent field and yields 1024 + q (low
@@ -57,10 +57,9 @@ struct SZ {
     float sc;
 };
 
-template <int MT, int NS, int NB>
+template <int NS, int NB>
 struct DecodeBatch {
     u32x4 w[NB][NS];
-    half8 a[NB][4][MT];  // register-X mode only
 };
 
 // Dynamic LDS: one private region per wave, back to back, holding the
@@ -81,7 +80,6 @@ struct DecodeLds {
 };
 
 // X modes of decode_kernel
-constexpr int kXReg = 0;  // A operands loaded into registers
 constexpr int kXRun = 1;  // the wave's run of X staged in LDS up front
 // 8, 16, 32 or 64: the X rows of each batch's blocks in an LDS ring of that
 // many rows (8 for M <= 8, else 16 per 16-row MFMA tile)
@@ -171,8 +169,9 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     constexpr bool kRun = XM == kXRun;
     constexpr bool kRing = XM >= 8;
     static_assert(!kRing || (MT == 1 && XM == 8) || XM == 16 * MT, "ring rows: 8, or 16 per row tile");
-    // X loads per block: 4 MT register loads, or one ring load per 4 rows
-    constexpr int kXLoads = XM == kXReg ? 4 * MT : (kRing ? XM / 4 : 0);
+    static_assert(kRun || kRing, "X mode");
+    // X copies per block: one ring copy per 4 rows (the staged run has none)
+    constexpr int kXLoads = kRing ? XM / 4 : 0;
     // loads of one batch and of the two batches issued ahead of the loop
     constexpr int kBatchLoads = NB * (NS + kXLoads);
     static_assert(2 * kBatchLoads <= 63, "vmcnt range");
@@ -224,10 +223,8 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         const int row = mt * 16 + col;
         if constexpr (kRun)  // rows >= M read row M-1: padding rows are never stored
             xoff[mt] = (uint32_t)((row < M ? row : M - 1) * L.x_stride + kq * 16);
-        else if constexpr (kRing)  // ring rows >= M hold zeros; rows >= XM (M <= 8) repeat rows < 8
+        else  // ring rows >= M hold zeros; rows >= XM (M <= 8) repeat rows < 8
             xoff[mt] = (uint32_t)((row & (XM - 1)) * kBlockK * 2);
-        else
-            xoff[mt] = (uint32_t)((row * K + kq * 8) * 2);
     }
     // ring copies: copy xi moves rows 4 xi .. 4 xi + 3 of a block, lane ->
     // row 4 xi + lane / 16, 16-byte chunk (lane & 15) ^ row, written to LDS
@@ -249,7 +246,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    typedef DecodeBatch<MT, NS, NB> Batch;
+    typedef DecodeBatch<NS, NB> Batch;
     // Blocks at or past the end of the wave's run load from the out-of-range
     // offset: no branch, no memory traffic, and the same instruction count
     // on every path. X rows >= M are out of range of X's descriptor too.
@@ -272,15 +269,6 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
             for (int j = 0; j < NS; ++j)
                 bt.w[i][j] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], wo, (b0 + i) * kTileBytes, kWeightLoadPolicy));
-            if constexpr (XM == kXReg) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        bt.a[i][t][mt] = __builtin_bit_cast(
-                            half8, __builtin_amdgcn_raw_buffer_load_b128(
-                                       rx, in ? xoff[mt] : kOobOffset, ((b0 + i) * kBlockK + t * 32) * 2, 0));
-            }
         }
     };
     auto compute = [&](int b0, const Batch &bt, const uint8_t *xr) {
@@ -296,11 +284,9 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                     if constexpr (kRun)
                         a[t][mt] = *reinterpret_cast<const half8 *>(
                             xl + xoff[mt] + ((b - wb) * kBlockK + t * 32) * 2);
-                    else if constexpr (kRing)
+                    else
                         a[t][mt] = *reinterpret_cast<const half8 *>(
                             xr + i * kSlot + xoff[mt] + (((4 * t + kq) ^ col) * 16));
-                    else
-                        a[t][mt] = bt.a[i][t][mt];
                 }
             block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngw, b, gw0, col, m_lo, m_hi, acc);
         }
@@ -415,194 +401,6 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     }
 }
 
-// LDS of the strip-parallel kernel: the slice's rows of X, shared by all
-// waves, [M][xs] (whole KiB chunks per row plus 16 bytes of bank padding),
-// then one record region per wave, [NS][ngc][16].
-struct SpLds {
-    uint32_t xs, x_bytes, ngc, rec_bytes, total;
-};
-
-__host__ __device__ inline SpLds sp_lds(int M, int NS, int WK, int slice_blocks, int G) {
-    SpLds l;
-    l.xs = (uint32_t)((slice_blocks + 3) / 4 * 1024 + 16);
-    l.x_bytes = (uint32_t)M * l.xs;
-    l.ngc = (uint32_t)((slice_blocks * kBlockK + G - 1) / G);  // slices start on a group boundary
-    l.rec_bytes = (uint32_t)(NS * l.ngc * 16 * sizeof(SZ));
-    l.total = l.x_bytes + (uint32_t)WK * l.rec_bytes;
-    return l;
-}
-
-// Strip-parallel decode kernel: the WK waves of a workgroup take different
-// strips (NS each) over the same slice of K, so the slice's rows of X are
-// staged in LDS once and feed WK x NS strips, and no cross-wave reduction is
-// needed. Each wave streams its strips' tiles of the slice with two batches
-// in flight, as in decode_kernel; with S > 1 slices the fp32 partials go to
-// the workspace for splitk_reduce_kernel.
-template <int MT, int NS, int WK, int NB, int GS>
-__global__ void __launch_bounds__(WK * 64)
-decode_sp_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
-                 uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int S,
-                 int slice_blocks) {
-    constexpr int G = 32 * GS;
-    constexpr int kBatchLoads = NB * NS;
-    static_assert(2 * kBatchLoads <= 63, "vmcnt range");
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-
-    const int lane = threadIdx.x & 63;
-    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int col = lane & 15;
-    const int kq = lane >> 4;
-    const int nblk = K / kBlockK;
-    const int ngrp = K / G;
-    const int nstrip = N / kStripCols;
-    const int strip0 = (blockIdx.x * WK + wk) * NS;  // this wave's first strip
-    const int split = blockIdx.y;
-    const int bb = split * slice_blocks;
-    const int be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
-    const int g0 = bb * kBlockK / G;
-    const int ng = (be * kBlockK + G - 1) / G - g0;
-
-    const SpLds L = sp_lds(M, NS, WK, slice_blocks, G);
-    uint8_t *xl = lds;
-    SZ *szl = reinterpret_cast<SZ *>(lds + L.x_bytes + wk * L.rec_bytes);
-
-    bool valid[NS];
-    __amdgpu_buffer_rsrc_t rw[NS];
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        valid[j] = strip0 + j < nstrip;
-        const int s = valid[j] ? strip0 + j : 0;
-        rw[j] = make_rsrc(packed + (size_t)s * nblk * kTileBytes, (uint32_t)nblk * kTileBytes);
-    }
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)((size_t)M * K * 2));
-    uint32_t xoff[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 16 + col;  // rows >= M read row M-1: never stored
-        xoff[mt] = (uint32_t)((row < M ? row : M - 1) * L.xs + kq * 16);
-    }
-    const uint32_t m_lo = kMagic, m_hi = kMagic64;
-
-    floatx4 acc[MT][NS];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NS; ++j) acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    struct Batch {
-        u32x4 w[NB][NS];
-    };
-    // blocks past the slice and strips past N load from the out-of-range offset
-    auto load = [&](int b0, Batch &bt) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-            for (int j = 0; j < NS; ++j)
-                bt.w[i][j] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rw[j], (b0 + i < be && valid[j]) ? (uint32_t)lane * 16u : kOobOffset,
-                               (b0 + i) * kTileBytes, kWeightLoadPolicy));
-    };
-    auto compute = [&](int b0, const Batch &bt) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int b = b0 + i;
-            if (b >= be) break;
-            half8 a[4][MT];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    a[t][mt] = *reinterpret_cast<const half8 *>(xl + xoff[mt] + ((b - bb) * kBlockK + t * 32) * 2);
-            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngc, b, g0, col, m_lo, m_hi, acc);
-        }
-    };
-
-    // ---- staging. X rows of the slice, cooperatively: instruction i moves
-    // chunk i % nch (blocks 4c..4c+3 of the slice) of row i / nch, lanes past
-    // the slice reading zeros into the row's spare bytes. Records of the
-    // wave's own strips: one unit (half a group record) per lane, units past
-    // the first 64 after a full wait. All of it is issued before the first two
-    // weight batches, and the wave waits for it alone.
-    const int run = be - bb, nch = (run + 3) / 4;
-    for (int i = wk; i < M * nch; i += WK) {
-        const int r = i / nch, c = i % nch;
-        const bool ok = c * 64 + lane < run * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(xl + r * L.xs + c * 1024), 16,
-                                                 ok ? (uint32_t)(r * K * 2 + lane * 16) : kOobOffset,
-                                                 (bb * kBlockK + c * 512) * 2, 0, 0);
-    }
-    const int nsv = strip0 >= nstrip ? 0 : (nstrip - strip0 < NS ? nstrip - strip0 : NS);
-    const int s0 = strip0 < nstrip ? strip0 : 0;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(packed + weight_bytes(K, N) + (size_t)s0 * ngrp * 32, (uint32_t)(nsv * ngrp * 32));
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(
-        packed + weight_bytes(K, N) + scale_bytes(K, N, G) + (size_t)s0 * ngrp * 8, (uint32_t)(nsv * ngrp * 8));
-    const int su_n = NS * ng * 2;
-    auto sz_load = [&](int u, u32x4 &sv, uint32_t &zv) {
-        const int j = u / (ng * 2), r = u % (ng * 2);
-        const bool ok = u < su_n && j < nsv;
-        const uint32_t rec = (uint32_t)(j * ngrp + g0 + (r >> 1));
-        sv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs, ok ? rec * 32u + (r & 1) * 16u : kOobOffset, 0, 0));
-        zv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rz, ok ? rec * 8u + (r & 1) * 4u : kOobOffset, 0, 0);
-    };
-    auto sz_store = [&](int u, const u32x4 &sv, uint32_t zv) {
-        if (u >= su_n) return;
-        const int j = u / (ng * 2), r = u % (ng * 2);
-        store_records(szl + (j * (int)L.ngc + (r >> 1)) * 16 + (r & 1) * 8, sv, zv);
-    };
-    u32x4 sv0;
-    uint32_t zv0;
-    sz_load(lane, sv0, zv0);
-    asm volatile("" ::: "memory");  // staging loads go out first
-    Batch b0, b1;
-    int b = bb;
-    load(b, b0);
-    asm volatile("" ::: "memory");  // keep the two batches apart in issue order
-    load(b + NB, b1);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBatchLoads));  // staging loads landed
-    sz_store(lane, sv0, zv0);
-    for (int u = 64 + lane; u - lane < su_n; u += 64) {
-        u32x4 sa;
-        uint32_t za;
-        sz_load(u, sa, za);
-        sz_store(u, sa, za);
-    }
-    __syncthreads();  // X is shared by the workgroup
-
-    if (nsv > 0) {
-        const int rounds = (be - b + 2 * NB - 1) / (2 * NB);
-        for (int r = 1; r < rounds; ++r, b += 2 * NB) {
-            compute(b, b0);
-            load(b + 2 * NB, b0);
-            compute(b + NB, b1);
-            load(b + 3 * NB, b1);
-        }
-        compute(b, b0);
-        compute(b + NB, b1);
-
-        // lane (col, kq) holds rows 4 kq + e of column col of every strip
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            if (!valid[j]) continue;
-            const size_t n = (size_t)(strip0 + j) * kStripCols + col;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = mt * 16 + kq * 4 + e;
-                    if (r >= M) continue;
-                    if (S == 1)
-                        Y[(size_t)r * N + n] = f32_to_f16_bits(acc[mt][j][e]);
-                    else
-                        part[((size_t)split * M + r) * N + n] = acc[mt][j][e];
-                }
-        }
-    }
-}
-
 // Y = sum over s of part[s] in split order, fp32 -> fp16. Each thread owns
 // four consecutive outputs and loads up to eight partials before adding any,
 // so the reduction costs one memory round trip per eight splits instead of
@@ -640,8 +438,7 @@ constexpr uint32_t kLdsMax = 160 * 1024;  // per CU on gfx950
 
 struct Plan {
     int mt, ns, wk;
-    bool sp;    // strip-parallel kernel
-    int xm;     // decode_kernel X mode: kXReg, kXRun, or ring rows (8, 16)
+    int xm;             // decode_kernel X mode: kXRun, or ring rows (8, 16, 32, 64)
     bool fixed_splits;  // automatic plan keeps K unsplit
     int splits, slice_blocks;
 };
@@ -656,76 +453,47 @@ int env_int(const char *name, int dflt) {
 // (gate/up 8192 x 57344, down 28672 x 8192):
 // * M = 1: X staged per run in LDS, 8 waves per workgroup, one strip per
 //   wave (two where N is very wide);
-// * 2 <= M <= 32: X through the LDS ring. Short K with narrow N (QKV-like):
+// * 2 <= M <= 64: X through the LDS ring. Short K with narrow N (QKV-like):
 //   K unsplit, 2 strips x 16 waves (x 4 waves for M > 16). Very wide N: 2
 //   strips x 4 waves, plenty of workgroups. Otherwise about one workgroup
 //   per CU with K unsplit for M <= 8 (16 waves); for larger M twice the
 //   strips per workgroup and K split in two, which halves the X each CU has
-//   to read (4 strips x 4 waves for M > 16);
-// * M > 32: register X shared by 2 strips per wave, K split across
-//   workgroups until there is about one workgroup per CU. The strip-parallel
-//   kernel and register X for smaller M remain available for tuning.
-// W4A16_DECODE_SP, _XM (0: register X, 1: staged run, 2: ring), _NS and _WK override the
-// kernel, X mode, NS and WK for tuning (instantiated values only).
+//   to read (4 strips x 4 waves for 17 <= M <= 32, 2 x 4 above).
+// W4A16_DECODE_XM (1: staged run, M <= 16; 2: ring, M >= 2), _NS and _WK
+// override the X mode, NS and WK for tuning (instantiated values only).
 Plan base_plan(int M, int N, int K) {
     Plan p;
     p.mt = decode_mt(M);
     p.xm = M == 1 ? kXRun : (M <= 8 ? 8 : 16 * p.mt);
-    p.sp = false;
     const int nstrip = N / kStripCols, nblk = K / kBlockK;
     const bool short_narrow = nstrip <= 384 && nblk <= 64;
     if (p.xm == kXRun) {
         p.ns = nstrip >= 2048 ? 2 : 1;
         p.wk = 8;
-    } else if (p.xm != kXReg) {
-        if (short_narrow || nstrip >= 1024) {
-            p.ns = 2;
-            p.wk = short_narrow && p.mt == 1 ? 16 : 4;
-        } else if (p.mt == 1) {
-            int ns = nstrip / 256;
-            ns = ns < 1 ? 1 : (ns > 2 ? 2 : ns);
-            p.ns = M <= 8 ? ns : 2 * ns;
-            p.wk = M <= 8 ? 16 : 8;
-        } else {
-            p.ns = p.mt == 2 ? 4 : 2;
-            p.wk = 4;
-        }
-    } else if (short_narrow) {
-        p.sp = p.mt == 2;
+    } else if (short_narrow || nstrip >= 1024) {
         p.ns = 2;
-        p.wk = 8;
+        p.wk = short_narrow && p.mt == 1 ? 16 : 4;
+    } else if (p.mt == 1) {
+        int ns = nstrip / 256;
+        ns = ns < 1 ? 1 : (ns > 2 ? 2 : ns);
+        p.ns = M <= 8 ? ns : 2 * ns;
+        p.wk = M <= 8 ? 16 : 8;
     } else {
-        p.ns = M <= 8 ? 2 : 4;
-        p.wk = p.mt == 1 ? 8 : 4;
+        p.ns = p.mt == 2 ? 4 : 2;
+        p.wk = 4;
     }
-    if (p.mt == 4) p.ns = 2;
     p.fixed_splits = p.xm != kXRun && short_narrow;
-    const int esp = env_int("W4A16_DECODE_SP", -1);
-    if (esp == 0 || esp == 1) p.sp = esp == 1 && p.mt <= 2;
-    if (p.sp) p.xm = kXReg;
     const int exm = env_int("W4A16_DECODE_XM", -1);
-    if (exm == 0 && p.xm != kXRun) p.xm = kXReg;
-    if (exm == 1 && p.mt == 1) {
-        p.sp = false;
-        p.xm = kXRun;
-    }
-    if (exm == 2 && M > 1) {
-        p.sp = false;
-        p.xm = M <= 8 ? 8 : 16 * p.mt;
-    }
-    if (p.sp) p.xm = kXReg;
+    if (exm == 1 && p.mt == 1) p.xm = kXRun;
+    if (exm == 2 && M > 1) p.xm = M <= 8 ? 8 : 16 * p.mt;
     const int ens = env_int("W4A16_DECODE_NS", 0), ewk = env_int("W4A16_DECODE_WK", 0);
     if (ens == 1 || ens == 2 || ens == 4) p.ns = ens;
     if (p.mt == 4 && p.ns == 4) p.ns = 2;
-    if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1 && !p.sp)) p.wk = ewk;
+    if (ewk == 4 || ewk == 8 || (ewk == 16 && p.mt == 1)) p.wk = ewk;
     if (p.mt > 1 && p.wk > 8) p.wk = 8;
     if (p.xm == 64) p.wk = 4;  // two 64-row slots per wave: 128 KiB of LDS at 4 waves
     p.splits = 1;
     p.slice_blocks = 0;
-    if (p.sp) {
-        if (p.wk == 16) p.wk = 8;
-        return p;
-    }
     // no more waves than blocks of K (idle waves would still hold LDS)
     while (p.wk > 4 && p.wk > nblk) p.wk /= 2;
     // the cross-wave reduction buffer must leave room for the staged records
@@ -752,8 +520,7 @@ uint32_t ring_lds(const Plan &p) {
 }
 
 uint32_t plan_lds(const Plan &p, int M, int G, int slice_blocks) {
-    return p.sp ? sp_lds(M, p.ns, p.wk, slice_blocks, G).total
-                : decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xm).total() + ring_lds(p);
+    return decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xm).total() + ring_lds(p);
 }
 
 // A plan may use all of a CU's LDS when it runs one workgroup per CU (the
@@ -764,10 +531,7 @@ bool lds_fits(const Plan &p, int M, int G, int slice_blocks, long workgroups, in
     return plan_lds(p, M, G, slice_blocks) <= (one_per_cu ? kLdsMax : kLdsBudget);
 }
 
-int plan_tiles(const Plan &p, int N) {
-    const int per = p.ns * (p.sp ? p.wk : 1);
-    return (N / kStripCols + per - 1) / per;
-}
+int plan_tiles(const Plan &p, int N) { return (N / kStripCols + p.ns - 1) / p.ns; }
 
 Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     Plan p = base_plan(M, N, K);
@@ -776,11 +540,11 @@ Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     if (splits <= 0 && p.fixed_splits) splits = 1;
     if (splits <= 0) {
         // Narrow N: about one workgroup per CU, keeping at least two blocks
-        // per wave (decode_kernel) or per slice (strip-parallel kernel).
+        // per wave.
         splits = 1;
         if (tiles < num_cus) {
             splits = (num_cus + tiles - 1) / tiles;
-            int cap = p.sp ? nblk / 2 : nblk / (2 * p.wk);
+            int cap = nblk / (2 * p.wk);
             if (cap < 1) cap = 1;
             if (splits > cap) splits = cap;
         }
@@ -794,59 +558,6 @@ Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     p.slice_blocks = slice_for(K, G, splits);
     p.splits = (nblk + p.slice_blocks - 1) / p.slice_blocks;
     return p;
-}
-
-template <int MT, int NS, int WK, int GS>
-hipError_t launch_sp_one(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y,
-                         float *part, const Plan &p, hipStream_t stream) {
-    constexpr int NB = (MT == 1 && NS == 1) ? 2 : 1;
-    const SpLds L = sp_lds(M, NS, WK, p.slice_blocks, 32 * GS);
-    const int tiles = (N / kStripCols + WK * NS - 1) / (WK * NS);
-    hipLaunchKernelGGL((decode_sp_kernel<MT, NS, WK, NB, GS>), dim3(tiles, p.splits), dim3(WK * 64), L.total,
-                       stream, X, packed, Y, part, M, N, K, p.splits, p.slice_blocks);
-    return hipGetLastError();
-}
-
-template <int MT, int NS, int WK>
-hipError_t launch_sp_g(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
-                       float *part, const Plan &p, hipStream_t stream) {
-    switch (G) {
-        case 32: return launch_sp_one<MT, NS, WK, 1>(X, packed, M, N, K, Y, part, p, stream);
-        case 64: return launch_sp_one<MT, NS, WK, 2>(X, packed, M, N, K, Y, part, p, stream);
-        case 128: return launch_sp_one<MT, NS, WK, 4>(X, packed, M, N, K, Y, part, p, stream);
-        case 256: return launch_sp_one<MT, NS, WK, 8>(X, packed, M, N, K, Y, part, p, stream);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int MT, int NS>
-hipError_t launch_sp_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
-                        float *part, const Plan &p, hipStream_t stream) {
-    if (p.wk == 8) return launch_sp_g<MT, NS, 8>(X, packed, M, N, K, G, Y, part, p, stream);
-    return launch_sp_g<MT, NS, 4>(X, packed, M, N, K, G, Y, part, p, stream);
-}
-
-hipError_t launch_sp(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
-                     float *part, const Plan &p, hipStream_t stream) {
-    switch (p.mt) {
-        case 1:
-            switch (p.ns) {
-                case 1: return launch_sp_wk<1, 1>(X, packed, M, N, K, G, Y, part, p, stream);
-                case 2: return launch_sp_wk<1, 2>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_sp_wk<1, 4>(X, packed, M, N, K, G, Y, part, p, stream);
-            }
-        case 2:
-            switch (p.ns) {
-                case 1: return launch_sp_wk<2, 1>(X, packed, M, N, K, G, Y, part, p, stream);
-                case 2: return launch_sp_wk<2, 2>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_sp_wk<2, 4>(X, packed, M, N, K, G, Y, part, p, stream);
-            }
-        default:
-            switch (p.ns) {
-                case 1: return launch_sp_wk<4, 1>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_sp_wk<4, 2>(X, packed, M, N, K, G, Y, part, p, stream);
-            }
-    }
 }
 
 template <int MT, int NS, int WK, int GS, int XM>
@@ -888,54 +599,35 @@ hipError_t launch_wk(const uint16_t *X, const uint8_t *packed, int M, int N, int
 
 hipError_t launch_plan(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                        float *part, const Plan &p, hipStream_t stream) {
-    if (p.sp) return launch_sp(X, packed, M, N, K, G, Y, part, p, stream);
-    if (p.xm == kXRun) {  // M = 1 (M <= 16 when tuning)
-        switch (p.ns) {
-            case 1: return launch_wk<1, 1, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
-            case 2: return launch_wk<1, 2, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
-            default: return launch_wk<1, 4, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
-        }
-    }
-    if (p.xm == 64) {  // 33 <= M <= 64
-        if (p.ns == 1) return launch_wk<4, 1, 64>(X, packed, M, N, K, G, Y, part, p, stream);
-        return launch_wk<4, 2, 64>(X, packed, M, N, K, G, Y, part, p, stream);
-    }
-    if (p.xm == 32) {  // 17 <= M <= 32
-        switch (p.ns) {
-            case 1: return launch_wk<2, 1, 32>(X, packed, M, N, K, G, Y, part, p, stream);
-            case 2: return launch_wk<2, 2, 32>(X, packed, M, N, K, G, Y, part, p, stream);
-            default: return launch_wk<2, 4, 32>(X, packed, M, N, K, G, Y, part, p, stream);
-        }
-    }
-    if (p.xm == 8 || p.xm == 16) {  // 2 <= M <= 16
-        const bool r8 = p.xm == 8;
-        switch (p.ns) {
-            case 1: return r8 ? launch_wk<1, 1, 8>(X, packed, M, N, K, G, Y, part, p, stream)
-                              : launch_wk<1, 1, 16>(X, packed, M, N, K, G, Y, part, p, stream);
-            case 2: return r8 ? launch_wk<1, 2, 8>(X, packed, M, N, K, G, Y, part, p, stream)
-                              : launch_wk<1, 2, 16>(X, packed, M, N, K, G, Y, part, p, stream);
-            default: return r8 ? launch_wk<1, 4, 8>(X, packed, M, N, K, G, Y, part, p, stream)
-                               : launch_wk<1, 4, 16>(X, packed, M, N, K, G, Y, part, p, stream);
-        }
-    }
-    switch (p.mt) {
-        case 1:
+    switch (p.xm) {
+        case kXRun:  // M = 1 (M <= 16 when tuning)
             switch (p.ns) {
-                case 1: return launch_wk<1, 1, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
-                case 2: return launch_wk<1, 2, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_wk<1, 4, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 1: return launch_wk<1, 1, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_wk<1, 2, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<1, 4, kXRun>(X, packed, M, N, K, G, Y, part, p, stream);
             }
-        case 2:
+        case 8:  // 2 <= M <= 8
             switch (p.ns) {
-                case 1: return launch_wk<2, 1, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
-                case 2: return launch_wk<2, 2, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_wk<2, 4, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 1: return launch_wk<1, 1, 8>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_wk<1, 2, 8>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<1, 4, 8>(X, packed, M, N, K, G, Y, part, p, stream);
             }
-        default:
+        case 16:  // 9 <= M <= 16
             switch (p.ns) {
-                case 1: return launch_wk<4, 1, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
-                default: return launch_wk<4, 2, kXReg>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 1: return launch_wk<1, 1, 16>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_wk<1, 2, 16>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<1, 4, 16>(X, packed, M, N, K, G, Y, part, p, stream);
             }
+        case 32:  // 17 <= M <= 32
+            switch (p.ns) {
+                case 1: return launch_wk<2, 1, 32>(X, packed, M, N, K, G, Y, part, p, stream);
+                case 2: return launch_wk<2, 2, 32>(X, packed, M, N, K, G, Y, part, p, stream);
+                default: return launch_wk<2, 4, 32>(X, packed, M, N, K, G, Y, part, p, stream);
+            }
+        case 64:  // 33 <= M <= 64
+            if (p.ns == 1) return launch_wk<4, 1, 64>(X, packed, M, N, K, G, Y, part, p, stream);
+            return launch_wk<4, 2, 64>(X, packed, M, N, K, G, Y, part, p, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 
