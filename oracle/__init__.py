@@ -12,6 +12,9 @@ Contents
   follows).
 * ``compare``: the parity metrics (max |dY| relative to max |Y_ref|, relative
   Frobenius error).
+* ``quantize``: the group-wise asymmetric 4-bit quantizer that produces
+  (q, z, s) from fp16 weights (``quantize.py``; its header states the
+  reading of the pages it follows).
 * ``layout_pack`` / ``layout_unpack``: the packed weight format written out as
   plain index arithmetic, so the bytes the GPU packer writes can be checked
   one by one. The pages ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
@@ -46,9 +49,11 @@ import subprocess
 
 import numpy as np
 
+from .quantize import quantize
+
 __all__ = [
     "lib_path", "build", "load", "half_to_double", "dequant", "gemm", "compare",
-    "packed_bytes", "layout_pack", "layout_unpack", "max_threads",
+    "packed_bytes", "layout_pack", "layout_unpack", "max_threads", "quantize",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -30,6 +30,12 @@ Draw order for one (workload, matrix), from a fresh ``np.random.default_rng
 5. ``X = standard_normal((M, K))`` in float64, outlier columns times 20, then
    one cast to float16.
 
+Quantizer inputs (fp16 weights before quantization), ``draw_fp16_weights``:
+from a fresh generator, ``normal(0, 0.02, (K, N))`` in float64, then 1% of
+the input channels (rows k, ``choice(K, round(0.01 K), replace=False)``)
+times 4, standing in for the salient channels AWQ scales up before it
+quantizes, then one cast to float16.
+
 Weights and the outlier set are drawn before X, so for a sweep over M they are
 identical, and X for a smaller M is the leading rows of X for a larger M.
 """
@@ -39,7 +45,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Instance", "WORKLOADS", "draw_weights", "draw_x", "draw", "workload_instances"]
+__all__ = ["Instance", "WORKLOADS", "draw_weights", "draw_x", "draw", "workload_instances",
+           "draw_fp16_weights"]
 
 
 @dataclass(frozen=True)
@@ -127,3 +134,12 @@ def draw(inst: Instance):
     q, z, s, idx, rng = draw_weights(inst.K, inst.N, inst.G, inst.seed, inst.outliers)
     X = draw_x(rng, inst.M, inst.K, idx)
     return X, q, z, s
+
+
+def draw_fp16_weights(K: int, N: int, seed: int = 0) -> np.ndarray:
+    """fp16 W [K][N] for the quantizer: N(0, 0.02) with 1% of the rows x4."""
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0.0, 0.02, (K, N))
+    rows = rng.choice(K, max(1, int(round(0.01 * K))), replace=False)
+    w[rows] *= 4.0
+    return w.astype(np.float16)
