@@ -20,23 +20,26 @@ plain asymmetric one: the group's own range [min, max] is spread over the 16
 codes, the zero is the code of the value 0, and every weight goes to the
 nearest code.
 
-Every step is float32 arithmetic, each operation rounded to nearest even
-(numpy float32 ufuncs), in this order:
+The scale is float32 arithmetic, each operation rounded to nearest even
+(numpy float32 ufuncs); the codes round an exact product once:
 
     wmax, wmin = largest and smallest weight of the group       (exact)
-    s32 = max((wmax - wmin) / 15, 2**-14)
-    s   = float16(s32)                                          (stored scale)
-    inv = 1 / float32(s)
+    s32 = max((wmax - wmin) / 15, 2**-14)                        (float32)
+    s   = float16(s32)                                           (stored scale)
+    inv = 1 / float32(s)                                         (float32)
     z   = min(max(rint(-wmin * inv), 0), 15)
-    q   = min(max(rint(w * inv) + z, 0), 15)                    (each weight)
+    q   = min(max(rint(w * inv) + z, 0), 15)                     (each weight)
 
-rint rounds half to even. The floor 2**-14 (the smallest normal fp16) gives a
-group whose weights are all equal a usable scale: all zeros quantize to
-q = z = 0 exactly; a constant c != 0 saturates to the code 15 or 0. Where the
-range excludes 0 the zero code saturates too, and weights beyond the
-representable end saturate; both are properties of the method, not of this
-code. Codes are decided with the reciprocal of the stored fp16 scale, so the
-codes are those of the scale actually stored.
+where w * inv is the exact product of an fp16 and a float32 number (at most
+35 significant bits, so float64 holds it exactly) and rint rounds it to the
+nearest integer, ties to even: one rounding, as round-to-nearest reads. The
+floor 2**-14 (the smallest normal fp16) gives a group whose weights are all
+equal a usable scale: all zeros quantize to q = z = 0 exactly; a constant
+c != 0 saturates to the code 15 or 0. Where the range excludes 0 the zero
+code saturates too, and weights beyond the representable end saturate; both
+are properties of the method, not of this code. Codes are decided with the
+reciprocal of the stored fp16 scale, so they are the codes of the scale
+actually stored.
 
 Inputs must be finite (a non-finite weight raises ValueError).
 """
@@ -65,7 +68,7 @@ def quantize(W, G: int):
     wmin = Wg.min(axis=1)
     s32 = np.maximum((wmax - wmin) / f32(15), SCALE_FLOOR)
     s = s32.astype(np.float16)
-    inv = f32(1) / s.astype(f32)
-    z = np.minimum(np.maximum(np.rint(-wmin * inv), f32(0)), f32(15))
-    q = np.minimum(np.maximum(np.rint(Wg * inv[:, None, :]) + z[:, None, :], f32(0)), f32(15))
+    inv = (f32(1) / s.astype(f32)).astype(np.float64)   # float32 value, held exactly
+    z = np.minimum(np.maximum(np.rint(-wmin.astype(np.float64) * inv), 0.0), 15.0)
+    q = np.minimum(np.maximum(np.rint(Wg.astype(np.float64) * inv[:, None, :]) + z[:, None, :], 0.0), 15.0)
     return (q.reshape(K, N).astype(np.uint8), z.astype(np.uint8), s)

@@ -48,6 +48,27 @@ def test_ties_round_to_even():
     assert list(q[:7, 3]) == [0, 15, 8, 10, 8, 6, 10]
 
 
+def test_codes_round_the_exact_product_once():
+    # range 0.1279296875 - (-0.125) = 0.2529296875; / 15 -> fp16 0x2451
+    # (0.016860961914...), whose float32 reciprocal is 59.308597564697266.
+    # The zero is rint(0.125 * 59.3086) = rint(7.41) = 7. The weight
+    # 0.00843048095703125 times that reciprocal is 0.50000000236 exactly
+    # (Fraction below): just above one half, so its code is 7 + 1 = 8, and
+    # its negative gets 7 - 1 = 6. Rounding the product to float32 first
+    # would land on exactly 0.5 and round to even (code 7).
+    from fractions import Fraction
+    w = 0.00843048095703125
+    vals = [-0.125, 0.1279296875, w, -w] + [0.0] * 28
+    q, z, s = oracle.quantize(_col(vals), 32)
+    assert np.all(s.view(np.uint16) == 0x2451)
+    inv = np.float32(1) / np.float32(s[0, 0])
+    assert float(inv) == 59.308597564697266
+    assert Fraction(w) * Fraction(float(inv)) > Fraction(1, 2)
+    assert float(np.float32(w * float(inv))) == 0.5
+    assert np.all(z == 7)
+    assert list(q[:4, 5]) == [0, 15, 8, 6]
+
+
 def test_all_zero_group():
     q, z, s = oracle.quantize(np.zeros((64, 16), np.float16), 64)
     assert np.all(s == np.float16(2.0 ** -14)) and np.all(z == 0) and np.all(q == 0)
@@ -101,8 +122,9 @@ def test_every_code_is_the_nearest(G):
     err = np.abs(w - (q.astype(np.float64) - z64) * s64)
     codes = np.arange(16, dtype=np.float64)[:, None, None]
     best = np.abs(w[None] - (codes - z64[None]) * s64[None]).min(axis=0)
-    # the code decision uses the float32 reciprocal of s: allow a relative
-    # slack of a few float32 ulps of the quotient near ties
+    # the code decision uses the float32 reciprocal of s (one rounding of
+    # the exact product): allow a relative slack of a few float32 ulps of
+    # the quotient near ties
     assert np.all(err <= best + 1e-6 * s64 * (1 + np.abs(w / s64)))
 
 
@@ -188,32 +210,36 @@ def _wrong_quantizers():
     f32 = np.float32
     real_quantize = oracle.quantize
 
-    def common(W, G, *, steps=15, zsign=1, rnd=np.rint, coded_scale=True, clamp_z=True):
+    def common(W, G, *, steps=15, zsign=1, rnd=np.rint, coded_scale=True, clamp_z=True, f32_product=False):
         K, N = W.shape
         Wg = W.astype(f32).reshape(K // G, G, N)
         wmax, wmin = Wg.max(axis=1), Wg.min(axis=1)
         s32 = np.maximum((wmax - wmin) / f32(steps), SCALE_FLOOR)
         s = s32.astype(np.float16)
         inv = f32(1) / (s.astype(f32) if coded_scale else s32)
+        if not f32_product:  # exact products, as the oracle takes them
+            inv, wmin, Wg = inv.astype(np.float64), wmin.astype(np.float64), Wg.astype(np.float64)
         zz = rnd(-zsign * wmin * inv)
-        z = np.minimum(np.maximum(zz, f32(0)), f32(15)) if clamp_z else np.mod(zz, 256)
-        q = np.minimum(np.maximum(rnd(Wg * inv[:, None, :]) + z[:, None, :], f32(0)), f32(15))
+        z = np.minimum(np.maximum(zz, 0), 15) if clamp_z else np.mod(zz, 256)
+        q = np.minimum(np.maximum(rnd(Wg * inv[:, None, :]) + z[:, None, :], 0), 15)
         return q.reshape(K, N).astype(np.uint8), z.astype(np.uint8), s
 
     return [
         lambda W, G: common(W, G, steps=16),                                  # 16 steps, not 15
         lambda W, G: common(W, G, zsign=-1),                                  # zero of the wrong sign
-        lambda W, G: common(W, G, rnd=lambda x: np.floor(x + f32(0.5))),     # ties away from even
+        lambda W, G: common(W, G, rnd=lambda x: np.floor(x + 0.5)),          # ties away from even
         lambda W, G: common(W, G, coded_scale=False),                         # codes from the unrounded scale
         lambda W, G: common(W, G, clamp_z=False),                             # zero not clamped
         lambda W, G: common(W, G, rnd=np.trunc),                              # truncation, not rounding
         lambda W, G: tuple(a.T.copy() for a in real_quantize(W.T.copy(), G)),  # groups along N
+        lambda W, G: common(W, G, f32_product=True),                          # product rounded twice
     ]
 
 
 def _pins_fail(fn):
     failures = 0
     checks = [test_exact_grid_group, test_ties_round_to_even, test_constant_group_saturates,
+              test_codes_round_the_exact_product_once,
               test_range_excluding_zero, test_groups_run_along_k, test_quantized_weights_round_trip,
               lambda: test_every_code_is_the_nearest(32)]
     real = oracle.quantize
@@ -229,7 +255,7 @@ def _pins_fail(fn):
     return failures
 
 
-@pytest.mark.parametrize("idx", range(7))
+@pytest.mark.parametrize("idx", range(8))
 def test_planted_mistakes_are_caught(idx):
     assert _pins_fail(_wrong_quantizers()[idx]) > 0
     assert _pins_fail(oracle.quantize) == 0
