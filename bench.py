@@ -64,6 +64,8 @@ def parse_args(argv=None):
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="before timing, run one device copy of BYTES bytes (reference for HBM counters)")
     p.add_argument("--detail", action="store_true", help="per-instance lines to stderr")
+    p.add_argument("--quantizer-only", action="store_true",
+                   help="time only the offline quantizer (fp16 W -> packed) and print its line")
     return p.parse_args(argv)
 
 
@@ -255,6 +257,50 @@ def run_prefill_secondary(args):
     }
 
 
+def run_quantize_secondary(args, calls=20):
+    """The offline quantizer (fp16 W -> packed) on the Llama-3-70B gate/up
+    weight, K=8192, N=57344, G=128: bytes = 2 K N read + the packed buffer
+    written. Each call clears the device status word, quantizes, reads the
+    word back and synchronizes; HIP events on the call's stream bracket the
+    whole call."""
+    import torch
+
+    import w4a16_mixed_precision_amd as w4
+    K, N, G = 8192, 57344, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(70)
+    # same recipe as synth.draw_fp16_weights, drawn on the device
+    W = torch.randn((K, N), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    rows = torch.randperm(K, generator=gen, device="cuda")[: round(0.01 * K)]
+    W[rows] *= 4.0
+    W = W.half()
+    packed = torch.empty(w4.w4a16_packed_bytes(K, N, G), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        w4.w4a16_quantize_pack(W, G, packed)
+    st = torch.cuda.current_stream()
+    times = []
+    for _ in range(calls):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        w4.w4a16_quantize_pack(W, G, packed)
+        b.record(st)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(sorted(times)[len(times) // 2])
+    nbytes = 2 * K * N + w4.w4a16_packed_bytes(K, N, G)
+    del W, packed
+    torch.cuda.empty_cache()
+    return {
+        "metric": "quantize+pack GB/s, Llama-3-70B gate_up weight (K=8192, N=57344, G=128)",
+        "value": nbytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "ms_per_call": ms,
+        "bytes_per_call": nbytes,
+        "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "timing": "median of %d synchronous calls, HIP events around each call" % calls,
+    }
+
+
 def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -270,6 +316,9 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.quantizer_only:
+        print(json.dumps(run_quantize_secondary(args)), flush=True)
+        return 0
     insts = synth.workload_instances(args.workload)
     prefill = all(i.M > 32 for i in insts)
     runner = Runner(insts, args.rotate_gib * 2 ** 30)
@@ -354,6 +403,7 @@ def main(argv=None):
     }
     if not prefill and not args.no_secondary:
         out["secondary"] = run_prefill_secondary(args)
+        out["quantizer"] = run_quantize_secondary(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(runner)
     print(json.dumps(out), flush=True)

@@ -16,7 +16,9 @@
  * ("LMDeploy Accelerates Mixed-Precision LLM Inference with TurboMind",
  * abstract: offline weight packing plus online acceleration):
  *   - w4a16_pack: an offline, lossless relayout of (q, z, s) into one packed
- *     buffer laid out in the order the gfx950 matrix instructions consume it;
+ *     buffer laid out in the order the gfx950 matrix instructions consume it
+ *     (w4a16_quantize produces (q, z, s) from fp16 weights;
+ *     w4a16_quantize_pack does both in one pass);
  *   - w4a16_gemm: the online dequantize-and-multiply.
  *
  * Conventions for every call
@@ -66,7 +68,8 @@ extern "C" {
 #define W4A16_ERR_NULL (-1)      /* a required pointer is NULL */
 #define W4A16_ERR_SHAPE (-2)     /* M, N, K or G outside the supported set */
 #define W4A16_ERR_ALIGN (-3)     /* a device pointer is not 16-byte aligned */
-#define W4A16_ERR_RANGE (-4)     /* pack: a q or z code is larger than 15 */
+#define W4A16_ERR_RANGE (-4)     /* pack: a q or z code is larger than 15;
+                                    quantize: a weight is Inf or NaN */
 #define W4A16_ERR_HIP (-5)       /* a HIP runtime call or kernel launch failed */
 #define W4A16_ERR_WORKSPACE (-6) /* workspace missing or smaller than required */
 #define W4A16_ERR_ARG (-7)       /* path or split selector out of range */
@@ -97,6 +100,45 @@ size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t G);
  */
 int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales,
                int64_t K, int64_t N, int64_t G, void *packed, void *stream);
+
+/*
+ * Group-wise asymmetric 4-bit quantizer, the step that produces the inputs
+ * of w4a16_pack from fp16 weights. The pages quantize weights to uniform
+ * 4-bit codes in groups of 128 rows with one scale per group ("LMDeploy, in
+ * depth", section "Quantization: AWQ weights and KV cache", paragraph
+ * "Weight quantization (W4A16)"), dequantized by the formula above, and call
+ * the plain form round-to-nearest ("LMDeploy" interview notes, the answer on
+ * AWQ versus naive RTN INT4; AWQ's calibrated channel scaling, applied to
+ * the weights before this step, is not part of it). The scale and zero
+ * spread the group's range [min, max] over 15 steps; per group g and
+ * column n, in float32 unless stated:
+ *   s   = fp16(max((max - min) / 15, 2^-14))     (round to nearest even)
+ *   inv = 1 / s
+ *   z   = clamp(rint(-min * inv), 0, 15)
+ *   q   = clamp(rint(w * inv) + z, 0, 15)         for every weight w
+ * where each product is exact and rint rounds it once to the nearest
+ * integer, ties to even. A group of equal weights gets the scale 2^-14 (all
+ * zeros give q = z = 0); codes saturate at 0 and 15.
+ *
+ *   W       fp16  [K][N]     weights (finite)
+ *   q       uint8 [K][N]     codes 0..15, one per byte
+ *   zeros   uint8 [K/G][N]   codes 0..15
+ *   scales  fp16  [K/G][N]
+ * Shapes as for w4a16_pack. Enqueued on `stream`, then synchronizes it
+ * (offline pass) to report W4A16_ERR_RANGE if a weight is Inf or NaN; on that
+ * error the outputs are unspecified.
+ */
+int w4a16_quantize(const uint16_t *W, int64_t K, int64_t N, int64_t G,
+                   uint8_t *q, uint8_t *zeros, uint16_t *scales, void *stream);
+
+/*
+ * w4a16_quantize fused with w4a16_pack: one pass over W writes the packed
+ * buffer (w4a16_packed_bytes(K, N, G) bytes, caller-allocated), byte for
+ * byte what w4a16_pack makes of w4a16_quantize's output. Synchronizes
+ * `stream`; W4A16_ERR_RANGE as for w4a16_quantize.
+ */
+int w4a16_quantize_pack(const uint16_t *W, int64_t K, int64_t N, int64_t G,
+                        void *packed, void *stream);
 
 /*
  * Exact inverse of w4a16_pack: recovers q, zeros and scales (same layouts as

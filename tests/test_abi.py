@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
               "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
-              "w4a16_layout_version", "w4a16_auto_path"):
+              "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack"):
         assert n in names
 
 
@@ -99,6 +99,19 @@ def test_pack_validation_before_any_hip_call():
     assert L.w4a16_pack(FAKE, FAKE, FAKE, 256, 256, 128, MISALIGNED, None) == w4.W4A16_ERR_ALIGN
     assert L.w4a16_unpack(FAKE, 256, 256, 128, None, FAKE, FAKE, None) == w4.W4A16_ERR_NULL
     assert L.w4a16_unpack(FAKE, 256, 256, 100, FAKE, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
+
+
+def test_quantize_validation_before_any_hip_call():
+    L = w4.lib()
+    assert L.w4a16_quantize(None, 256, 256, 128, FAKE, FAKE, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_quantize(FAKE, 256, 256, 128, FAKE, None, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_quantize(FAKE, 256, 250, 128, FAKE, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_quantize(FAKE, 192, 256, 64, FAKE, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_quantize(MISALIGNED, 256, 256, 128, FAKE, FAKE, FAKE, None) == w4.W4A16_ERR_ALIGN
+    assert L.w4a16_quantize(FAKE, 256, 256, 128, FAKE, MISALIGNED, FAKE, None) == w4.W4A16_ERR_ALIGN
+    assert L.w4a16_quantize_pack(FAKE, 256, 256, 128, None, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_quantize_pack(FAKE, 256, 256, 96, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_quantize_pack(FAKE, 256, 256, 128, MISALIGNED, None) == w4.W4A16_ERR_ALIGN
 
 
 def test_status_strings():

@@ -1,0 +1,158 @@
+"""GPU parity of the group-wise 4-bit quantizer against the oracle.
+
+Codes, zeros and scales are integer and byte decisions taken in the same
+precision on both sides, so the bar is bit-exact: w4a16_quantize must return
+the oracle's (q, z, s) byte for byte, and w4a16_quantize_pack must write the
+bytes that the oracle's layout writer (and w4a16_pack) makes of them.
+
+Inputs: ``synth.draw_fp16_weights`` (N(0, 0.02) with 1% of the rows x4),
+plus groups built by hand for the method's degenerate cases (all zeros,
+constant, a range that excludes zero, exact ties, a product just above one
+half). The quantizer works column by column, so at full size the oracle
+runs on column windows and the device output is compared on the same
+windows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a16_mixed_precision_amd as w4
+from gpu_util import TOL_FRO, TOL_MAX, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_plain(W, G):
+    q, z, s = oracle.quantize(W, G)
+    qd, zd, sd = (host(t) for t in w4.w4a16_quantize(dev(W), G))
+    assert np.array_equal(qd, q), np.argwhere(qd != q)[:5]
+    assert np.array_equal(zd, z), np.argwhere(zd != z)[:5]
+    assert np.array_equal(sd.view(np.uint16), s.view(np.uint16))
+    return q, z, s
+
+
+def _check_packed(W, G, q, z, s):
+    pd = host(w4.w4a16_quantize_pack(dev(W), G))
+    ref = oracle.layout_pack(q, z, s, G)
+    assert pd.shape == ref.shape
+    bad = np.flatnonzero(pd != ref)
+    assert bad.size == 0, bad[:8]
+
+
+SHAPES = [
+    # K, N, G: several tiles in both directions and ragged column tails
+    (256, 256, 128), (512, 80, 32), (512, 48, 64), (1024, 208, 128), (512, 144, 256),
+    (768, 16, 128), (384, 6160, 128), (4096, 112, 64), (256, 4112, 256), (1280, 1040, 32),
+]
+
+
+@pytest.mark.parametrize("K,N,G", SHAPES)
+def test_quantize_matches_oracle(K, N, G):
+    say(f"quantize K={K} N={N} G={G}")
+    W = synth.draw_fp16_weights(K, N, seed=K + N + G)
+    q, z, s = _check_plain(W, G)
+    _check_packed(W, G, q, z, s)
+
+
+def _edge_matrix(G):
+    """Columns of hand-built groups, one case per 16-column strip."""
+    K, N = 2 * max(G, 128), 128
+    rng = np.random.default_rng(G)
+    W = rng.normal(0, 0.02, (K, N))
+    w = 0.00843048095703125
+    for g0 in range(0, K, G):
+        rows = slice(g0, g0 + G)
+        W[rows, 0:16] = 0.0                                   # all zeros
+        W[rows, 16:32] = 0.5                                  # constant
+        W[rows, 32:48] = 2.5                                  # range excluding zero
+        W[g0, 32:48], W[g0 + 1, 32:48] = 2.0, 3.5
+        grid = np.array([(i - 8) * 0.125 for i in range(16)] * (G // 16))
+        W[rows, 48:64] = grid[:, None]                        # exact grid
+        W[g0 + 2: g0 + 7, 48:64] = np.array([0.0625, 0.1875, -0.0625, -0.1875, 0.3125])[:, None]
+        W[rows, 64:80] = 0.0                                  # product just above 1/2
+        W[g0: g0 + 4, 64:80] = np.array([-0.125, 0.1279296875, w, -w])[:, None]
+        W[rows, 80:96] = -1e-7                                # fp16 subnormals: scale
+        W[g0, 80:96] = 3e-7                                   # floored, 1/s = 16384, and
+        W[g0 + 1, 80:96] = 5e-5                               # 5e-5 * 16384 = 0.82 -> code 1
+        W[rows, 96:112] = 65504.0 * np.sign(rng.standard_normal((G, 16)))   # extremes
+    W[:, 112:128] *= 1e3                                      # large ordinary weights
+    return W.astype(np.float16)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
+def test_degenerate_groups(G):
+    say(f"quantize edge groups G={G}")
+    W = _edge_matrix(G)
+    q, z, s = _check_plain(W, G)
+    _check_packed(W, G, q, z, s)
+
+
+def test_non_finite_weight_is_reported():
+    W = synth.draw_fp16_weights(256, 64, seed=3)
+    for bad in (np.inf, -np.inf, np.nan):
+        Wb = W.copy()
+        Wb[100, 17] = bad
+        with pytest.raises(w4.W4A16Error) as ei:
+            w4.w4a16_quantize(dev(Wb), 128)
+        assert ei.value.status == w4.W4A16_ERR_RANGE
+        with pytest.raises(w4.W4A16Error):
+            w4.w4a16_quantize_pack(dev(Wb), 128)
+    # the status word is cleared per call: a good call afterwards succeeds
+    _check_plain(W, 128)
+
+
+def test_quantize_pack_equals_pack_of_quantize():
+    W = synth.draw_fp16_weights(1024, 528, seed=9)
+    Wd = dev(W)
+    q, z, s = w4.w4a16_quantize(Wd, 64)
+    a = host(w4.w4a16_pack(q, z, s, 64))
+    b = host(w4.w4a16_quantize_pack(Wd, 64))
+    assert np.array_equal(a, b)
+
+
+def test_tile_width_knob_gives_the_same_bytes(monkeypatch):
+    W = synth.draw_fp16_weights(512, 272, seed=4)
+    Wd = dev(W)
+    outs = []
+    for cb in ("64", "128"):
+        monkeypatch.setenv("W4A16_QUANTIZE_CB", cb)
+        outs.append(host(w4.w4a16_quantize_pack(Wd, 128)))
+        q, z, s = (host(t) for t in w4.w4a16_quantize(Wd, 128))
+        outs.append(np.concatenate([q.ravel(), z.ravel(), s.view(np.uint8).ravel()]))
+    assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+
+
+def test_quantized_weights_through_the_gemm():
+    # fp16 W -> device quantize+pack -> GEMM, against the oracle GEMM on the
+    # oracle's codes: the whole offline + online pipeline
+    K, N, G, M = 2048, 1024, 128, 8
+    W = synth.draw_fp16_weights(K, N, seed=21)
+    X = np.random.default_rng(22).standard_normal((M, K)).astype(np.float16)
+    q, z, s = oracle.quantize(W, G)
+    Yref = oracle.gemm(X, q, z, s, G)
+    packed = w4.w4a16_quantize_pack(dev(W), G)
+    Y = host(w4.w4a16_gemm(dev(X), packed, N, K, G))
+    c = oracle.compare(Y, Yref)
+    assert c["finite"] and c["rel_max"] <= TOL_MAX and c["rel_fro"] <= TOL_FRO, c
+
+
+def test_full_size_llama3_70b_gate_up_windows():
+    # 8192 x 57344 fp16 (940 MB), G = 128, as the 70B gate/up projection
+    import torch
+    K, N, G = 8192, 57344, 128
+    say("quantize full size 8192 x 57344: drawing weights")
+    W = synth.draw_fp16_weights(K, N, seed=70)
+    Wd = dev(W)
+    packed = w4.w4a16_quantize_pack(Wd, G)
+    q, z, s = w4.w4a16_quantize(Wd, G)
+    del Wd
+    qp, zp, sp = w4.w4a16_unpack(packed, K, N, G)
+    assert torch.equal(qp, q) and torch.equal(zp, z) and torch.equal(sp.view(torch.int16), s.view(torch.int16))
+    rng = np.random.default_rng(70)
+    for c0 in (0, int(rng.integers(1, N // 64 - 2)) * 64, N - 64):
+        say(f"  window {c0}..{c0 + 64}")
+        qo, zo, so = oracle.quantize(np.ascontiguousarray(W[:, c0:c0 + 64]), G)
+        assert np.array_equal(host(q[:, c0:c0 + 64]), qo)
+        assert np.array_equal(host(z[:, c0:c0 + 64]), zo)
+        assert np.array_equal(host(s[:, c0:c0 + 64]).view(np.uint16), so.view(np.uint16))

@@ -20,7 +20,7 @@ __all__ = [
     "W4A16_PATH_AUTO", "W4A16_PATH_DECODE", "W4A16_PATH_PREFILL",
     "w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
-    "w4a16_layout_version", "w4a16_auto_path",
+    "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack",
 ]
 
 W4A16_OK = 0
@@ -74,6 +74,10 @@ def lib():
     L.w4a16_layout_version.argtypes = []
     L.w4a16_layout_version.restype = I
     L.w4a16_auto_path.argtypes = [I64, I64, I64, I64]
+    L.w4a16_quantize.argtypes = [P, I64, I64, I64, P, P, P, P]
+    L.w4a16_quantize.restype = I
+    L.w4a16_quantize_pack.argtypes = [P, I64, I64, I64, P, P]
+    L.w4a16_quantize_pack.restype = I
     L.w4a16_auto_path.restype = I
     _lib = L
     return L
@@ -151,6 +155,35 @@ def w4a16_pack(q, zeros, scales, G: int, packed=None, stream=None):
     _check(lib().w4a16_pack(_dev_ptr(q, torch.uint8, "q"), _dev_ptr(zeros, torch.uint8, "zeros"),
                             _dev_ptr(scales, torch.float16, "scales"), K, N, G,
                             _dev_ptr(packed, torch.uint8, "packed"), _stream(stream, q.device)))
+    return packed
+
+
+def w4a16_quantize(W, G: int, stream=None):
+    """Quantize fp16 W [K][N] (device tensor) group-wise to 4 bits: returns
+    (q uint8 [K][N], zeros uint8 [K/G][N], scales fp16 [K/G][N]) device tensors.
+    Synchronizes the stream."""
+    import torch
+    K, N = W.shape
+    dev = W.device
+    q = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    z = torch.empty((K // G, N), dtype=torch.uint8, device=dev)
+    s = torch.empty((K // G, N), dtype=torch.float16, device=dev)
+    _check(lib().w4a16_quantize(_dev_ptr(W, torch.float16, "W"), K, N, G, q.data_ptr(), z.data_ptr(),
+                                s.data_ptr(), _stream(stream, dev)))
+    return q, z, s
+
+
+def w4a16_quantize_pack(W, G: int, packed=None, stream=None):
+    """Quantize fp16 W [K][N] (device tensor) straight into the packed layout
+    (a uint8 device tensor of w4a16_packed_bytes(K, N, G) bytes, the same
+    bytes as w4a16_pack of w4a16_quantize's output). Synchronizes the stream."""
+    import torch
+    K, N = W.shape
+    nbytes = w4a16_packed_bytes(K, N, G)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    _check(lib().w4a16_quantize_pack(_dev_ptr(W, torch.float16, "W"), K, N, G,
+                                     _dev_ptr(packed, torch.uint8, "packed"), _stream(stream, W.device)))
     return packed
 
 

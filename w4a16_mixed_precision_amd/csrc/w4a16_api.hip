@@ -1,5 +1,5 @@
 // C ABI of the W4A16 library: argument validation, plan selection and the
-// per-device state (a small status word for pack, the lazily grown split-K
+// per-device state (a small status word for pack and the quantizer, the lazily grown split-K
 // workspace of w4a16_gemm). The declarations and their contract are in
 // include/w4a16.h.
 #include <hip/hip_runtime.h>
@@ -57,7 +57,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
     std::mutex mu;
     int num_cus = 0;
-    int *flag = nullptr;       // pack range-error word
+    int *flag = nullptr;       // pack range / quantizer finiteness error word
     void *ws = nullptr;        // w4a16_gemm split-K workspace
     size_t ws_bytes = 0;
 };
@@ -177,6 +177,28 @@ int launch(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t 
     return W4A16_OK;
 }
 
+// Runs one quantizer launch between clearing and reading the device's status
+// word; synchronizes `st`.
+template <class Launch>
+int run_quantizer(hipStream_t st, Launch &&launch_fn) {
+    int dev, rc;
+    if ((rc = current_device(&dev))) return rc;
+    int *flag;
+    if ((rc = device_flag(dev, &flag))) return rc;
+    hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
+    if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
+    e = launch_fn(flag);
+    if (e != hipSuccess) return fail_hip(e, "quantize launch");
+    int host_flag = 0;
+    e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    if (host_flag) return fail(W4A16_ERR_RANGE, "a weight is not finite (Inf or NaN)");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,6 +232,31 @@ int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales, i
     if (host_flag) return fail(W4A16_ERR_RANGE, "a q or zero code is larger than 15");
     g_last_error[0] = 0;
     return W4A16_OK;
+}
+
+int w4a16_quantize(const uint16_t *W, int64_t K, int64_t N, int64_t G, uint8_t *q, uint8_t *zeros,
+                   uint16_t *scales, void *stream) {
+    if (!W || !q || !zeros || !scales)
+        return fail(W4A16_ERR_NULL, "W, q, zeros and scales must be non-NULL");
+    int rc = check_shape(K, N, G);
+    if (rc) return rc;
+    if (!aligned16(W) || !aligned16(q) || !aligned16(zeros) || !aligned16(scales))
+        return fail(W4A16_ERR_ALIGN, "W, q, zeros and scales must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    return run_quantizer(st, [&](int *flag) {
+        return w4a16::launch_quantize(W, (int)K, (int)N, (int)G, q, zeros, scales, flag, st);
+    });
+}
+
+int w4a16_quantize_pack(const uint16_t *W, int64_t K, int64_t N, int64_t G, void *packed, void *stream) {
+    if (!W || !packed) return fail(W4A16_ERR_NULL, "W and packed must be non-NULL");
+    int rc = check_shape(K, N, G);
+    if (rc) return rc;
+    if (!aligned16(W) || !aligned16(packed)) return fail(W4A16_ERR_ALIGN, "W and packed must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    return run_quantizer(st, [&](int *flag) {
+        return w4a16::launch_quantize_pack(W, (int)K, (int)N, (int)G, (uint8_t *)packed, flag, st);
+    });
 }
 
 int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G, uint8_t *q, uint8_t *zeros,

@@ -15,6 +15,14 @@ hipError_t launch_pack(const uint8_t *q, const uint8_t *z, const uint16_t *s, in
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int G, uint8_t *q, uint8_t *z,
                          uint16_t *s, hipStream_t stream);
 
+// Group-wise 4-bit quantizer: fp16 W[K][N] -> plain (q, z, s) arrays, or
+// straight into the packed layout. `bad` is set to nonzero when a weight is
+// not finite.
+hipError_t launch_quantize(const uint16_t *W, int K, int N, int G, uint8_t *q, uint8_t *z, uint16_t *s,
+                           int *bad, hipStream_t stream);
+hipError_t launch_quantize_pack(const uint16_t *W, int K, int N, int G, uint8_t *packed, int *bad,
+                                hipStream_t stream);
+
 // Decode path (M <= 64): one 16-column strip per workgroup, waves split K,
 // MFMA with M padded to 16; optional split of K across workgroups (narrow N)
 // with fp32 partials in a workspace and a second reduce kernel.
