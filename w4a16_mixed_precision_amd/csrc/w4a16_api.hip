@@ -57,7 +57,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
     std::mutex mu;
     int num_cus = 0;
-    int *flag = nullptr;       // pack range / quantizer finiteness error word
+    int *flag = nullptr;       // pack range / quantizer finiteness error word (pinned host memory)
     void *ws = nullptr;        // w4a16_gemm split-K workspace
     size_t ws_bytes = 0;
 };
@@ -84,14 +84,35 @@ int device_cus(int dev, int *cus) {
     return W4A16_OK;
 }
 
+// The status word of the synchronous offline calls (pack, quantize) lives in
+// pinned, device-mapped host memory: the host clears it before the launch and
+// reads it after the stream synchronization, so a call costs no fill kernel
+// and no device-to-host copy. Kernels only ever store 1 into it.
 int device_flag(int dev, int **flag) {
     DeviceState &d = g_dev[dev];
     std::lock_guard<std::mutex> lk(d.mu);
     if (!d.flag) {
-        hipError_t e = hipMalloc((void **)&d.flag, 256);
-        if (e != hipSuccess) return fail_hip(e, "hipMalloc(status word)");
+        hipError_t e = hipHostMalloc((void **)&d.flag, 256, hipHostMallocMapped | hipHostMallocCoherent);
+        if (e != hipSuccess) return fail_hip(e, "hipHostMalloc(status word)");
     }
     *flag = d.flag;
+    return W4A16_OK;
+}
+
+// Clears the status word, runs `launch_fn(flag)` on `st`, synchronizes `st`
+// and reports whether a kernel set the word.
+template <class Launch>
+int run_flagged(hipStream_t st, const char *what, Launch &&launch_fn, bool *raised) {
+    int dev, rc;
+    if ((rc = current_device(&dev))) return rc;
+    int *flag;
+    if ((rc = device_flag(dev, &flag))) return rc;
+    *(volatile int *)flag = 0;
+    hipError_t e = launch_fn(flag);
+    if (e != hipSuccess) return fail_hip(e, what);
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    *raised = *(volatile int *)flag != 0;
     return W4A16_OK;
 }
 
@@ -177,24 +198,13 @@ int launch(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t 
     return W4A16_OK;
 }
 
-// Runs one quantizer launch between clearing and reading the device's status
-// word; synchronizes `st`.
+// One quantizer launch with the finiteness status word; synchronizes `st`.
 template <class Launch>
 int run_quantizer(hipStream_t st, Launch &&launch_fn) {
-    int dev, rc;
-    if ((rc = current_device(&dev))) return rc;
-    int *flag;
-    if ((rc = device_flag(dev, &flag))) return rc;
-    hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
-    if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
-    e = launch_fn(flag);
-    if (e != hipSuccess) return fail_hip(e, "quantize launch");
-    int host_flag = 0;
-    e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st);
-    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
-    if (host_flag) return fail(W4A16_ERR_RANGE, "a weight is not finite (Inf or NaN)");
+    bool raised = false;
+    int rc = run_flagged(st, "quantize launch", launch_fn, &raised);
+    if (rc) return rc;
+    if (raised) return fail(W4A16_ERR_RANGE, "a weight is not finite (Inf or NaN)");
     g_last_error[0] = 0;
     return W4A16_OK;
 }
@@ -216,19 +226,11 @@ int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales, i
     if (rc) return rc;
     if (!aligned16(packed)) return fail(W4A16_ERR_ALIGN, "packed must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
-    int dev;
-    if ((rc = current_device(&dev))) return rc;
-    int *flag;
-    if ((rc = device_flag(dev, &flag))) return rc;
-    hipError_t e = hipMemsetAsync(flag, 0, sizeof(int), st);
-    if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
-    e = w4a16::launch_pack(q, zeros, scales, (int)K, (int)N, (int)G, (uint8_t *)packed, flag, st);
-    if (e != hipSuccess) return fail_hip(e, "pack launch");
-    int host_flag = 0;
-    e = hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st);
-    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync");
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    bool host_flag = false;
+    rc = run_flagged(st, "pack launch", [&](int *flag) {
+        return w4a16::launch_pack(q, zeros, scales, (int)K, (int)N, (int)G, (uint8_t *)packed, flag, st);
+    }, &host_flag);
+    if (rc) return rc;
     if (host_flag) return fail(W4A16_ERR_RANGE, "a q or zero code is larger than 15");
     g_last_error[0] = 0;
     return W4A16_OK;

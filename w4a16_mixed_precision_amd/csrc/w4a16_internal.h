@@ -8,16 +8,17 @@
 
 namespace w4a16 {
 
-// Offline relayout (pack) and its inverse (unpack). `bad` is a device int set
-// to nonzero by pack when a code is larger than 15.
+// Offline relayout (pack) and its inverse (unpack). `bad` is a
+// device-visible int (pinned host memory) that pack sets to 1 when a code is
+// larger than 15.
 hipError_t launch_pack(const uint8_t *q, const uint8_t *z, const uint16_t *s, int K, int N, int G,
                        uint8_t *packed, int *bad, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int G, uint8_t *q, uint8_t *z,
                          uint16_t *s, hipStream_t stream);
 
 // Group-wise 4-bit quantizer: fp16 W[K][N] -> plain (q, z, s) arrays, or
-// straight into the packed layout. `bad` is set to nonzero when a weight is
-// not finite.
+// straight into the packed layout. `bad` (as for pack) is set to 1 when a
+// weight is not finite.
 hipError_t launch_quantize(const uint16_t *W, int K, int N, int G, uint8_t *q, uint8_t *z, uint16_t *s,
                            int *bad, hipStream_t stream);
 hipError_t launch_quantize_pack(const uint16_t *W, int K, int N, int G, uint8_t *packed, int *bad,

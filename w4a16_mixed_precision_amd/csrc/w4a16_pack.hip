@@ -52,7 +52,7 @@ pack_weights_kernel(const uint8_t *__restrict__ q, int K, int N, u32x4 *__restri
             v[w] = word;
         }
         out[idx] = v;
-        if (over > 15u) atomicOr(bad, 1);
+        if (over > 15u) *bad = 1;
     }
 }
 
@@ -71,7 +71,7 @@ pack_scales_zeros_kernel(const uint8_t *__restrict__ z, const uint16_t *__restri
         const int g = (int)(rec % ngrp);
         const int n = strip * kStripCols + 2 * pr;
         const uint32_t z0 = z[(int64_t)g * N + n], z1 = z[(int64_t)g * N + n + 1];
-        if ((z0 | z1) > 15u) atomicOr(bad, 1);
+        if ((z0 | z1) > 15u) *bad = 1;
         zout[idx] = (uint8_t)((z0 & 15u) | ((z1 & 15u) << 4));
         sout[rec * 16 + 2 * pr] = s[(int64_t)g * N + n];
         sout[rec * 16 + 2 * pr + 1] = s[(int64_t)g * N + n + 1];
