@@ -15,6 +15,9 @@ Contents
 * ``quantize``: the group-wise asymmetric 4-bit quantizer that produces
   (q, z, s) from fp16 weights (``quantize.py``; its header states the
   reading of the pages it follows).
+* ``kvcache``: the low-bit KV cache (per-token, per-head asymmetric 8/4-bit
+  quantization, the blocked cache layout written out as index arithmetic)
+  and float64 decode attention over it (``kvcache.py``).
 * ``layout_pack`` / ``layout_unpack``: the packed weight format written out as
   plain index arithmetic, so the bytes the GPU packer writes can be checked
   one by one. The pages ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
@@ -49,11 +52,12 @@ import subprocess
 
 import numpy as np
 
+from . import kvcache
 from .quantize import quantize
 
 __all__ = [
     "lib_path", "build", "load", "half_to_double", "dequant", "gemm", "compare",
-    "packed_bytes", "layout_pack", "layout_unpack", "max_threads", "quantize",
+    "packed_bytes", "layout_pack", "layout_unpack", "max_threads", "quantize", "kvcache",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
