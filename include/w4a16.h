@@ -191,6 +191,75 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
                   int64_t G, uint16_t *Y, void *workspace, size_t workspace_bytes,
                   int path, int splits, void *stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Low-bit KV cache and decode attention (the pages' second pipeline:
+ * "LMDeploy Guide: Fast Mixed-Precision LLM Inference Engine", architecture
+ * figure, pipeline B, sections 2 "Adaptive Head Alignment" and 4
+ * "Asynchronous KV Memory Loading Pipeline"; "LMDeploy, in depth", the
+ * blocked KV cache (64 tokens per block) and KV cache quantization: online,
+ * asymmetric, per head and per token, 8 or 4 bits).
+ *
+ * Head dimension 128. Every key and value vector of one (token, KV head) is
+ * quantized on its own, with L = 2^bits - 1 steps over its range (the same
+ * reading as w4a16_quantize): s = fp16(max((max - min) / L, 2^-14)),
+ * z = clamp(rint(-min / s), 0, L), c = clamp(rint(x / s) + z, 0, L), the
+ * products with the float32 reciprocal of s exact and rounded once.
+ *
+ * Cache: an array of num_blocks blocks of w4a16_kv_block_bytes(bits,
+ * kv_heads) bytes; block b holds kv_heads regions, region (b, h) at byte
+ * (b * kv_heads + h) * (w4a16_kv_block_bytes / kv_heads). Inside a region,
+ * KC = 64 * 128 * bits / 8:
+ *   [0, KC)          K codes, token-major rows of 128 codes
+ *   [KC, 2 KC)       V codes, rows d = 0..127 of the 64 tokens at positions
+ *                    p(t) = 16 ((t % 16) / 4) + 8 (t / 32) + 4 ((t / 16) % 2) + t % 4
+ *   [2 KC, +256)     K parameters, 4 bytes per token: fp16 scale, zero, 0
+ *   [2 KC + 256, +256) V parameters
+ * 4-bit codes are two per byte, the even index in the low nibble. Token i of
+ * a sequence lives in block block_table[b][i / 64] at offset i % 64.
+ * ---------------------------------------------------------------------------
+ */
+
+/* Bytes of one cache block for kv_heads heads; 0 if bits is not 4 or 8. */
+size_t w4a16_kv_block_bytes(int bits, int64_t kv_heads);
+
+/*
+ * Quantize and store new tokens:
+ *   k, v    fp16 [ntok][kv_heads][128]
+ *   slots   int32 [ntok], block * 64 + offset of each token; a negative
+ *           slot, or one past num_blocks blocks, skips that token
+ *   cache   the cache (num_blocks blocks)
+ * Asynchronous on `stream`. Tokens of one call may share cache blocks;
+ * two tokens of one call must not share a slot. Non-finite inputs give
+ * unspecified codes.
+ */
+int w4a16_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int64_t ntok,
+                    int64_t kv_heads, int bits, void *cache, int64_t num_blocks, void *stream);
+
+/* Workspace bytes of w4a16_kv_attention for this batch (depends on the
+ * current device's CU count; 0 for an invalid shape). */
+size_t w4a16_kv_attention_workspace_bytes(int64_t B, int64_t kv_heads, int64_t max_blocks);
+
+/*
+ * Decode attention of one new query token per sequence:
+ *   out[b][h] = softmax(sm_scale * q[b][h] . K_b^T) . V_b
+ * over the lengths[b] tokens of sequence b, with K and V dequantized as
+ * (c - z) * s and query head h reading KV head h / (q_heads / kv_heads).
+ *   q, out       fp16 [B][q_heads][128]
+ *   block_table  int32 [B][max_blocks]; entries outside [0, num_blocks) are
+ *                read as empty blocks
+ *   lengths      int32 [B]; a length <= 0 gives zeros, one above
+ *                max_blocks * 64 is clamped
+ *   workspace    at least w4a16_kv_attention_workspace_bytes(B, kv_heads,
+ *                max_blocks) bytes of device memory (any contents)
+ * q_heads must be a multiple of kv_heads, at most 16 query heads per KV
+ * head. Asynchronous on `stream`; calls sharing a workspace must be ordered.
+ */
+int w4a16_kv_attention(const uint16_t *q, const void *cache, int64_t num_blocks,
+                       const int32_t *block_table, int64_t max_blocks, const int32_t *lengths,
+                       int64_t B, int64_t q_heads, int64_t kv_heads, int bits, float sm_scale,
+                       uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *w4a16_status_string(int status);
 

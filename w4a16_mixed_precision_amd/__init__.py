@@ -21,6 +21,7 @@ __all__ = [
     "w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
     "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack",
+    "w4a16_kv_block_bytes", "w4a16_kv_append", "w4a16_kv_attention_workspace_bytes", "w4a16_kv_attention",
 ]
 
 W4A16_OK = 0
@@ -78,6 +79,14 @@ def lib():
     L.w4a16_quantize.restype = I
     L.w4a16_quantize_pack.argtypes = [P, I64, I64, I64, P, P]
     L.w4a16_quantize_pack.restype = I
+    L.w4a16_kv_block_bytes.argtypes = [I, I64]
+    L.w4a16_kv_block_bytes.restype = SZ
+    L.w4a16_kv_append.argtypes = [P, P, P, I64, I64, I, P, I64, P]
+    L.w4a16_kv_append.restype = I
+    L.w4a16_kv_attention_workspace_bytes.argtypes = [I64, I64, I64]
+    L.w4a16_kv_attention_workspace_bytes.restype = SZ
+    L.w4a16_kv_attention.argtypes = [P, P, I64, P, I64, P, I64, I64, I64, I, ctypes.c_float, P, P, SZ, P]
+    L.w4a16_kv_attention.restype = I
     L.w4a16_auto_path.restype = I
     _lib = L
     return L
@@ -185,6 +194,51 @@ def w4a16_quantize_pack(W, G: int, packed=None, stream=None):
     _check(lib().w4a16_quantize_pack(_dev_ptr(W, torch.float16, "W"), K, N, G,
                                      _dev_ptr(packed, torch.uint8, "packed"), _stream(stream, W.device)))
     return packed
+
+
+def w4a16_kv_block_bytes(bits: int, kv_heads: int) -> int:
+    return int(lib().w4a16_kv_block_bytes(bits, kv_heads))
+
+
+def w4a16_kv_append(k, v, slots, bits: int, cache, stream=None):
+    """Quantize fp16 k, v [ntok][kv_heads][128] (device) into the cache
+    (uint8 device tensor of whole blocks) at int32 `slots` [ntok]. Asynchronous."""
+    import torch
+    ntok, hkv, d = k.shape
+    if d != 128 or tuple(v.shape) != tuple(k.shape) or slots.numel() != ntok:
+        raise ValueError("k and v must be [ntok][kv_heads][128], slots [ntok]")
+    nb = cache.numel() // max(w4a16_kv_block_bytes(bits, hkv), 1)
+    _check(lib().w4a16_kv_append(_dev_ptr(k, torch.float16, "k"), _dev_ptr(v, torch.float16, "v"),
+                                 _dev_ptr(slots, torch.int32, "slots"), ntok, hkv, bits,
+                                 _dev_ptr(cache, torch.uint8, "cache"), nb, _stream(stream, k.device)))
+
+
+def w4a16_kv_attention_workspace_bytes(B: int, kv_heads: int, max_blocks: int) -> int:
+    return int(lib().w4a16_kv_attention_workspace_bytes(B, kv_heads, max_blocks))
+
+
+def w4a16_kv_attention(q, cache, block_table, lengths, bits: int, kv_heads: int, sm_scale: float,
+                       out=None, workspace=None, stream=None):
+    """fp16 out [B][q_heads][128] = softmax(sm_scale q K^T) V over each
+    sequence's cached tokens. Asynchronous."""
+    import torch
+    B, hq, d = q.shape
+    max_blocks = block_table.shape[1]
+    if d != 128 or tuple(block_table.shape) != (B, max_blocks) or lengths.numel() != B:
+        raise ValueError("q must be [B][q_heads][128], block_table [B][max_blocks], lengths [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    need = w4a16_kv_attention_workspace_bytes(B, kv_heads, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nb = cache.numel() // max(w4a16_kv_block_bytes(bits, kv_heads), 1)
+    _check(lib().w4a16_kv_attention(_dev_ptr(q, torch.float16, "q"), _dev_ptr(cache, torch.uint8, "cache"), nb,
+                                    _dev_ptr(block_table, torch.int32, "block_table"), max_blocks,
+                                    _dev_ptr(lengths, torch.int32, "lengths"), B, hq, kv_heads, bits,
+                                    float(sm_scale), _dev_ptr(out, torch.float16, "out"),
+                                    _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                    _stream(stream, q.device)))
+    return out
 
 
 def w4a16_unpack(packed, K: int, N: int, G: int, stream=None):

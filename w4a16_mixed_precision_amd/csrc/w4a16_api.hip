@@ -278,6 +278,70 @@ int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G, uint8_t *q
     return W4A16_OK;
 }
 
+size_t w4a16_kv_block_bytes(int bits, int64_t kv_heads) {
+    if ((bits != 4 && bits != 8) || kv_heads < 1 || kv_heads > 65535) return 0;
+    return (size_t)kv_heads * w4a16::kv_region_bytes(bits);
+}
+
+int w4a16_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int64_t ntok, int64_t kv_heads,
+                    int bits, void *cache, int64_t num_blocks, void *stream) {
+    if (!k || !v || !slots || !cache) return fail(W4A16_ERR_NULL, "k, v, slots and cache must be non-NULL");
+    if (bits != 4 && bits != 8) return fail(W4A16_ERR_ARG, "bits must be 4 or 8 (got %d)", bits);
+    if (ntok < 0 || ntok > kMaxDim || kv_heads < 1 || kv_heads > 65535 || num_blocks < 1)
+        return fail(W4A16_ERR_SHAPE, "bad KV append shape ntok=%lld kv_heads=%lld num_blocks=%lld", (long long)ntok,
+                    (long long)kv_heads, (long long)num_blocks);
+    if (!aligned16(k) || !aligned16(v) || !aligned16(slots) || !aligned16(cache))
+        return fail(W4A16_ERR_ALIGN, "k, v, slots and cache must be 16-byte aligned");
+    hipError_t e = w4a16::launch_kv_append(k, v, slots, (int)ntok, (int)kv_heads, bits, num_blocks, (uint8_t *)cache,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "KV append launch");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
+size_t w4a16_kv_attention_workspace_bytes(int64_t B, int64_t kv_heads, int64_t max_blocks) {
+    if (B < 1 || B > kMaxDim || kv_heads < 1 || kv_heads > 65535 || max_blocks < 1 || max_blocks > kMaxDim) return 0;
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        int v = 0;
+        if (device_cus(dev, &v) == W4A16_OK) cus = v;
+    }
+    return w4a16::kv_workspace_bytes((int)B, (int)kv_heads, (int)max_blocks, cus);
+}
+
+int w4a16_kv_attention(const uint16_t *q, const void *cache, int64_t num_blocks, const int32_t *block_table,
+                       int64_t max_blocks, const int32_t *lengths, int64_t B, int64_t q_heads, int64_t kv_heads,
+                       int bits, float sm_scale, uint16_t *out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    if (!q || !cache || !block_table || !lengths || !out)
+        return fail(W4A16_ERR_NULL, "q, cache, block_table, lengths and out must be non-NULL");
+    if (bits != 4 && bits != 8) return fail(W4A16_ERR_ARG, "bits must be 4 or 8 (got %d)", bits);
+    if (B < 1 || B > kMaxDim || kv_heads < 1 || kv_heads > 65535 || q_heads < kv_heads ||
+        q_heads % kv_heads != 0 || q_heads / kv_heads > 16 || max_blocks < 1 || max_blocks > kMaxDim ||
+        num_blocks < 1 || B * q_heads > kMaxDim)
+        return fail(W4A16_ERR_SHAPE,
+                    "bad KV attention shape B=%lld q_heads=%lld kv_heads=%lld max_blocks=%lld num_blocks=%lld "
+                    "(need q_heads a multiple of kv_heads, at most 16 query heads per KV head)",
+                    (long long)B, (long long)q_heads, (long long)kv_heads, (long long)max_blocks,
+                    (long long)num_blocks);
+    if (!aligned16(q) || !aligned16(cache) || !aligned16(out) || !aligned16(block_table) || !aligned16(lengths))
+        return fail(W4A16_ERR_ALIGN, "q, cache, block_table, lengths and out must be 16-byte aligned");
+    int dev, rc, cus;
+    if ((rc = current_device(&dev))) return rc;
+    if ((rc = device_cus(dev, &cus))) return rc;
+    const size_t need = w4a16::kv_workspace_bytes((int)B, (int)kv_heads, (int)max_blocks, cus);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4A16_ERR_WORKSPACE, "KV attention needs a workspace of %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+    hipError_t e = w4a16::launch_kv_attention(q, (const uint8_t *)cache, block_table, (int)max_blocks, lengths,
+                                              (int)B, (int)q_heads, (int)kv_heads, bits, num_blocks, sm_scale, out,
+                                              workspace, cus, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "KV attention launch");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits) {
     if (M < 1 || M > kMaxDim || !shape_ok(K, N, G)) return 0;
     // The plan depends on the device's CU count; size for the current device

@@ -24,6 +24,20 @@ hipError_t launch_quantize(const uint16_t *W, int K, int N, int G, uint8_t *q, u
 hipError_t launch_quantize_pack(const uint16_t *W, int K, int N, int G, uint8_t *packed, int *bad,
                                 hipStream_t stream);
 
+// Low-bit KV cache (8 or 4 bits, blocks of 64 tokens, head dimension 128)
+// and decode attention over it.
+size_t kv_region_bytes(int bits);  // one (block, KV head) region
+struct KvPlan {
+    int chunk_blocks, nchunks;
+};
+KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus);
+size_t kv_workspace_bytes(int B, int Hkv, int max_blocks, int num_cus);
+hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int ntok, int Hkv, int bits,
+                            int64_t num_blocks, uint8_t *cache, hipStream_t stream);
+hipError_t launch_kv_attention(const uint16_t *q, const uint8_t *cache, const int32_t *block_table, int max_blocks,
+                               const int32_t *lengths, int B, int Hq, int Hkv, int bits, int64_t num_blocks,
+                               float sm_scale, uint16_t *out, void *workspace, int num_cus, hipStream_t stream);
+
 // Decode path (M <= 64): one 16-column strip per workgroup, waves split K,
 // MFMA with M padded to 16; optional split of K across workgroups (narrow N)
 // with fp32 partials in a workspace and a second reduce kernel.

@@ -1,0 +1,469 @@
+// Low-bit KV cache and decode attention (the pages' second pipeline).
+//
+// KV quantization is online, asymmetric, per head and per token, 8 or 4 bits
+// ("LMDeploy, in depth", "Quantization: AWQ weights and KV cache", paragraph
+// on KV cache quantization); the cache is blocked, 64 tokens per block (same
+// page, section on the blocked KV cache). Attention of one new query token
+// per sequence reads the low-bit K and V straight from the cache
+// ("LMDeploy Guide: Fast Mixed-Precision LLM Inference Engine", architecture
+// figure, pipeline B; sections 2 "Adaptive Head Alignment" and 4
+// "Asynchronous KV Memory Loading Pipeline").
+//
+// Scale and zero of a vector x of D = 128 numbers (L = 2^bits - 1 steps),
+// the reading the weight quantizer uses:
+//   s = fp16(max(fp32(max - min) / L, 2^-14)), inv = fp32(1 / s),
+//   z = clamp(rint(-min * inv), 0, L), c = clamp(rint(x * inv) + z, 0, L)
+// with exact products rounded once (ties to even).
+//
+// Cache region of one (block, KV head), KC = 64 * 128 * bits / 8 bytes:
+//   [0, KC)        K codes, token-major rows of 128 codes
+//   [KC, 2 KC)     V codes, rows d = 0..127 of 64 tokens in position order
+//                  p(t) = 16 ((t % 16) / 4) + 8 (t / 32) + 4 ((t / 16) % 2) + t % 4
+//   [2 KC, +256)   K parameters per token: fp16 scale, zero code, 0
+//   [2 KC + 256, +256) V parameters per token
+// (4-bit codes two per byte, the even index in the low nibble.)
+//
+// Decode attention on gfx950, one wave per (sequence, KV head, chunk of
+// blocks):
+// * S^T = K . Q^T on the matrix cores (16 x 16 x 32 fp16 MFMA): rows are 16
+//   tokens, columns up to 16 query heads of the KV head's group. A lane's A
+//   operand is one token's codes, 32 contiguous dimensions per lane (16 or
+//   32 bytes): the dimension order inside the reduction is permuted so that
+//   every lane reads contiguous codes, and the query is permuted the same way
+//   once per wave (the pages' adaptive head alignment, "Q rearranged once so
+//   its K-slices match the low-bit key layout"). The codes become fp16 by
+//   exponent-OR (1024 + c), the zero is subtracted exactly, and the token's
+//   scale (times the softmax scale and log2 e) multiplies the score row.
+// * Online softmax in fp32 per head (exp2).
+// * O^T = V^T . P^T on the matrix cores: the V rows are stored index-major in
+//   the position order above, which puts in each lane exactly the eight
+//   tokens whose probabilities that lane already holds after the score
+//   product, so P needs no data movement; V's per-token scale is folded into
+//   P and its zero subtracted exactly from the codes.
+// * The loads of the next cache block are issued before the current one is
+//   multiplied (two register sets), the pages' double-buffered KV pipeline.
+// * Each wave writes a partial (max, sum, unnormalized O) per head; a second
+//   kernel merges the chunks of a sequence (log-sum-exp).
+#include "w4a16_device.h"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+constexpr int kHD = 128;    // head dimension
+constexpr int kBS = 64;     // tokens per cache block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRoundMagic = 12582912.0f;         // 1.5 * 2^23
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+constexpr float kScaleFloor = 6.103515625e-05f;    // 2^-14
+
+template <int BITS>
+struct KvGeom {
+    static constexpr int kCodeBytes = kBS * kHD * BITS / 8;  // K (or V) codes of one region
+    static constexpr int kRowBytes = kHD * BITS / 8;         // one K row
+    static constexpr int kVRowBytes = kBS * BITS / 8;        // one V row (64 positions)
+    static constexpr int kKPar = 2 * kCodeBytes;
+    static constexpr int kVPar = 2 * kCodeBytes + 4 * kBS;
+    static constexpr int kRegion = 2 * kCodeBytes + 8 * kBS;
+};
+
+__device__ inline int v_position(int t) { return 16 * ((t & 15) >> 2) + 8 * (t >> 5) + 4 * ((t >> 4) & 1) + (t & 3); }
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ inline float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ------------------------------------------------------------------ append
+// One wave per (token, KV head): lane l owns dimensions 2l and 2l + 1 of the
+// key and of the value. Tokens with a negative slot, or a slot past the
+// cache, are skipped.
+template <int BITS>
+__global__ void __launch_bounds__(64)
+kv_append_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int32_t *__restrict__ slots,
+                 int Hkv, int64_t num_blocks, uint8_t *__restrict__ cache) {
+    typedef KvGeom<BITS> Geo;
+    constexpr int L = (1 << BITS) - 1;
+    const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    const int slot = slots[i];
+    if (slot < 0 || slot / kBS >= num_blocks) return;
+    const int blk = slot / kBS, t = slot % kBS;
+    uint8_t *region = cache + ((size_t)blk * Hkv + h) * Geo::kRegion;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const uint16_t *src = (which ? v : k) + ((size_t)i * Hkv + h) * kHD;
+        const uint32_t pair = *reinterpret_cast<const uint32_t *>(src + 2 * lane);
+        const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFF));
+        const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+        const float xmax = wave_max(__builtin_fmaxf(x0, x1));
+        const float xmin = wave_min(__builtin_fminf(x0, x1));
+        const float s32 = __builtin_fmaxf((xmax - xmin) / (float)L, kScaleFloor);
+        const _Float16 s16 = (_Float16)s32;
+        const float inv = 1.0f / (float)s16;
+        const double zr = __builtin_rint(-(double)xmin * (double)inv);  // exact product
+        const int z = zr < 0.0 ? 0 : (zr > (double)L ? L : (int)zr);
+        const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
+        const float y0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0, inv, kRoundMagic), lo, hi);
+        const float y1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1, inv, kRoundMagic), lo, hi);
+        const uint32_t c0 = __builtin_bit_cast(uint32_t, y0) - kRoundMagicBits + z;
+        const uint32_t c1 = __builtin_bit_cast(uint32_t, y1) - kRoundMagicBits + z;
+        if (which == 0) {
+            uint8_t *row = region + t * Geo::kRowBytes;
+            if constexpr (BITS == 8)
+                *reinterpret_cast<uint16_t *>(row + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+            else
+                row[lane] = (uint8_t)(c0 | (c1 << 4));
+        } else {
+            uint8_t *vrows = region + Geo::kCodeBytes;
+            const int p = v_position(t);
+            if constexpr (BITS == 8) {
+                vrows[(2 * lane) * kBS + p] = (uint8_t)c0;
+                vrows[(2 * lane + 1) * kBS + p] = (uint8_t)c1;
+            } else {
+                // two tokens share a byte: update this token's nibble of the
+                // containing word with atomics (other tokens of the same call
+                // may update the other nibble)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int byte = (2 * lane + e) * Geo::kVRowBytes + p / 2;
+                    uint32_t *word = reinterpret_cast<uint32_t *>(vrows + (byte & ~3));
+                    const uint32_t sh = 8 * (byte & 3) + 4 * (p & 1);
+                    atomicAnd(word, ~(15u << sh));
+                    atomicOr(word, (e ? c1 : c0) << sh);
+                }
+            }
+        }
+        if (lane == 0) {
+            const uint32_t par = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)z << 16);
+            *reinterpret_cast<uint32_t *>(region + (which ? Geo::kVPar : Geo::kKPar) + 4 * t) = par;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ attention
+// Registers of one cache block for one wave.
+template <int BITS>
+struct KvBlock {
+    u32x4 kc[4][BITS == 8 ? 2 : 1];  // K codes of token tile tt, 32 dims per lane
+    uint32_t kz[4];                  // K parameters of the lane's own token per tile
+    u32x4 kp[4];                     // K parameters of tokens 16 tt + 4 kq + 0..3
+    u32x4 vp[4];                     // V parameters of the same tokens
+    uint32_t vc[2][8][BITS == 8 ? 2 : 1];  // V codes: half, d tile, 8 positions
+    bool valid;                            // the table entry names a cache block
+};
+
+// fp16 pair (1024 + b0, 1024 + b1) of two bytes of w (8-bit codes)
+__device__ inline uint32_t bytes_to_h2(uint32_t w, int first) {
+    const uint32_t b0 = (w >> (8 * first)) & 0xFFu, b1 = (w >> (8 * first + 8)) & 0xFFu;
+    return b0 | (b1 << 16) | 0x64006400u;
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(256)
+kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
+                    const int32_t *__restrict__ block_table, int max_blocks, const int32_t *__restrict__ lengths,
+                    int B, int Hq, int Hkv, int64_t num_blocks, float score_scale, int chunk_blocks, int nchunks,
+                    float *__restrict__ part_o, float2 *__restrict__ part_ml) {
+    typedef KvGeom<BITS> Geo;
+    typedef KvBlock<BITS> Blk;
+    const int lane = threadIdx.x & 63;
+    const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int units = B * Hkv * nchunks;
+    if (unit >= units) return;  // uniform per wave; no block-wide barrier below
+    const int chunk = unit % nchunks;
+    const int kh = (unit / nchunks) % Hkv;
+    const int b = unit / (nchunks * Hkv);
+    const int g = Hq / Hkv;
+    const int c = lane & 15, kq = lane >> 4;
+    int len = lengths[b];
+    if (len > max_blocks * kBS) len = max_blocks * kBS;
+    const int nblk = len > 0 ? (len + kBS - 1) / kBS : 0;
+    const int b0 = chunk * chunk_blocks;
+    const int b1 = b0 + chunk_blocks < nblk ? b0 + chunk_blocks : nblk;
+
+    // query of head kh * g + c in the key's dimension order (B operand of
+    // S^T = K . Q^T): step s, slot j of lane group kq holds dimension
+    // 32 kq + 8 s + j (8-bit keys) or 32 kq + 8 s + sigma(j) with
+    // sigma = 0 4 1 5 2 6 3 7 (4-bit keys, whose nibble extraction yields
+    // that order)
+    half8 qf[4];
+    {
+        const bool ok = c < g;
+        const uint16_t *qh = q + ((size_t)b * Hq + kh * g + (ok ? c : 0)) * kHD + 32 * kq;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const half8 raw = ok ? *reinterpret_cast<const half8 *>(qh + 8 * s) : half8{};
+            if constexpr (BITS == 8) {
+                qf[s] = raw;
+            } else {
+                half8 p;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[2 * j] = raw[j];
+                    p[2 * j + 1] = raw[j + 4];
+                }
+                qf[s] = p;
+            }
+        }
+    }
+
+    auto region_of = [&](int bi) -> int64_t {
+        int id = block_table[(size_t)b * max_blocks + bi];
+        if (id < 0 || id >= num_blocks) id = -1;
+        return id < 0 ? -1 : ((int64_t)id * Hkv + kh) * Geo::kRegion;
+    };
+    auto load = [&](int bi, Blk &B_) {
+        const int64_t reg = region_of(bi);
+        B_.valid = reg >= 0;
+        const uint8_t *base = cache + (reg < 0 ? 0 : reg);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base, reg < 0 ? 0u : (uint32_t)Geo::kRegion);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int tok = 16 * tt + c;
+#pragma unroll
+            for (int u = 0; u < (BITS == 8 ? 2 : 1); ++u)
+                B_.kc[tt][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              r, (uint32_t)(tok * Geo::kRowBytes + (32 * kq) * BITS / 8 + 16 * u), 0, 0));
+            B_.kz[tt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(Geo::kKPar + 4 * tok), 0, 0);
+            const int t4 = 16 * tt + 4 * kq;
+            B_.kp[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kKPar + 4 * t4), 0, 0));
+            B_.vp[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kVPar + 4 * t4), 0, 0));
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const uint32_t off = (uint32_t)(Geo::kCodeBytes + (16 * dt + c) * Geo::kVRowBytes + (16 * kq + 8 * hf) * BITS / 8);
+                if constexpr (BITS == 8) {
+                    const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+                    B_.vc[hf][dt][0] = (uint32_t)w2[0];
+                    B_.vc[hf][dt][1] = (uint32_t)w2[1];
+                } else {
+                    B_.vc[hf][dt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+                }
+            }
+    };
+
+    floatx4 o[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -__builtin_inff(), l_run = 0.f;
+
+    auto compute = [&](int bi, const Blk &B_) {
+        const int tok0 = bi * kBS;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if (tok0 + 32 * hf >= len || !B_.valid) break;  // uniform
+            // ---- scores of tokens 32 hf .. +31 (two 16-token tiles)
+            float x[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tt = 2 * hf + u;
+                const uint32_t zc = B_.kz[tt] >> 16 & 0xFFu;
+                const uint32_t nb = (0xE400u | zc) * 0x10001u;  // -(1024 + z) pair (8-bit: z up to 255)
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    half8 a;
+                    if constexpr (BITS == 8) {
+                        const u32x4 &w = B_.kc[tt][s >> 1];
+                        const uint32_t w0 = w[2 * (s & 1)], w1 = w[2 * (s & 1) + 1];
+                        a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(nb), as_h2(bytes_to_h2(w0, 2)) + as_h2(nb),
+                                    as_h2(bytes_to_h2(w1, 0)) + as_h2(nb), as_h2(bytes_to_h2(w1, 2)) + as_h2(nb));
+                    } else {
+                        const uint32_t w = B_.kc[tt][0][s];
+                        a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)) + as_h2(nb),
+                                    as_h2(and_or(w >> 4, kLoMask, kMagic)) + as_h2(nb),
+                                    as_h2(and_or(w >> 8, kLoMask, kMagic)) + as_h2(nb),
+                                    as_h2(and_or(w >> 12, kLoMask, kMagic)) + as_h2(nb));
+                    }
+                    acc = mfma16x16x32(a, qf[s], acc);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = tok0 + 16 * tt + 4 * kq + e;
+                    const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)(B_.kp[tt][e] & 0xFFFFu));
+                    const float sc = acc[e] * (ks * score_scale);
+                    x[u][e] = tok < len && B_.valid ? sc : -__builtin_inff();
+                }
+            }
+            // ---- online softmax for head c (the four kq lane groups hold
+            // different tokens of the same head)
+            float mt = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(x[0][0], x[0][1]), __builtin_fmaxf(x[0][2], x[0][3])),
+                                       __builtin_fmaxf(__builtin_fmaxf(x[1][0], x[1][1]), __builtin_fmaxf(x[1][2], x[1][3])));
+            mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float m_new = __builtin_fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            float p[2][4];
+            float psum = 0.f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[u][e] = __builtin_amdgcn_exp2f(x[u][e] - m_new);
+                    psum += p[u][e];
+                }
+            l_run = l_run * alpha + psum;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[dt][e] *= alpha;
+            // ---- B operand P^T for O^T = V^T . P^T: slot j holds token
+            // 32 hf + 4 kq + j (j < 4) or 32 hf + 16 + 4 kq + j - 4, times
+            // its V scale; masked tokens contribute exactly zero
+            half8 pb;
+            uint32_t vzn[4];  // -(1024 + z) pairs of the slot pairs
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t par = B_.vp[2 * hf + u][e];
+                    const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(par & 0xFFFFu));
+                    const float pv = x[u][e] == -__builtin_inff() ? 0.f : p[u][e] * vs;
+                    const int j = 4 * u + e;
+                    // 4-bit V: the nibble extraction yields slots 0 4 1 5 2 6 3 7
+                    const int slot = BITS == 8 ? j : (j < 4 ? 2 * j : 2 * (j - 4) + 1);
+                    pb[slot] = (_Float16)pv;
+                }
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+                // slot pair (2 pr, 2 pr + 1): 8-bit tokens j = 2 pr, 2 pr + 1;
+                // 4-bit tokens j = pr, pr + 4
+                const int ja = BITS == 8 ? 2 * pr : pr, jb = BITS == 8 ? 2 * pr + 1 : pr + 4;
+                const uint32_t za = B_.vp[2 * hf + ja / 4][ja % 4] >> 16 & 0xFFu;
+                const uint32_t zb = B_.vp[2 * hf + jb / 4][jb % 4] >> 16 & 0xFFu;
+                vzn[pr] = (0xE400u | za) | ((0xE400u | zb) << 16);
+            }
+            // ---- O^T += V^T . P^T over the 8 tiles of 16 dimensions
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                half8 a;
+                if constexpr (BITS == 8) {
+                    const uint32_t w0 = B_.vc[hf][dt][0], w1 = B_.vc[hf][dt][1];
+                    a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(vzn[0]), as_h2(bytes_to_h2(w0, 2)) + as_h2(vzn[1]),
+                                as_h2(bytes_to_h2(w1, 0)) + as_h2(vzn[2]), as_h2(bytes_to_h2(w1, 2)) + as_h2(vzn[3]));
+                } else {
+                    const uint32_t w = B_.vc[hf][dt][0];
+                    a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)) + as_h2(vzn[0]),
+                                as_h2(and_or(w >> 4, kLoMask, kMagic)) + as_h2(vzn[1]),
+                                as_h2(and_or(w >> 8, kLoMask, kMagic)) + as_h2(vzn[2]),
+                                as_h2(and_or(w >> 12, kLoMask, kMagic)) + as_h2(vzn[3]));
+                }
+                o[dt] = mfma16x16x32(a, pb, o[dt]);
+            }
+        }
+    };
+
+    if (b0 < b1) {
+        Blk bufA, bufB;
+        load(b0, bufA);
+        int bi = b0;
+        for (; bi + 1 < b1; bi += 2) {
+            load(bi + 1, bufB);
+            compute(bi, bufA);
+            if (bi + 2 < b1) load(bi + 2, bufA);
+            compute(bi + 1, bufB);
+        }
+        if (bi < b1) compute(bi, bufA);
+    }
+
+    // ---- partial results of this chunk: (max, sum) and unnormalized O^T
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (c < g) {
+        if (kq == 0) part_ml[(size_t)unit * 16 + c] = float2{m_run, l_run};
+        float *po = part_o + ((size_t)unit * 16 + c) * kHD;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<floatx4 *>(po + 16 * dt + 4 * kq) = o[dt];
+    }
+}
+
+// O[b][h] = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i over the chunks of
+// (b, h / g); one workgroup of 128 threads per (b, h), thread = dimension.
+__global__ void __launch_bounds__(128)
+kv_combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml, int Hq, int Hkv,
+                  int nchunks, uint16_t *__restrict__ out) {
+    const int bh = blockIdx.x, d = threadIdx.x;
+    const int b = bh / Hq, h = bh % Hq, g = Hq / Hkv;
+    const int kh = h / g, c = h % g;
+    const size_t u0 = ((size_t)b * Hkv + kh) * nchunks;
+    float M = -__builtin_inff();
+    for (int i = 0; i < nchunks; ++i) M = __builtin_fmaxf(M, part_ml[(u0 + i) * 16 + c].x);
+    float num = 0.f, den = 0.f;
+    if (M != -__builtin_inff()) {
+        for (int i = 0; i < nchunks; ++i) {
+            const float2 ml = part_ml[(u0 + i) * 16 + c];
+            if (ml.x == -__builtin_inff()) continue;
+            const float w = __builtin_amdgcn_exp2f(ml.x - M);
+            num += w * part_o[((u0 + i) * 16 + c) * kHD + d];
+            den += w * ml.y;
+        }
+    }
+    out[(size_t)bh * kHD + d] = f32_to_f16_bits(den > 0.f ? num / den : 0.f);
+}
+
+}  // namespace
+
+size_t kv_region_bytes(int bits) { return bits == 8 ? KvGeom<8>::kRegion : KvGeom<4>::kRegion; }
+
+hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int ntok, int Hkv, int bits,
+                            int64_t num_blocks, uint8_t *cache, hipStream_t stream) {
+    if (ntok == 0) return hipSuccess;
+    const dim3 grid((unsigned)ntok, (unsigned)Hkv);
+    if (bits == 8)
+        hipLaunchKernelGGL(kv_append_kernel<8>, grid, dim3(64), 0, stream, k, v, slots, Hkv, num_blocks, cache);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(64), 0, stream, k, v, slots, Hkv, num_blocks, cache);
+    return hipGetLastError();
+}
+
+KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus) {
+    KvPlan p;
+    // enough waves for eight per CU; chunks of whole blocks
+    const long pairs = (long)B * Hkv;
+    const long want = (long)num_cus * 8;
+    int nchunks = (int)((want + pairs - 1) / pairs);
+    if (nchunks > max_blocks) nchunks = max_blocks;
+    if (nchunks < 1) nchunks = 1;
+    p.chunk_blocks = (max_blocks + nchunks - 1) / nchunks;
+    p.nchunks = (max_blocks + p.chunk_blocks - 1) / p.chunk_blocks;
+    return p;
+}
+
+size_t kv_workspace_bytes(int B, int Hkv, int max_blocks, int num_cus) {
+    const KvPlan p = kv_plan(B, Hkv, max_blocks, num_cus);
+    const size_t units = (size_t)B * Hkv * p.nchunks;
+    return units * 16 * kHD * sizeof(float) + units * 16 * sizeof(float2);
+}
+
+hipError_t launch_kv_attention(const uint16_t *q, const uint8_t *cache, const int32_t *block_table, int max_blocks,
+                               const int32_t *lengths, int B, int Hq, int Hkv, int bits, int64_t num_blocks,
+                               float sm_scale, uint16_t *out, void *workspace, int num_cus, hipStream_t stream) {
+    const KvPlan p = kv_plan(B, Hkv, max_blocks, num_cus);
+    const size_t units = (size_t)B * Hkv * p.nchunks;
+    float *part_o = static_cast<float *>(workspace);
+    float2 *part_ml = reinterpret_cast<float2 *>(part_o + units * 16 * kHD);
+    const unsigned wgs = (unsigned)((units + 3) / 4);
+    const float score_scale = sm_scale * kLog2e;
+    if (bits == 8)
+        hipLaunchKernelGGL(kv_attention_kernel<8>, dim3(wgs), dim3(256), 0, stream, q, cache, block_table, max_blocks,
+                           lengths, B, Hq, Hkv, num_blocks, score_scale, p.chunk_blocks, p.nchunks, part_o, part_ml);
+    else
+        hipLaunchKernelGGL(kv_attention_kernel<4>, dim3(wgs), dim3(256), 0, stream, q, cache, block_table, max_blocks,
+                           lengths, B, Hq, Hkv, num_blocks, score_scale, p.chunk_blocks, p.nchunks, part_o, part_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kv_combine_kernel, dim3((unsigned)(B * Hq)), dim3(kHD), 0, stream, part_o, part_ml, Hq, Hkv,
+                       p.nchunks, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16
