@@ -66,6 +66,8 @@ def parse_args(argv=None):
     p.add_argument("--detail", action="store_true", help="per-instance lines to stderr")
     p.add_argument("--quantizer-only", action="store_true",
                    help="time only the offline quantizer (fp16 W -> packed) and print its line")
+    p.add_argument("--kv-only", action="store_true",
+                   help="time only the low-bit KV cache decode attention (int8 and int4) and print its lines")
     return p.parse_args(argv)
 
 
@@ -301,6 +303,68 @@ def run_quantize_secondary(args, calls=20):
     }
 
 
+def run_kv_secondary(args, bits, reps=20):
+    """Decode attention over the low-bit KV cache: 50 sequences of 4000
+    tokens, 32 query heads over 8 KV heads, head dimension 128 (the
+    Llama-3-8B decode batch the pages size for an int8 cache). Algorithmic
+    bytes = the K and V codes and per-token parameters of every cached token
+    plus q and out. Copies of the cache are rotated so that every call reads
+    from HBM; HIP events around `reps` rounds of eager calls."""
+    import math
+
+    import torch
+
+    import w4a16_mixed_precision_amd as w4
+    B, T, hq, hkv, D = 50, 4000, 32, 8, 128
+    nblk = (T + 63) // 64
+    bb = w4.w4a16_kv_block_bytes(bits, hkv)
+    cache_bytes = B * nblk * bb
+    copies = max(1, int(math.ceil(args.rotate_gib * 2 ** 30 / cache_bytes)))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(bits)
+    table = torch.arange(B * nblk, dtype=torch.int32, device="cuda").reshape(B, nblk)
+    slots = (table[:, :, None] * 64 + torch.arange(64, dtype=torch.int32, device="cuda")).reshape(B, -1)[:, :T]
+    slots = slots.reshape(-1).contiguous()
+    caches = []
+    for _ in range(copies):
+        c = torch.empty(cache_bytes, dtype=torch.uint8, device="cuda")
+        k = torch.randn((B * T, hkv, D), generator=gen, device="cuda", dtype=torch.float32).half()
+        v = torch.randn((B * T, hkv, D), generator=gen, device="cuda", dtype=torch.float32).half()
+        w4.w4a16_kv_append(k, v, slots, bits, c)
+        del k, v
+        caches.append(c)
+    q = torch.randn((B, hq, D), generator=gen, device="cuda", dtype=torch.float32).half()
+    out = torch.empty_like(q)
+    lengths = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    ws = torch.empty(w4.w4a16_kv_attention_workspace_bytes(B, hkv, nblk), dtype=torch.uint8, device="cuda")
+    sm = 1 / math.sqrt(D)
+    for c in caches:
+        w4.w4a16_kv_attention(q, c, table, lengths, bits, hkv, sm, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for c in caches:
+            w4.w4a16_kv_attention(q, c, table, lengths, bits, hkv, sm, out=out, workspace=ws)
+    b.record()
+    b.synchronize()
+    calls = reps * copies
+    ms = a.elapsed_time(b) / calls
+    nbytes = B * hkv * T * (2 * D * bits // 8 + 8) + 2 * q.numel() * 2
+    del caches, ws
+    torch.cuda.empty_cache()
+    return {
+        "metric": f"decode attention GB/s over an int{bits} KV cache, 50 x 4000 tokens, 32/8 heads, d 128",
+        "value": nbytes / (ms * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "us_per_call": ms * 1e3,
+        "bytes_per_call": nbytes,
+        "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "rotation_copies": copies,
+        "timing": "eager calls (attention + chunk merge kernels), HIP events around %d calls" % calls,
+    }
+
+
 def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -318,6 +382,10 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.quantizer_only:
         print(json.dumps(run_quantize_secondary(args)), flush=True)
+        return 0
+    if args.kv_only:
+        for bits in (8, 4):
+            print(json.dumps(run_kv_secondary(args, bits)), flush=True)
         return 0
     insts = synth.workload_instances(args.workload)
     prefill = all(i.M > 32 for i in insts)
@@ -404,6 +472,7 @@ def main(argv=None):
     if not prefill and not args.no_secondary:
         out["secondary"] = run_prefill_secondary(args)
         out["quantizer"] = run_quantize_secondary(args)
+        out["kv_attention"] = [run_kv_secondary(args, 8), run_kv_secondary(args, 4)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(runner)
     print(json.dumps(out), flush=True)

@@ -30,7 +30,7 @@ size_t kv_region_bytes(int bits);  // one (block, KV head) region
 struct KvPlan {
     int chunk_blocks, nchunks;
 };
-KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus);
+KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus, int bits);
 size_t kv_workspace_bytes(int B, int Hkv, int max_blocks, int num_cus);
 hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int ntok, int Hkv, int bits,
                             int64_t num_blocks, uint8_t *cache, hipStream_t stream);

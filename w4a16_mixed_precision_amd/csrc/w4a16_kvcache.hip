@@ -30,16 +30,17 @@
 //   operand is one token's codes, 32 contiguous dimensions per lane (16 or
 //   32 bytes): the dimension order inside the reduction is permuted so that
 //   every lane reads contiguous codes, and the query is permuted the same way
-//   once per wave (the pages' adaptive head alignment, "Q rearranged once so
-//   its K-slices match the low-bit key layout"). The codes become fp16 by
-//   exponent-OR (1024 + c), the zero is subtracted exactly, and the token's
-//   scale (times the softmax scale and log2 e) multiplies the score row.
+//   once per wave (the pages' adaptive head alignment: the query is
+//   rearranged once so that its slices match the low-bit key layout). The
+//   codes enter as 1024 + c (exponent-OR, one instruction per two codes);
+//   each score then loses (1024 + z) * sum(q) and is multiplied by the
+//   token's scale times the softmax scale and log2 e.
 // * Online softmax in fp32 per head (exp2).
 // * O^T = V^T . P^T on the matrix cores: the V rows are stored index-major in
 //   the position order above, which puts in each lane exactly the eight
 //   tokens whose probabilities that lane already holds after the score
 //   product, so P needs no data movement; V's per-token scale is folded into
-//   P and its zero subtracted exactly from the codes.
+//   P (rounded to fp16) and its zero subtracted exactly from the codes.
 // * The loads of the next cache block are issued before the current one is
 //   multiplied (two register sets), the pages' double-buffered KV pipeline.
 // * Each wave writes a partial (max, sum, unnormalized O) per head; a second
@@ -147,31 +148,35 @@ kv_append_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
 }
 
 // ------------------------------------------------------------------ attention
-// Registers of one cache block for one wave.
+// Registers of one half block (32 tokens) for one wave: the pipeline stage.
 template <int BITS>
-struct KvBlock {
-    u32x4 kc[4][BITS == 8 ? 2 : 1];  // K codes of token tile tt, 32 dims per lane
-    uint32_t kz[4];                  // K parameters of the lane's own token per tile
-    u32x4 kp[4];                     // K parameters of tokens 16 tt + 4 kq + 0..3
-    u32x4 vp[4];                     // V parameters of the same tokens
-    uint32_t vc[2][8][BITS == 8 ? 2 : 1];  // V codes: half, d tile, 8 positions
-    bool valid;                            // the table entry names a cache block
+struct KvStage {
+    u32x4 kc[2][BITS == 8 ? 2 : 1];  // K codes of the two 16-token tiles, 32 dims per lane
+    u32x4 kp[2];                     // K parameters of tokens 16 tt + 4 kq + 0..3
+    u32x4 vp[2];                     // V parameters of the same tokens
+    uint32_t vc[8][BITS == 8 ? 2 : 1];  // V codes: d tile, 8 positions
 };
 
-// fp16 pair (1024 + b0, 1024 + b1) of two bytes of w (8-bit codes)
-__device__ inline uint32_t bytes_to_h2(uint32_t w, int first) {
-    const uint32_t b0 = (w >> (8 * first)) & 0xFFu, b1 = (w >> (8 * first + 8)) & 0xFFu;
-    return b0 | (b1 << 16) | 0x64006400u;
+// fp16 pair (1024 + byte 2i, 1024 + byte 2i + 1) of the 8-bit codes in w:
+// v_perm_b32 takes bytes 0-3 from its second source and 4-7 from its first
+__device__ inline uint32_t bytes_to_h2(uint32_t w, int i) {
+    return __builtin_amdgcn_perm(0x64646464u, w, i ? 0x04030402u : 0x04010400u);
 }
 
+// Waves per SIMD the attention kernel is built for (register budget: with
+// one half block in flight, 8-bit stages fit two waves and 4-bit stages
+// three without the compiler reusing registers of loads still in flight).
 template <int BITS>
-__global__ void __launch_bounds__(256)
+constexpr int kv_waves_per_simd() { return BITS == 8 ? 2 : 3; }
+
+template <int BITS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kv_waves_per_simd<BITS>(), kv_waves_per_simd<BITS>())))
 kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ cache,
                     const int32_t *__restrict__ block_table, int max_blocks, const int32_t *__restrict__ lengths,
                     int B, int Hq, int Hkv, int64_t num_blocks, float score_scale, int chunk_blocks, int nchunks,
                     float *__restrict__ part_o, float2 *__restrict__ part_ml) {
     typedef KvGeom<BITS> Geo;
-    typedef KvBlock<BITS> Blk;
+    typedef KvStage<BITS> Stage;
     const int lane = threadIdx.x & 63;
     const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int units = B * Hkv * nchunks;
@@ -184,8 +189,11 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
     int len = lengths[b];
     if (len > max_blocks * kBS) len = max_blocks * kBS;
     const int nblk = len > 0 ? (len + kBS - 1) / kBS : 0;
-    const int b0 = chunk * chunk_blocks;
-    const int b1 = b0 + chunk_blocks < nblk ? b0 + chunk_blocks : nblk;
+    const int bb0 = chunk * chunk_blocks;
+    const int bb1 = bb0 + chunk_blocks < nblk ? bb0 + chunk_blocks : nblk;
+    // half blocks [h0, h1) of this chunk that hold tokens
+    const int h0 = 2 * bb0;
+    const int h1 = bb1 > bb0 ? (2 * bb1 < (len + 31) / 32 ? 2 * bb1 : (len + 31) / 32) : h0;
 
     // query of head kh * g + c in the key's dimension order (B operand of
     // S^T = K . Q^T): step s, slot j of lane group kq holds dimension
@@ -212,42 +220,59 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
             }
         }
     }
-
-    auto region_of = [&](int bi) -> int64_t {
-        int id = block_table[(size_t)b * max_blocks + bi];
-        if (id < 0 || id >= num_blocks) id = -1;
-        return id < 0 ? -1 : ((int64_t)id * Hkv + kh) * Geo::kRegion;
-    };
-    auto load = [&](int bi, Blk &B_) {
-        const int64_t reg = region_of(bi);
-        B_.valid = reg >= 0;
-        const uint8_t *base = cache + (reg < 0 ? 0 : reg);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base, reg < 0 ? 0u : (uint32_t)Geo::kRegion);
+    // The key codes enter the matrix instruction as bias + c: 1024 + c
+    // (8-bit codes and the low nibbles of 4-bit ones, exponent-OR) or 64 + c
+    // (high nibbles, which need no shift). A score then loses
+    // sum_d bias_d q_d + z * sum(q); both sums are per head (the four kq lane
+    // groups hold 32 dimensions each). In the 4-bit slot order the slots
+    // 0, 1, 4, 5 of a step hold low nibbles and 2, 3, 6, 7 high ones.
+    float qsum = 0.f, qbias = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float qv = (float)qf[s][j];
+            qsum += qv;
+            qbias += qv * (BITS == 8 || ((j >> 1) & 1) == 0 ? 1024.f : 64.f);
+        }
+    qsum += __shfl_xor(qsum, 16, 64);
+    qsum += __shfl_xor(qsum, 32, 64);
+    qbias += __shfl_xor(qbias, 16, 64);
+    qbias += __shfl_xor(qbias, 32, 64);
+
+    // Half block hb = 2 * block + half. Stages past the chunk, or in a block
+    // the table does not name, load through an empty descriptor: no memory
+    // traffic and the same instructions on every path.
+    auto load = [&](int hb, Stage &S) {
+        const int bi = hb >> 1, hf = hb & 1;
+        const int bic = bi < max_blocks ? bi : max_blocks - 1;  // stays inside the table
+        int id = hb < h1 ? block_table[(size_t)b * max_blocks + bic] : -1;
+        if (id >= num_blocks) id = -1;
+        const uint8_t *base = cache + (id < 0 ? 0 : ((int64_t)id * Hkv + kh) * Geo::kRegion);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base, id < 0 ? 0u : (uint32_t)Geo::kRegion);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tt = 2 * hf + u;
             const int tok = 16 * tt + c;
 #pragma unroll
-            for (int u = 0; u < (BITS == 8 ? 2 : 1); ++u)
-                B_.kc[tt][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                              r, (uint32_t)(tok * Geo::kRowBytes + (32 * kq) * BITS / 8 + 16 * u), 0, 0));
-            B_.kz[tt] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(Geo::kKPar + 4 * tok), 0, 0);
+            for (int w = 0; w < (BITS == 8 ? 2 : 1); ++w)
+                S.kc[u][w] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           r, (uint32_t)(tok * Geo::kRowBytes + (32 * kq) * BITS / 8 + 16 * w), 0, 0));
             const int t4 = 16 * tt + 4 * kq;
-            B_.kp[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kKPar + 4 * t4), 0, 0));
-            B_.vp[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kVPar + 4 * t4), 0, 0));
+            S.kp[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kKPar + 4 * t4), 0, 0));
+            S.vp[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kVPar + 4 * t4), 0, 0));
         }
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const uint32_t off = (uint32_t)(Geo::kCodeBytes + (16 * dt + c) * Geo::kVRowBytes + (16 * kq + 8 * hf) * BITS / 8);
-                if constexpr (BITS == 8) {
-                    const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-                    B_.vc[hf][dt][0] = (uint32_t)w2[0];
-                    B_.vc[hf][dt][1] = (uint32_t)w2[1];
-                } else {
-                    B_.vc[hf][dt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-                }
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t off = (uint32_t)(Geo::kCodeBytes + (16 * dt + c) * Geo::kVRowBytes + (16 * kq + 8 * hf) * BITS / 8);
+            if constexpr (BITS == 8) {
+                const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+                S.vc[dt][0] = (uint32_t)w2[0];
+                S.vc[dt][1] = (uint32_t)w2[1];
+            } else {
+                S.vc[dt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
             }
+        }
     };
 
     floatx4 o[8];
@@ -255,124 +280,130 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
     for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff(), l_run = 0.f;
 
-    auto compute = [&](int bi, const Blk &B_) {
-        const int tok0 = bi * kBS;
+    auto compute = [&](int hb, const Stage &S) {
+        const int tok0 = 32 * hb;  // sequence position of the stage's first token
+        const int bi = hb >> 1;
+        int id = block_table[(size_t)b * max_blocks + bi];
+        if (id < 0 || id >= num_blocks) return;  // uniform: an absent block holds no tokens
+        const bool full = tok0 + 32 <= len;
+        // ---- scores of the 32 tokens (two 16-token tiles): the matrix
+        // instruction multiplies the codes as 1024 + c (exponent-OR, no
+        // per-code subtraction); the zero enters each score once as
+        // -(1024 + z) * sum(q), exact products summed in fp32
+        float x[2][4];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            if (tok0 + 32 * hf >= len || !B_.valid) break;  // uniform
-            // ---- scores of tokens 32 hf .. +31 (two 16-token tiles)
-            float x[2][4];
+        for (int u = 0; u < 2; ++u) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int tt = 2 * hf + u;
-                const uint32_t zc = B_.kz[tt] >> 16 & 0xFFu;
-                const uint32_t nb = (0xE400u | zc) * 0x10001u;  // -(1024 + z) pair (8-bit: z up to 255)
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    half8 a;
-                    if constexpr (BITS == 8) {
-                        const u32x4 &w = B_.kc[tt][s >> 1];
-                        const uint32_t w0 = w[2 * (s & 1)], w1 = w[2 * (s & 1) + 1];
-                        a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(nb), as_h2(bytes_to_h2(w0, 2)) + as_h2(nb),
-                                    as_h2(bytes_to_h2(w1, 0)) + as_h2(nb), as_h2(bytes_to_h2(w1, 2)) + as_h2(nb));
-                    } else {
-                        const uint32_t w = B_.kc[tt][0][s];
-                        a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)) + as_h2(nb),
-                                    as_h2(and_or(w >> 4, kLoMask, kMagic)) + as_h2(nb),
-                                    as_h2(and_or(w >> 8, kLoMask, kMagic)) + as_h2(nb),
-                                    as_h2(and_or(w >> 12, kLoMask, kMagic)) + as_h2(nb));
-                    }
-                    acc = mfma16x16x32(a, qf[s], acc);
+            for (int s = 0; s < 4; ++s) {
+                half8 a;
+                if constexpr (BITS == 8) {
+                    const u32x4 &w = S.kc[u][s >> 1];
+                    const uint32_t w0 = w[2 * (s & 1)], w1 = w[2 * (s & 1) + 1];
+                    a = pack_h8(as_h2(bytes_to_h2(w0, 0)), as_h2(bytes_to_h2(w0, 1)), as_h2(bytes_to_h2(w1, 0)),
+                                as_h2(bytes_to_h2(w1, 1)));
+                } else {
+                    const uint32_t w = S.kc[u][0][s], w8 = w >> 8;
+                    a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)), as_h2(and_or(w, kHiMask, kMagic64)),
+                                as_h2(and_or(w8, kLoMask, kMagic)), as_h2(and_or(w8, kHiMask, kMagic64)));
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tok = tok0 + 16 * tt + 4 * kq + e;
-                    const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)(B_.kp[tt][e] & 0xFFFFu));
-                    const float sc = acc[e] * (ks * score_scale);
-                    x[u][e] = tok < len && B_.valid ? sc : -__builtin_inff();
-                }
+                acc = mfma16x16x32(a, qf[s], acc);
             }
-            // ---- online softmax for head c (the four kq lane groups hold
-            // different tokens of the same head)
-            float mt = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(x[0][0], x[0][1]), __builtin_fmaxf(x[0][2], x[0][3])),
-                                       __builtin_fmaxf(__builtin_fmaxf(x[1][0], x[1][1]), __builtin_fmaxf(x[1][2], x[1][3])));
-            mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float m_new = __builtin_fmaxf(m_run, mt);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t par = S.kp[u][e];
+                const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)(par & 0xFFFFu));
+                const float zk = (float)(par >> 16 & 0xFFu);
+                const float sc = __builtin_fmaf(-zk, qsum, acc[e] - qbias) * (ks * score_scale);
+                x[u][e] = full || tok0 + 16 * u + 4 * kq + e < len ? sc : -__builtin_inff();
+            }
+        }
+        // ---- online softmax for head c (the four kq lane groups hold
+        // different tokens of the same head)
+        float mt = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(x[0][0], x[0][1]), __builtin_fmaxf(x[0][2], x[0][3])),
+                                   __builtin_fmaxf(__builtin_fmaxf(x[1][0], x[1][1]), __builtin_fmaxf(x[1][2], x[1][3])));
+        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32, 64));
+        // The running maximum moves only when a head's maximum rises by more
+        // than 8 (log2 units): the probabilities stay below 2^8 (exact
+        // enough in fp16 after the V scale) and most stages skip the rescale
+        // of O. The result does not depend on which maximum is used.
+        const float m_new = mt > m_run + 8.f ? mt : m_run;
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {  // some head's max moved: rescale
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float p[2][4];
-            float psum = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[u][e] = __builtin_amdgcn_exp2f(x[u][e] - m_new);
-                    psum += p[u][e];
-                }
-            l_run = l_run * alpha + psum;
+            l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[dt][e] *= alpha;
-            // ---- B operand P^T for O^T = V^T . P^T: slot j holds token
-            // 32 hf + 4 kq + j (j < 4) or 32 hf + 16 + 4 kq + j - 4, times
-            // its V scale; masked tokens contribute exactly zero
-            half8 pb;
-            uint32_t vzn[4];  // -(1024 + z) pairs of the slot pairs
+            m_run = m_new;
+        }
+        // ---- B operand P^T for O^T = V^T . P^T: slot j holds token
+        // 4 kq + j (j < 4) or 16 + 4 kq + j - 4 of the stage, times its V
+        // scale; masked tokens contribute exactly zero
+        half8 pb;
+        float psum = 0.f;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t par = B_.vp[2 * hf + u][e];
-                    const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(par & 0xFFFFu));
-                    const float pv = x[u][e] == -__builtin_inff() ? 0.f : p[u][e] * vs;
-                    const int j = 4 * u + e;
-                    // 4-bit V: the nibble extraction yields slots 0 4 1 5 2 6 3 7
-                    const int slot = BITS == 8 ? j : (j < 4 ? 2 * j : 2 * (j - 4) + 1);
-                    pb[slot] = (_Float16)pv;
-                }
-#pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-                // slot pair (2 pr, 2 pr + 1): 8-bit tokens j = 2 pr, 2 pr + 1;
-                // 4-bit tokens j = pr, pr + 4
-                const int ja = BITS == 8 ? 2 * pr : pr, jb = BITS == 8 ? 2 * pr + 1 : pr + 4;
-                const uint32_t za = B_.vp[2 * hf + ja / 4][ja % 4] >> 16 & 0xFFu;
-                const uint32_t zb = B_.vp[2 * hf + jb / 4][jb % 4] >> 16 & 0xFFu;
-                vzn[pr] = (0xE400u | za) | ((0xE400u | zb) << 16);
+            for (int e = 0; e < 4; ++e) {
+                const float p = __builtin_amdgcn_exp2f(x[u][e] - m_run);
+                psum += p;
+                const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(S.vp[u][e] & 0xFFFFu));
+                const _Float16 pv = (_Float16)(x[u][e] == -__builtin_inff() ? 0.f : p * vs);
+                const int j = 4 * u + e;
+                // 4-bit V: the nibble extraction yields slots 0 4 1 5 2 6 3 7
+                const int slot = BITS == 8 ? j : (j < 4 ? 2 * j : 2 * (j - 4) + 1);
+                pb[slot] = pv;
             }
-            // ---- O^T += V^T . P^T over the 8 tiles of 16 dimensions
+        l_run += psum;
+        uint32_t vzn[4];  // -(1024 + z) pairs of the slot pairs
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                half8 a;
-                if constexpr (BITS == 8) {
-                    const uint32_t w0 = B_.vc[hf][dt][0], w1 = B_.vc[hf][dt][1];
-                    a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(vzn[0]), as_h2(bytes_to_h2(w0, 2)) + as_h2(vzn[1]),
-                                as_h2(bytes_to_h2(w1, 0)) + as_h2(vzn[2]), as_h2(bytes_to_h2(w1, 2)) + as_h2(vzn[3]));
-                } else {
-                    const uint32_t w = B_.vc[hf][dt][0];
-                    a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)) + as_h2(vzn[0]),
-                                as_h2(and_or(w >> 4, kLoMask, kMagic)) + as_h2(vzn[1]),
-                                as_h2(and_or(w >> 8, kLoMask, kMagic)) + as_h2(vzn[2]),
-                                as_h2(and_or(w >> 12, kLoMask, kMagic)) + as_h2(vzn[3]));
-                }
-                o[dt] = mfma16x16x32(a, pb, o[dt]);
+        for (int pr = 0; pr < 4; ++pr) {
+            // slot pair (2 pr, 2 pr + 1): 8-bit tokens j = 2 pr, 2 pr + 1;
+            // 4-bit tokens j = pr, pr + 4
+            const int ja = BITS == 8 ? 2 * pr : pr, jb = BITS == 8 ? 2 * pr + 1 : pr + 4;
+            const uint32_t za = S.vp[ja / 4][ja % 4] >> 16 & 0xFFu;
+            const uint32_t zb = S.vp[jb / 4][jb % 4] >> 16 & 0xFFu;
+            // -(1024 + z) for 8-bit codes and low nibbles, -(64 + z) for the
+            // high nibbles of 4-bit codes (slot pairs 1 and 3)
+            const uint32_t lo = 0xE400u | za, hi = 0xE400u | zb;
+            const uint32_t pair = lo | (hi << 16);
+            vzn[pr] = BITS == 4 && (pr & 1) ? neg_bias64_from_1024(pair) : pair;
+        }
+        // ---- O^T += V^T . P^T over the 8 tiles of 16 dimensions with the
+        // exact integers c - z (the outputs are averages much smaller than
+        // the codes, so the zero is not deferred as it is for the scores)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            half8 a;
+            if constexpr (BITS == 8) {
+                const uint32_t w0 = S.vc[dt][0], w1 = S.vc[dt][1];
+                a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(vzn[0]), as_h2(bytes_to_h2(w0, 1)) + as_h2(vzn[1]),
+                            as_h2(bytes_to_h2(w1, 0)) + as_h2(vzn[2]), as_h2(bytes_to_h2(w1, 1)) + as_h2(vzn[3]));
+            } else {
+                const uint32_t w = S.vc[dt][0], w8 = w >> 8;
+                a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)) + as_h2(vzn[0]),
+                            as_h2(and_or(w, kHiMask, kMagic64)) + as_h2(vzn[1]),
+                            as_h2(and_or(w8, kLoMask, kMagic)) + as_h2(vzn[2]),
+                            as_h2(and_or(w8, kHiMask, kMagic64)) + as_h2(vzn[3]));
             }
+            o[dt] = mfma16x16x32(a, pb, o[dt]);
         }
     };
 
-    if (b0 < b1) {
-        Blk bufA, bufB;
-        load(b0, bufA);
-        int bi = b0;
-        for (; bi + 1 < b1; bi += 2) {
-            load(bi + 1, bufB);
-            compute(bi, bufA);
-            if (bi + 2 < b1) load(bi + 2, bufA);
-            compute(bi + 1, bufB);
+    // Two stages: the next half block is in flight while one is multiplied
+    // (the pages' double-buffered KV loading).
+    if (h0 < h1) {
+        Stage s0, s1;
+        load(h0, s0);
+        for (int hb = h0; hb < h1; hb += 2) {
+            load(hb + 1, s1);
+            compute(hb, s0);
+            if (hb + 1 >= h1) break;
+            load(hb + 2, s0);
+            compute(hb + 1, s1);
         }
-        if (bi < b1) compute(bi, bufA);
     }
 
     // ---- partial results of this chunk: (max, sum) and unnormalized O^T
@@ -425,12 +456,13 @@ hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t 
     return hipGetLastError();
 }
 
-KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus) {
+KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus, int bits) {
     KvPlan p;
-    // enough waves for eight per CU; chunks of whole blocks
+    // split each (sequence, KV head) into as many chunks of whole blocks as
+    // keep the work in one round of resident waves (4 SIMDs per CU)
     const long pairs = (long)B * Hkv;
-    const long want = (long)num_cus * 8;
-    int nchunks = (int)((want + pairs - 1) / pairs);
+    const long resident = (long)num_cus * 4 * (bits == 8 ? kv_waves_per_simd<8>() : kv_waves_per_simd<4>());
+    int nchunks = (int)(resident / pairs);
     if (nchunks > max_blocks) nchunks = max_blocks;
     if (nchunks < 1) nchunks = 1;
     p.chunk_blocks = (max_blocks + nchunks - 1) / nchunks;
@@ -439,15 +471,16 @@ KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus) {
 }
 
 size_t kv_workspace_bytes(int B, int Hkv, int max_blocks, int num_cus) {
-    const KvPlan p = kv_plan(B, Hkv, max_blocks, num_cus);
-    const size_t units = (size_t)B * Hkv * p.nchunks;
+    // sized for the larger of the two code widths' plans
+    const KvPlan p8 = kv_plan(B, Hkv, max_blocks, num_cus, 8), p4 = kv_plan(B, Hkv, max_blocks, num_cus, 4);
+    const size_t units = (size_t)B * Hkv * (p8.nchunks > p4.nchunks ? p8.nchunks : p4.nchunks);
     return units * 16 * kHD * sizeof(float) + units * 16 * sizeof(float2);
 }
 
 hipError_t launch_kv_attention(const uint16_t *q, const uint8_t *cache, const int32_t *block_table, int max_blocks,
                                const int32_t *lengths, int B, int Hq, int Hkv, int bits, int64_t num_blocks,
                                float sm_scale, uint16_t *out, void *workspace, int num_cus, hipStream_t stream) {
-    const KvPlan p = kv_plan(B, Hkv, max_blocks, num_cus);
+    const KvPlan p = kv_plan(B, Hkv, max_blocks, num_cus, bits);
     const size_t units = (size_t)B * Hkv * p.nchunks;
     float *part_o = static_cast<float *>(workspace);
     float2 *part_ml = reinterpret_cast<float2 *>(part_o + units * 16 * kHD);
