@@ -18,6 +18,8 @@ Contents
 * ``kvcache``: the low-bit KV cache (per-token, per-head asymmetric 8/4-bit
   quantization, the blocked cache layout written out as index arithmetic)
   and float64 decode attention over it (``kvcache.py``).
+* ``w8a8``: the 8-bit-weight, 8-bit-activation GEMM (symmetric per-channel
+  and per-token scales, exact integer sums) (``w8a8.py``).
 * ``layout_pack`` / ``layout_unpack``: the packed weight format written out as
   plain index arithmetic, so the bytes the GPU packer writes can be checked
   one by one. The pages ("LMDeploy Guide: Fast Mixed-Precision LLM Inference
@@ -52,12 +54,12 @@ import subprocess
 
 import numpy as np
 
-from . import kvcache
+from . import kvcache, w8a8
 from .quantize import quantize
 
 __all__ = [
     "lib_path", "build", "load", "half_to_double", "dequant", "gemm", "compare",
-    "packed_bytes", "layout_pack", "layout_unpack", "max_threads", "quantize", "kvcache",
+    "packed_bytes", "layout_pack", "layout_unpack", "max_threads", "quantize", "kvcache", "w8a8",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -1,0 +1,119 @@
+"""Pins of the oracle's W8A8 GEMM (no GPU needed).
+
+Hand-worked scales and codes (power-of-two scales make every step exact),
+the nearest-code property, the per-token / per-channel scale axes, the
+exact integer product against plain Python loops, and a closed form: when
+X and W lie on their quantization grids with power-of-two scales the
+quantized GEMM is the fp16 rounding of the exact float product. Planted
+mistakes each fail a pin.
+"""
+import numpy as np
+import pytest
+
+from oracle import w8a8
+
+
+def test_hand_worked_scale_and_ties():
+    # max |x| = 127/64: scale 1/64 exactly, reciprocal 64; 0.5 -> 32;
+    # 32.5/64 -> 32.5 -> 32 (even); 33.5/64 -> 34; -127/64 -> -127
+    x = np.array([[127 / 64, 0.5, 32.5 / 64, 33.5 / 64, -127 / 64, 0.0]], np.float16)
+    q, s = w8a8.quantize_activations(x)
+    assert s[0] == np.float32(1 / 64)
+    assert q[0].tolist() == [127, 32, 32, 34, -127, 0]
+
+
+def test_zero_row_and_column():
+    q, s = w8a8.quantize_activations(np.zeros((2, 8), np.float16))
+    assert np.all(s == 1) and not q.any()
+    q, s = w8a8.quantize_weights(np.zeros((8, 3), np.float16))
+    assert np.all(s == 1) and not q.any()
+
+
+def test_scale_axes():
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((5, 64)).astype(np.float16)
+    X[2] *= 10
+    qx, sx = w8a8.quantize_activations(X)
+    assert sx.shape == (5,) and np.argmax(sx) == 2
+    W = rng.standard_normal((64, 7)).astype(np.float16)
+    W[:, 4] *= 10
+    qw, sw = w8a8.quantize_weights(W)
+    assert sw.shape == (7,) and np.argmax(sw) == 4
+    # the largest |value| of every row / column maps to +-127
+    assert np.all(np.abs(qx).max(axis=1) == 127) and np.all(np.abs(qw).max(axis=0) == 127)
+
+
+def test_codes_are_nearest():
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((16, 256)).astype(np.float16)
+    q, s = w8a8.quantize_activations(X)
+    err = np.abs(X.astype(np.float64) - q.astype(np.float64) * s.astype(np.float64)[:, None])
+    assert np.all(err <= 0.5 * s.astype(np.float64)[:, None] * (1 + 1e-6))
+
+
+def test_integer_product_against_loops():
+    rng = np.random.default_rng(3)
+    qx = rng.integers(-127, 128, (3, 40)).astype(np.int8)
+    qw = rng.integers(-127, 128, (40, 5)).astype(np.int8)
+    ref = [[sum(int(qx[m, k]) * int(qw[k, n]) for k in range(40)) for n in range(5)] for m in range(3)]
+    assert np.array_equal(w8a8.gemm_int(qx, qw), np.array(ref))
+
+
+def test_on_grid_inputs_give_the_rounded_exact_product():
+    rng = np.random.default_rng(4)
+    M, K, N = 6, 128, 9
+    cx = rng.integers(-127, 128, (M, K))
+    cx[:, 0] = 127
+    cw = rng.integers(-127, 128, (K, N))
+    cw[1, :] = -127
+    X = (cx / 64.0).astype(np.float16)   # on the grid: exact in fp16
+    W = (cw / 32.0).astype(np.float16)
+    qx, sx = w8a8.quantize_activations(X)
+    qw, sw = w8a8.quantize_weights(W)
+    assert np.array_equal(qx, cx) and np.array_equal(qw, cw)
+    Y = w8a8.gemm(qx, sx, qw, sw)
+    exact = (cx @ cw) / 2048.0  # |acc| < 2^24: float32 exact, power-of-two scales exact
+    assert np.array_equal(Y, exact.astype(np.float16))
+
+
+def test_quantization_error_is_small():
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((8, 1024)).astype(np.float16)
+    W = (rng.standard_normal((1024, 64)) * 0.02).astype(np.float16)
+    qx, sx = w8a8.quantize_activations(X)
+    qw, sw = w8a8.quantize_weights(W)
+    Y = w8a8.gemm(qx, sx, qw, sw).astype(np.float64)
+    ref = w8a8.dequant_gemm(X, W)
+    assert np.linalg.norm(Y - ref) / np.linalg.norm(ref) < 0.02
+
+
+def _wrong():
+    def per_tensor(X):
+        f = X.astype(np.float32)
+        s = np.float32(np.abs(f).max() / 127)
+        q = np.clip(np.rint(f.astype(np.float64) * float(np.float32(1) / s)), -127, 127).astype(np.int8)
+        return q, np.full(X.shape[0], s, np.float32)
+
+    def wrong_axis(X):
+        q, s = w8a8.quantize_symmetric(X, axis=0)
+        return q, s
+
+    def levels_128(X):
+        f = X.astype(np.float32)
+        amax = np.abs(f).max(axis=1)
+        s = np.where(amax > 0, amax / np.float32(128), np.float32(1)).astype(np.float32)
+        q = np.clip(np.rint(f.astype(np.float64) * (np.float32(1) / s).astype(np.float64)[:, None]), -128, 127)
+        return q.astype(np.int8), s
+    return [per_tensor, wrong_axis, levels_128]
+
+
+@pytest.mark.parametrize("idx", range(3))
+def test_planted_mistakes_are_caught(idx, monkeypatch):
+    monkeypatch.setattr(w8a8, "quantize_activations", _wrong()[idx])
+    failed = 0
+    for t in (test_hand_worked_scale_and_ties, test_scale_axes):
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed > 0
