@@ -260,6 +260,49 @@ int w4a16_kv_attention(const uint16_t *q, const void *cache, int64_t num_blocks,
                        int64_t B, int64_t q_heads, int64_t kv_heads, int bits, float sm_scale,
                        uint16_t *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * W8A8 GEMM: 8-bit weights times 8-bit activations on the int8 matrix cores
+ * (W8A8 is the precision format "LMDeploy Guide: Fast Mixed-Precision LLM
+ * Inference Engine" lists beside W4A16; the pages give no formula). Symmetric
+ * scales: one per output channel for W (offline), one per token for X (per
+ * call): s = max|v| / 127 in float32 (1 for an all-zero vector), code =
+ * clamp(rint(v / s), -127, 127) with the product of v and the float32
+ * reciprocal of s exact and rounded once; Y[m][n] =
+ * fp16(float32(float32(acc) * s_x[m]) * s_w[n]) with acc the exact int32 sum
+ * of code products.
+ *
+ * Shapes: K % 256 == 0, K <= 131072 (the int32 sum cannot overflow),
+ * N % 16 == 0, K * N < 2^32, 1 <= M <= 2^30.
+ * Packed weights (K * N bytes): 1 KiB tiles of 16 columns x 64 rows of K,
+ * tile (n / 16) * (K / 64) + k / 64; inside a tile, 16 bytes per lane
+ * l = 16 * ((k % 64) / 16) + n % 16, byte k % 16 (int8 codes).
+ * ---------------------------------------------------------------------------
+ */
+
+/* Bytes of the packed W8A8 weights (K * N); 0 for an unsupported shape. */
+size_t w4a16_w8a8_packed_bytes(int64_t K, int64_t N);
+
+/* Offline: fp16 W [K][N] -> packed int8 codes and float32 w_scales [N].
+ * Asynchronous on `stream`; non-finite weights give unspecified codes. */
+int w4a16_w8a8_quantize_weights(const uint16_t *W, int64_t K, int64_t N, void *packed, float *w_scales,
+                                void *stream);
+
+/* Per call: fp16 X [M][K] -> int8 xq [M][K] and float32 x_scales [M].
+ * Asynchronous on `stream`. */
+int w4a16_w8a8_quantize_act(const uint16_t *X, int64_t M, int64_t K, int8_t *xq, float *x_scales,
+                            void *stream);
+
+/* Workspace bytes of w4a16_w8a8_gemm (int32 partial sums when K is split
+ * across workgroups; depends on the current device's CU count; 0 if none). */
+size_t w4a16_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* Y[M][N] (fp16) from the codes and scales above. Asynchronous on `stream`;
+ * calls sharing a workspace must be ordered. */
+int w4a16_w8a8_gemm(const int8_t *xq, const float *x_scales, const void *packed, const float *w_scales,
+                    int64_t M, int64_t N, int64_t K, uint16_t *Y, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* Static description of a status code. */
 const char *w4a16_status_string(int status);
 

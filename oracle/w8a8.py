@@ -33,7 +33,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["quantize_symmetric", "quantize_weights", "quantize_activations", "gemm_int", "gemm", "dequant_gemm"]
+__all__ = ["quantize_symmetric", "quantize_weights", "quantize_activations", "gemm_int", "gemm", "dequant_gemm",
+           "pack_weights"]
 
 
 def quantize_symmetric(x, axis: int):
@@ -82,3 +83,23 @@ def dequant_gemm(X, W):
     """float64 reference of the unquantized product (for the error the
     quantization itself introduces, not for parity)."""
     return X.astype(np.float64) @ W.astype(np.float64)
+
+
+def pack_weights(q):
+    """Packed bytes (uint8 [K*N]) of int8 codes q [K][N]: 1 KiB tiles of 16
+    columns x 64 rows of K, tile (n // 16) * (K // 64) + k // 64; inside a
+    tile, 16 bytes per lane l = 16 * ((k % 64) // 16) + n % 16, byte k % 16
+    (this library's layout: the B operand of one 16 x 16 x 64 int8 matrix
+    instruction per lane)."""
+    q = np.ascontiguousarray(q)
+    K, N = q.shape
+    if K % 64 or N % 16:
+        raise ValueError("K must be a multiple of 64 and N of 16")
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    tile = (n // 16) * (K // 64) + k // 64
+    lane = 16 * ((k % 64) // 16) + n % 16
+    pos = 1024 * tile + 16 * lane + k % 16
+    out = np.zeros(K * N, np.uint8)
+    out[pos.ravel()] = q.view(np.uint8).ravel()
+    return out

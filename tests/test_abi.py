@@ -18,14 +18,17 @@ MISALIGNED = ctypes.c_void_p(0x10008)
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
               "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
-              "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack"):
+              "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack",
+              "w4a16_kv_block_bytes", "w4a16_kv_append", "w4a16_kv_attention_workspace_bytes",
+              "w4a16_kv_attention", "w4a16_w8a8_packed_bytes", "w4a16_w8a8_quantize_weights",
+              "w4a16_w8a8_quantize_act", "w4a16_w8a8_workspace_bytes", "w4a16_w8a8_gemm"):
         assert n in names
 
 
@@ -112,6 +115,26 @@ def test_quantize_validation_before_any_hip_call():
     assert L.w4a16_quantize_pack(FAKE, 256, 256, 128, None, None) == w4.W4A16_ERR_NULL
     assert L.w4a16_quantize_pack(FAKE, 256, 256, 96, FAKE, None) == w4.W4A16_ERR_SHAPE
     assert L.w4a16_quantize_pack(FAKE, 256, 256, 128, MISALIGNED, None) == w4.W4A16_ERR_ALIGN
+
+
+def test_kv_and_w8a8_validation_before_any_hip_call():
+    L = w4.lib()
+    assert w4.w4a16_kv_block_bytes(8, 8) == 8 * (2 * 64 * 128 + 512)
+    assert w4.w4a16_kv_block_bytes(4, 2) == 2 * (2 * 64 * 64 + 512)
+    assert w4.w4a16_kv_block_bytes(5, 2) == 0
+    assert L.w4a16_kv_append(None, FAKE, FAKE, 1, 8, 8, FAKE, 1, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_kv_append(FAKE, FAKE, FAKE, 1, 8, 6, FAKE, 1, None) == w4.W4A16_ERR_ARG
+    assert L.w4a16_kv_append(FAKE, FAKE, MISALIGNED, 1, 8, 8, FAKE, 1, None) == w4.W4A16_ERR_ALIGN
+    # 12 query heads over 8 KV heads, and 17 query heads per KV head, are refused
+    args = lambda hq, hkv: L.w4a16_kv_attention(FAKE, FAKE, 1, FAKE, 1, FAKE, 1, hq, hkv, 8,
+                                                 ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, None)
+    assert args(12, 8) == w4.W4A16_ERR_SHAPE and args(17, 1) == w4.W4A16_ERR_SHAPE
+    assert w4.w4a16_w8a8_packed_bytes(512, 64) == 512 * 64
+    assert w4.w4a16_w8a8_packed_bytes(320, 64) == 0 and w4.w4a16_w8a8_packed_bytes(1 << 18, 16) == 0
+    assert L.w4a16_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 1, 64, 320, FAKE, None, 0, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_w8a8_gemm(FAKE, None, FAKE, FAKE, 1, 64, 256, FAKE, None, 0, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_w8a8_quantize_act(FAKE, 0, 256, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_w8a8_quantize_weights(FAKE, 256, 24, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
 
 
 def test_status_strings():

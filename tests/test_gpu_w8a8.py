@@ -1,0 +1,87 @@
+"""GPU parity of the W8A8 GEMM and its quantizers against the oracle.
+
+Every decision is taken in the same float32 order on both sides (scales,
+codes from the exact product rounded once, exact int32 sums, the two
+float32 scale products, one fp16 rounding), so the bar is bit-exact:
+codes, scales, packed bytes and Y must equal the oracle's.
+"""
+import numpy as np
+import pytest
+
+import w4a16_mixed_precision_amd as w4
+from gpu_util import dev, host, say
+from oracle import w8a8
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K))
+    X[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20  # outlier channels
+    W = rng.standard_normal((K, N)) * 0.02
+    X, W = X.astype(np.float16), W.astype(np.float16)
+    if M > 2:
+        X[1] = 0  # an all-zero token
+    return X, W
+
+
+def _gpu(X, W):
+    import torch
+    Wd = dev(W)
+    packed, ws = w4.w4a16_w8a8_quantize_weights(Wd)
+    xq, xs = w4.w4a16_w8a8_quantize_act(dev(X))
+    Y = w4.w4a16_w8a8_gemm(xq, xs, packed, ws, W.shape[1])
+    torch.cuda.synchronize()
+    return host(packed), host(ws), host(xq), host(xs), host(Y)
+
+
+SHAPES = [(1, 256, 16), (3, 512, 272), (16, 1024, 1040), (17, 768, 256), (64, 256, 528),
+          (100, 2048, 320), (300, 512, 1024), (1, 4096, 6144), (33, 4096, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w8a8_bit_exact(M, K, N):
+    say(f"w8a8 M={M} K={K} N={N}")
+    X, W = _inputs(M, K, N, M + K + N)
+    packed, ws, xq, xs, Y = _gpu(X, W)
+    qw, sw = w8a8.quantize_weights(W)
+    qx, sx = w8a8.quantize_activations(X)
+    assert np.array_equal(ws.view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(xs.view(np.uint32), sx.view(np.uint32))
+    assert np.array_equal(xq, qx)
+    assert np.array_equal(packed, w8a8.pack_weights(qw))
+    ref = w8a8.gemm(qx, sx, qw, sw)
+    bad = np.argwhere(Y.view(np.uint16) != ref.view(np.uint16))
+    assert bad.size == 0, (bad[:5], Y[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+def test_forced_tile_shapes_agree(monkeypatch):
+    import torch
+    X, W = _inputs(40, 1024, 512, 7)
+    outs = []
+    for t in ("16", "64"):
+        monkeypatch.setenv("W4A16_W8A8_TILE", t)
+        outs.append(_gpu(X, W)[-1])
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+    torch.cuda.synchronize()
+
+
+def test_full_size_llama3_8b_sampled():
+    # gate/up of the Llama-3-8B prefill (M = 2048, K = 4096, N = 28672) and
+    # a decode row block (M = 16), sampled on column windows
+    import torch
+    K, N = 4096, 28672
+    X, W = _inputs(2048, K, N, 99)
+    Wd = dev(W)
+    packed, ws = w4.w4a16_w8a8_quantize_weights(Wd)
+    qw, sw = w8a8.quantize_weights(W)
+    assert np.array_equal(host(ws).view(np.uint32), sw.view(np.uint32))
+    for M in (2048, 16):
+        xq, xs = w4.w4a16_w8a8_quantize_act(dev(X[:M]))
+        Y = host(w4.w4a16_w8a8_gemm(xq, xs, packed, ws, N))
+        torch.cuda.synchronize()
+        qx, sx = w8a8.quantize_activations(X[:M])
+        for c0 in (0, 12288, N - 64):
+            ref = w8a8.gemm(qx, sx, qw[:, c0:c0 + 64], sw[c0:c0 + 64])
+            assert np.array_equal(Y[:, c0:c0 + 64].view(np.uint16), ref.view(np.uint16)), (M, c0)

@@ -117,3 +117,14 @@ def test_planted_mistakes_are_caught(idx, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             failed += 1
     assert failed > 0
+
+
+def test_pack_layout_hand_checked_and_bijective():
+    K, N = 128, 32
+    q = (np.arange(K * N) % 251 - 125).astype(np.int8).reshape(K, N)
+    b = w8a8.pack_weights(q)
+    assert sorted(b.view(np.int8).tolist()) == sorted(q.ravel().tolist())
+    # (k=70, n=19): strip 1, k-tile 1 -> tile 3; lane 16 * ((70 % 64) // 16) + 3 = 3; byte 70 % 16 = 6
+    assert b.view(np.int8)[1024 * 3 + 16 * 3 + 6] == q[70, 19]
+    # (k=33, n=0): tile 0, lane 32, byte 1
+    assert b.view(np.int8)[16 * 32 + 1] == q[33, 0]

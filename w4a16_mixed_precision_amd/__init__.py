@@ -22,6 +22,8 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
     "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack",
     "w4a16_kv_block_bytes", "w4a16_kv_append", "w4a16_kv_attention_workspace_bytes", "w4a16_kv_attention",
+    "w4a16_w8a8_packed_bytes", "w4a16_w8a8_quantize_weights", "w4a16_w8a8_quantize_act",
+    "w4a16_w8a8_workspace_bytes", "w4a16_w8a8_gemm",
 ]
 
 W4A16_OK = 0
@@ -87,6 +89,16 @@ def lib():
     L.w4a16_kv_attention_workspace_bytes.restype = SZ
     L.w4a16_kv_attention.argtypes = [P, P, I64, P, I64, P, I64, I64, I64, I, ctypes.c_float, P, P, SZ, P]
     L.w4a16_kv_attention.restype = I
+    L.w4a16_w8a8_packed_bytes.argtypes = [I64, I64]
+    L.w4a16_w8a8_packed_bytes.restype = SZ
+    L.w4a16_w8a8_quantize_weights.argtypes = [P, I64, I64, P, P, P]
+    L.w4a16_w8a8_quantize_weights.restype = I
+    L.w4a16_w8a8_quantize_act.argtypes = [P, I64, I64, P, P, P]
+    L.w4a16_w8a8_quantize_act.restype = I
+    L.w4a16_w8a8_workspace_bytes.argtypes = [I64, I64, I64]
+    L.w4a16_w8a8_workspace_bytes.restype = SZ
+    L.w4a16_w8a8_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, P, SZ, P]
+    L.w4a16_w8a8_gemm.restype = I
     L.w4a16_auto_path.restype = I
     _lib = L
     return L
@@ -239,6 +251,53 @@ def w4a16_kv_attention(q, cache, block_table, lengths, bits: int, kv_heads: int,
                                     _dev_ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                     _stream(stream, q.device)))
     return out
+
+
+def w4a16_w8a8_packed_bytes(K: int, N: int) -> int:
+    return int(lib().w4a16_w8a8_packed_bytes(K, N))
+
+
+def w4a16_w8a8_quantize_weights(W, stream=None):
+    """fp16 W [K][N] (device) -> (packed uint8 [K*N], w_scales float32 [N]). Asynchronous."""
+    import torch
+    K, N = W.shape
+    packed = torch.empty(max(w4a16_w8a8_packed_bytes(K, N), 1), dtype=torch.uint8, device=W.device)
+    ws = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib().w4a16_w8a8_quantize_weights(_dev_ptr(W, torch.float16, "W"), K, N, packed.data_ptr(),
+                                             ws.data_ptr(), _stream(stream, W.device)))
+    return packed, ws
+
+
+def w4a16_w8a8_quantize_act(X, stream=None):
+    """fp16 X [M][K] (device) -> (xq int8 [M][K], x_scales float32 [M]). Asynchronous."""
+    import torch
+    M, K = X.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    xs = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(lib().w4a16_w8a8_quantize_act(_dev_ptr(X, torch.float16, "X"), M, K, xq.data_ptr(), xs.data_ptr(),
+                                         _stream(stream, X.device)))
+    return xq, xs
+
+
+def w4a16_w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().w4a16_w8a8_workspace_bytes(M, N, K))
+
+
+def w4a16_w8a8_gemm(xq, x_scales, packed, w_scales, N: int, Y=None, workspace=None, stream=None):
+    """Y fp16 [M][N] from int8 activation codes and packed int8 weights. Asynchronous."""
+    import torch
+    M, K = xq.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=xq.device)
+    need = w4a16_w8a8_workspace_bytes(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xq.device)
+    wptr = _dev_ptr(workspace, None, "workspace") if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().w4a16_w8a8_gemm(_dev_ptr(xq, torch.int8, "xq"), _dev_ptr(x_scales, torch.float32, "x_scales"),
+                                 _dev_ptr(packed, torch.uint8, "packed"), _dev_ptr(w_scales, torch.float32, "w_scales"),
+                                 M, N, K, _dev_ptr(Y, torch.float16, "Y"), wptr, wbytes, _stream(stream, xq.device)))
+    return Y
 
 
 def w4a16_unpack(packed, K: int, N: int, G: int, stream=None):

@@ -342,6 +342,83 @@ int w4a16_kv_attention(const uint16_t *q, const void *cache, int64_t num_blocks,
     return W4A16_OK;
 }
 
+// ------------------------------------------------------------- W8A8
+static bool w8a8_shape_ok(int64_t K, int64_t N) {
+    return K > 0 && N > 0 && K % 256 == 0 && N % 16 == 0 && K <= (1 << 17) && N <= kMaxKN &&
+           K * N <= (int64_t)0xFFFFFFFF;
+}
+
+static int w8a8_check_shape(int64_t K, int64_t N) {
+    if (!w8a8_shape_ok(K, N))
+        return fail(W4A16_ERR_SHAPE,
+                    "unsupported W8A8 shape K=%lld N=%lld (need K %% 256 == 0, K <= 131072, N %% 16 == 0, "
+                    "K * N < 2^32)",
+                    (long long)K, (long long)N);
+    return W4A16_OK;
+}
+
+size_t w4a16_w8a8_packed_bytes(int64_t K, int64_t N) { return w8a8_shape_ok(K, N) ? (size_t)(K * N) : 0; }
+
+int w4a16_w8a8_quantize_weights(const uint16_t *W, int64_t K, int64_t N, void *packed, float *w_scales,
+                                void *stream) {
+    if (!W || !packed || !w_scales) return fail(W4A16_ERR_NULL, "W, packed and w_scales must be non-NULL");
+    int rc = w8a8_check_shape(K, N);
+    if (rc) return rc;
+    if (!aligned16(W) || !aligned16(packed) || !aligned16(w_scales))
+        return fail(W4A16_ERR_ALIGN, "W, packed and w_scales must be 16-byte aligned");
+    hipError_t e = w4a16::launch_w8a8_quant_weights(W, (int)K, (int)N, (uint8_t *)packed, w_scales,
+                                                    (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "W8A8 weight quantization launch");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
+int w4a16_w8a8_quantize_act(const uint16_t *X, int64_t M, int64_t K, int8_t *xq, float *x_scales, void *stream) {
+    if (!X || !xq || !x_scales) return fail(W4A16_ERR_NULL, "X, xq and x_scales must be non-NULL");
+    if (M < 1 || M > kMaxDim) return fail(W4A16_ERR_SHAPE, "M=%lld out of range", (long long)M);
+    int rc = w8a8_check_shape(K, 16);
+    if (rc) return rc;
+    if (!aligned16(X) || !aligned16(xq) || !aligned16(x_scales))
+        return fail(W4A16_ERR_ALIGN, "X, xq and x_scales must be 16-byte aligned");
+    hipError_t e = w4a16::launch_w8a8_quant_act(X, (int)M, (int)K, xq, x_scales, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "W8A8 activation quantization launch");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
+size_t w4a16_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > kMaxDim || !w8a8_shape_ok(K, N)) return 0;
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        int v = 0;
+        if (device_cus(dev, &v) == W4A16_OK) cus = v;
+    }
+    return w4a16::w8a8_workspace_bytes((int)M, (int)N, (int)K, cus);
+}
+
+int w4a16_w8a8_gemm(const int8_t *xq, const float *x_scales, const void *packed, const float *w_scales, int64_t M,
+                    int64_t N, int64_t K, uint16_t *Y, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!xq || !x_scales || !packed || !w_scales || !Y)
+        return fail(W4A16_ERR_NULL, "xq, x_scales, packed, w_scales and Y must be non-NULL");
+    if (M < 1 || M > kMaxDim) return fail(W4A16_ERR_SHAPE, "M=%lld out of range", (long long)M);
+    int rc = w8a8_check_shape(K, N);
+    if (rc) return rc;
+    if (!aligned16(xq) || !aligned16(packed) || !aligned16(Y) || !aligned16(x_scales) || !aligned16(w_scales))
+        return fail(W4A16_ERR_ALIGN, "xq, x_scales, packed, w_scales and Y must be 16-byte aligned");
+    int dev, cus;
+    if ((rc = current_device(&dev))) return rc;
+    if ((rc = device_cus(dev, &cus))) return rc;
+    const size_t need = w4a16::w8a8_workspace_bytes((int)M, (int)N, (int)K, cus);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(W4A16_ERR_WORKSPACE, "W8A8 GEMM needs a workspace of %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    hipError_t e = w4a16::launch_w8a8_gemm(xq, x_scales, (const uint8_t *)packed, w_scales, (int)M, (int)N, (int)K,
+                                           Y, workspace, cus, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "W8A8 GEMM launch");
+    g_last_error[0] = 0;
+    return W4A16_OK;
+}
+
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits) {
     if (M < 1 || M > kMaxDim || !shape_ok(K, N, G)) return 0;
     // The plan depends on the device's CU count; size for the current device

@@ -38,6 +38,14 @@ hipError_t launch_kv_attention(const uint16_t *q, const uint8_t *cache, const in
                                const int32_t *lengths, int B, int Hq, int Hkv, int bits, int64_t num_blocks,
                                float sm_scale, uint16_t *out, void *workspace, int num_cus, hipStream_t stream);
 
+// W8A8 GEMM: int8 codes (symmetric, per token / per output channel) on the
+// int8 matrix cores.
+size_t w8a8_workspace_bytes(int M, int N, int K, int num_cus);
+hipError_t launch_w8a8_quant_act(const uint16_t *X, int M, int K, int8_t *xq, float *xs, hipStream_t stream);
+hipError_t launch_w8a8_quant_weights(const uint16_t *W, int K, int N, uint8_t *packed, float *ws, hipStream_t stream);
+hipError_t launch_w8a8_gemm(const int8_t *xq, const float *xs, const uint8_t *packed, const float *ws, int M, int N,
+                            int K, uint16_t *Y, void *workspace, int num_cus, hipStream_t stream);
+
 // Decode path (M <= 64): one 16-column strip per workgroup, waves split K,
 // MFMA with M padded to 16; optional split of K across workgroups (narrow N)
 // with fp32 partials in a workspace and a second reduce kernel.

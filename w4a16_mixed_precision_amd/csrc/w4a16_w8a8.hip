@@ -1,0 +1,360 @@
+// W8A8 GEMM: 8-bit weights times 8-bit activations on the int8 matrix
+// cores, the precision format the pages list beside W4A16 ("LMDeploy
+// Guide: Fast Mixed-Precision LLM Inference Engine", the two pillars and the
+// table of quantization formats; SmoothQuant named among the post-training
+// methods; the interview notes on the PyTorch engine's w8a8 quantization).
+//
+// Reading (no formula on the pages): symmetric scales, one per output
+// channel for the weights (offline) and one per token for the activations
+// (per call): s = max|v| / 127 in float32 (1 for an all-zero vector),
+// code = clamp(rint(v * (1 / s)), -127, 127) with the exact product of the
+// fp16 value and the float32 reciprocal rounded once (ties to even).
+// Y[m][n] = fp16(float32(float32(acc) * s_x[m]) * s_w[n]) with acc the exact
+// int32 sum of code products.
+//
+// Packed weights: K * N bytes in 1 KiB tiles of 16 columns x 64 rows of K,
+// strip-major (tile (n / 16) * (K / 64) + k / 64); in a tile, lane
+// l = 16 * ((k % 64) / 16) + n % 16 holds the 16 codes k % 16 = 0..15 of its
+// column, the B operand of one v_mfma_i32_16x16x64_i8 step. The activation
+// operand takes the same 16 consecutive k per lane group, so A and B agree
+// on every k (whatever order the instruction sums them in).
+//
+// GEMM: workgroup tile BM x 256 (four waves side by side, each 64 columns);
+// the BM x 256-byte tile of codes of X for the next 256 rows of K is copied
+// global -> LDS by direct 16-byte loads (XOR-swizzled by row, two stages)
+// while the current one is multiplied; each wave streams its packed weight
+// tiles into registers one block ahead. Split-K writes int32 partials that
+// a second kernel adds (exactly) and scales.
+#include <stdlib.h>
+
+#include "w4a16_device.h"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+constexpr float kRoundMagic = 12582912.0f;         // 1.5 * 2^23
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;
+constexpr int kW8Tile = 1024;   // 16 columns x 64 k
+constexpr int kW8Block = 256;   // rows of K per pipeline stage (4 MFMA steps)
+
+// code of v with reciprocal inv: rint of the exact product, clamped to
+// [-127, 127] (adding 1.5 * 2^23 rounds once; the clamp keeps the result in
+// that binade, whose bit pattern is bits(1.5 * 2^23) + code)
+__device__ inline int code8(float v, float inv) {
+    const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(v, inv, kRoundMagic), kRoundMagic - 127.f,
+                                            kRoundMagic + 127.f);
+    return (int)(__builtin_bit_cast(uint32_t, y) - kRoundMagicBits);
+}
+
+__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// fp16(float32(float32(acc) * sx) * sw), every product rounded to float32
+// first: the empty asm keeps the compiler from fusing the last product with
+// the conversion into one mixed-precision instruction (a single rounding
+// straight to fp16, which can differ by one fp16 step)
+__device__ inline uint16_t scale_out(int32_t acc, float sx, float sw) {
+    float y = ((float)acc * sx) * sw;
+    asm volatile("" : "+v"(y));
+    return f32_to_f16_bits(y);
+}
+
+// ------------------------------------------------------------ activations
+// One workgroup of 256 threads per token (row); 8 values per thread per
+// 16-byte load. K % 256 == 0.
+__global__ void __launch_bounds__(256)
+w8a8_quant_act_kernel(const uint16_t *__restrict__ X, int K, int8_t *__restrict__ xq, float *__restrict__ xs) {
+    __shared__ float red[4];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const uint16_t *row = X + (size_t)m * K;
+    float amax = 0.f;
+    for (int k = tid * 8; k < K; k += 256 * 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f((uint16_t)(v[d] & 0xFFFF))));
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f((uint16_t)(v[d] >> 16))));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    const float s = amax > 0.f ? amax / 127.0f : 1.0f;
+    const float inv = 1.0f / s;
+    if (tid == 0) xs[m] = s;
+    int8_t *out = xq + (size_t)m * K;
+    for (int k = tid * 8; k < K; k += 256 * 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t c0 = (uint32_t)code8(h2f((uint16_t)(v[d] & 0xFFFF)), inv) & 0xFFu;
+            const uint32_t c1 = (uint32_t)code8(h2f((uint16_t)(v[d] >> 16)), inv) & 0xFFu;
+            const uint32_t pair = c0 | (c1 << 8);
+            if (d < 2)
+                lo |= pair << (16 * d);
+            else
+                hi |= pair << (16 * (d - 2));
+        }
+        *reinterpret_cast<uint2 *>(out + k) = make_uint2(lo, hi);
+    }
+}
+
+// ------------------------------------------------------------ weights
+// Per-column maxima: one thread per column, rows in order.
+__global__ void __launch_bounds__(256)
+w8a8_weight_scale_kernel(const uint16_t *__restrict__ W, int K, int N, float *__restrict__ ws) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    float amax = 0.f;
+    for (int k = 0; k < K; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f(W[(size_t)k * N + n])));
+    ws[n] = amax > 0.f ? amax / 127.0f : 1.0f;
+}
+
+// One thread per 16-byte lane slot of a packed tile.
+__global__ void __launch_bounds__(256)
+w8a8_weight_pack_kernel(const uint16_t *__restrict__ W, int K, int N, const float *__restrict__ ws,
+                        u32x4 *__restrict__ out) {
+    const int64_t slots = (int64_t)K * N / 16;
+    const int kt = K / 64;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < slots;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int lane = (int)(idx & 63);
+        const int64_t tile = idx >> 6;
+        const int strip = (int)(tile / kt), kb = (int)(tile % kt);
+        const int n = strip * 16 + (lane & 15);
+        const int k0 = kb * 64 + 16 * (lane >> 4);
+        const float inv = 1.0f / ws[n];
+        u32x4 v;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int c = code8(h2f(W[(size_t)(k0 + 4 * d + b) * N + n]), inv);
+                word |= ((uint32_t)c & 0xFFu) << (8 * b);
+            }
+            v[d] = word;
+        }
+        out[idx] = v;
+    }
+}
+
+// ------------------------------------------------------------ GEMM
+template <int MTW, int NSW, int OCC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, const uint8_t *__restrict__ packed,
+                 const float *__restrict__ ws, uint16_t *__restrict__ Y, int32_t *__restrict__ part, int M, int N,
+                 int K, int tiles_m, int S, int slice_blocks) {
+    constexpr int WAVES = 4;
+    constexpr int BM = MTW * 16;
+    constexpr int STAGE = BM * kW8Block;         // bytes of X per stage
+    constexpr int XLOADS = BM * 16 / 256;         // 16-byte copies per thread per stage
+    static_assert(XLOADS >= 1 && BM * 16 % 256 == 0, "X tile must split over the threads");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, kq = lane >> 4;
+    const int nblk = K / kW8Block;
+    const int nstrip = N / 16;
+    const int tile = blockIdx.x;
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int split = blockIdx.y;
+    const int bb = split * slice_blocks;
+    const int be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
+    const int m0 = tm * BM;
+    const int strip_w = (tn * WAVES + wave) * NSW;
+
+    // X copies: copy i of this thread moves row r0(i) + lane / 16 of the
+    // tile, r0(i) = 4 (i WAVES + wave), source chunk (lane & 15) ^ (row & 15)
+    // to LDS position lane: LDS row r holds chunk p ^ (r & 15) at p. Rows at
+    // or past M read zeros (one descriptor per copy, ending at row M).
+    const int rows_here = M - m0 < BM ? M - m0 : BM;
+    __amdgpu_buffer_rsrc_t rx[XLOADS];
+#pragma unroll
+    for (int i = 0; i < XLOADS; ++i) {
+        const int r0 = 4 * (i * WAVES + wave);
+        const int nrows = rows_here - r0 > 0 ? rows_here - r0 : 0;
+        rx[i] = make_rsrc(X + (size_t)(m0 + (r0 < rows_here ? r0 : 0)) * K, (uint32_t)((size_t)nrows * K));
+    }
+    const int xrow = lane >> 4;
+    const uint32_t xoff = (uint32_t)(xrow * K + (((lane & 15) ^ ((4 * wave + xrow) & 15)) * 16));
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed, (uint32_t)((size_t)K * N));
+    int sstrip[NSW];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) sstrip[j] = strip_w + j < nstrip ? strip_w + j : nstrip - 1;
+
+    auto issue_x = [&](int b, int stage) {
+#pragma unroll
+        for (int i = 0; i < XLOADS; ++i) {
+            const __amdgpu_buffer_rsrc_t r = rx[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void *)(lds + stage * STAGE + (i * WAVES + wave) * 1024), 16, xoff, b * kW8Block, 0, 0);
+        }
+    };
+    typedef u32x4 WBlk[NSW][4];
+    auto load_w = [&](int b, WBlk &w) {
+#pragma unroll
+        for (int j = 0; j < NSW; ++j)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                w[j][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rw, lane * 16u, ((size_t)sstrip[j] * (K / 64) + 4 * b + s) * kW8Tile, 0));
+    };
+
+    int32x4 acc[MTW][NSW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int j = 0; j < NSW; ++j) acc[mt][j] = int32x4{0, 0, 0, 0};
+
+    auto compute = [&](int stage, const WBlk &w) {
+        const uint8_t *st = lds + stage * STAGE;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            int32x4 a[MTW];
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+                a[mt] = *reinterpret_cast<const int32x4 *>(st + (mt * 16 + col) * kW8Block + (((4 * s + kq) ^ col) * 16));
+#pragma unroll
+            for (int j = 0; j < NSW; ++j) {
+                const int32x4 bq = __builtin_bit_cast(int32x4, w[j][s]);
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt)
+                    acc[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt], bq, acc[mt][j], 0, 0, 0);
+            }
+        }
+    };
+
+    if (bb < be) {
+        WBlk wc, wn;
+        issue_x(bb, 0);
+        load_w(bb, wc);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int b = bb; b < be; ++b) {
+            const int cur = (b - bb) & 1;
+            if (b + 1 < be) {
+                issue_x(b + 1, cur ^ 1);
+                load_w(b + 1, wn);
+            }
+            compute(cur, wc);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NSW; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) wc[j][s] = wn[j][s];
+        }
+    }
+
+    // epilogue: exact int32 sums -> fp16 with the two scales, or partials
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int j = 0; j < NSW; ++j) {
+            const int sj = strip_w + j;
+            if (sj >= nstrip) continue;
+            const int n = sj * 16 + col;
+            const float swn = S == 1 ? ws[n] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + mt * 16 + 4 * kq + e;
+                if (row >= M) continue;
+                if (S == 1)
+                    Y[(size_t)row * N + n] = scale_out(acc[mt][j][e], xs[row], swn);
+                else
+                    part[((size_t)split * M + row) * N + n] = acc[mt][j][e];
+            }
+        }
+}
+
+__global__ void __launch_bounds__(256)
+w8a8_reduce_kernel(const int32_t *__restrict__ part, const float *__restrict__ xs, const float *__restrict__ ws,
+                   uint16_t *__restrict__ Y, int M, int N, int S) {
+    const int64_t MN = (int64_t)M * N;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < MN; i += (int64_t)gridDim.x * blockDim.x) {
+        int32_t a = 0;
+        for (int s = 0; s < S; ++s) a += part[(size_t)s * MN + i];
+        const int m = (int)(i / N), n = (int)(i % N);
+        Y[i] = scale_out(a, xs[m], ws[n]);
+    }
+}
+
+inline unsigned grid_for(int64_t items) {
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return (unsigned)(blocks < 1 ? 1 : blocks);
+}
+
+struct W8Plan {
+    int big;  // 1: 64-row tiles, 0: 16-row tiles
+    int splits, slice_blocks;
+};
+
+// 16-row tiles up to M = 16, 64-row tiles above; split K until the tiles
+// times splits fill the GPU's resident slots (eight waves per CU), keeping
+// at least two blocks of K per split.
+W8Plan w8_plan(int M, int N, int K, int num_cus) {
+    W8Plan p;
+    p.big = M > 16;
+    if (const char *e = getenv("W4A16_W8A8_TILE")) p.big = atoi(e) == 64;
+    const int BM = p.big ? 64 : 16;
+    const int tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
+    const int nblk = K / kW8Block;
+    const int slots = num_cus * 2;  // two 4-wave workgroups per CU
+    int s = tiles >= slots ? 1 : slots / tiles;
+    const int cap = nblk / 2 > 1 ? nblk / 2 : 1;
+    if (s > cap) s = cap;
+    const int sb = (nblk + s - 1) / s;
+    p.slice_blocks = sb;
+    p.splits = (nblk + sb - 1) / sb;
+    return p;
+}
+
+}  // namespace
+
+size_t w8a8_workspace_bytes(int M, int N, int K, int num_cus) {
+    const W8Plan p = w8_plan(M, N, K, num_cus);
+    return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(int32_t) : 0;
+}
+
+hipError_t launch_w8a8_quant_act(const uint16_t *X, int M, int K, int8_t *xq, float *xs, hipStream_t stream) {
+    hipLaunchKernelGGL(w8a8_quant_act_kernel, dim3((unsigned)M), dim3(256), 0, stream, X, K, xq, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a8_quant_weights(const uint16_t *W, int K, int N, uint8_t *packed, float *ws, hipStream_t stream) {
+    hipLaunchKernelGGL(w8a8_weight_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, W, K, N, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(w8a8_weight_pack_kernel, dim3(grid_for((int64_t)K * N / 16)), dim3(256), 0, stream, W, K, N,
+                       ws, reinterpret_cast<u32x4 *>(packed));
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a8_gemm(const int8_t *xq, const float *xs, const uint8_t *packed, const float *ws, int M, int N,
+                            int K, uint16_t *Y, void *workspace, int num_cus, hipStream_t stream) {
+    const W8Plan p = w8_plan(M, N, K, num_cus);
+    int32_t *part = p.splits > 1 ? static_cast<int32_t *>(workspace) : nullptr;
+    const int BM = p.big ? 64 : 16;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + 255) / 256;
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.splits);
+    if (p.big)
+        hipLaunchKernelGGL((w8a8_gemm_kernel<4, 4, 2>), grid, dim3(256), 0, stream, xq, xs, packed, ws, Y, part, M, N,
+                           K, tiles_m, p.splits, p.slice_blocks);
+    else
+        hipLaunchKernelGGL((w8a8_gemm_kernel<1, 4, 2>), grid, dim3(256), 0, stream, xq, xs, packed, ws, Y, part, M, N,
+                           K, tiles_m, p.splits, p.slice_blocks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits <= 1) return e;
+    hipLaunchKernelGGL(w8a8_reduce_kernel, dim3(grid_for((int64_t)M * N)), dim3(256), 0, stream, part, xs, ws, Y, M,
+                       N, p.splits);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16
