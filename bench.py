@@ -66,6 +66,8 @@ def parse_args(argv=None):
     p.add_argument("--detail", action="store_true", help="per-instance lines to stderr")
     p.add_argument("--quantizer-only", action="store_true",
                    help="time only the offline quantizer (fp16 W -> packed) and print its line")
+    p.add_argument("--w8a8-only", action="store_true",
+                   help="time only the W8A8 GEMM legs and print their lines")
     p.add_argument("--kv-only", action="store_true",
                    help="time only the low-bit KV cache decode attention (int8 and int4) and print its lines")
     return p.parse_args(argv)
@@ -365,6 +367,59 @@ def run_kv_secondary(args, bits, reps=20):
     }
 
 
+def run_w8a8_secondary(args, reps=20):
+    """W8A8 GEMM (int8 codes on the int8 matrix cores) on Llama-3-8B shapes:
+    the QKV decode block (M=16, K=4096, N=6144; weight copies rotated so
+    every call reads HBM; bytes = int8 weights + scales + codes of X + Y)
+    and the prefill gate/up (M=2048, K=4096, N=28672; ops = 2 M N K). Per
+    call: activation quantization + GEMM, eager calls, HIP events."""
+    import math
+
+    import torch
+
+    import w4a16_mixed_precision_amd as w4
+    out = []
+    for M, K, N, what in ((16, 4096, 6144, "decode qkv"), (2048, 4096, 28672, "prefill gate_up")):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(M)
+        W = (torch.randn((K, N), generator=gen, device="cuda", dtype=torch.float32) * 0.02).half()
+        X = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).half()
+        wbytes = K * N
+        copies = max(1, int(math.ceil(args.rotate_gib * 2 ** 30 / wbytes))) if M <= 64 else 1
+        packs = [w4.w4a16_w8a8_quantize_weights(W) for _ in range(copies)]
+        del W
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        need = w4.w4a16_w8a8_workspace_bytes(M, N, K)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        for p, s in packs:
+            xq, xs = w4.w4a16_w8a8_quantize_act(X)
+            w4.w4a16_w8a8_gemm(xq, xs, p, s, N, Y=Y, workspace=ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for p, s in packs:
+                xq, xs = w4.w4a16_w8a8_quantize_act(X)
+                w4.w4a16_w8a8_gemm(xq, xs, p, s, N, Y=Y, workspace=ws)
+        b.record()
+        b.synchronize()
+        us = a.elapsed_time(b) / (reps * copies) * 1e3
+        nbytes = K * N + 4 * N + M * K + 4 * M + 2 * M * N
+        ops = 2 * M * N * K
+        out.append({
+            "metric": f"W8A8 GEMM {what} (M={M}, K={K}, N={N}), activation quantization + GEMM per call",
+            "us_per_call": us,
+            "GBps": nbytes / (us * 1e-6) / 1e9,
+            "TOPs": ops / (us * 1e-6) / 1e12,
+            "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "frac_of_int8_mfma_peak": ops / (us * 1e-6) / 1e12 / 5000.0,
+            "rotation_copies": copies,
+        })
+        del packs, ws, X, Y
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -382,6 +437,10 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.quantizer_only:
         print(json.dumps(run_quantize_secondary(args)), flush=True)
+        return 0
+    if args.w8a8_only:
+        for line in run_w8a8_secondary(args):
+            print(json.dumps(line), flush=True)
         return 0
     if args.kv_only:
         for bits in (8, 4):
@@ -473,6 +532,7 @@ def main(argv=None):
         out["secondary"] = run_prefill_secondary(args)
         out["quantizer"] = run_quantize_secondary(args)
         out["kv_attention"] = [run_kv_secondary(args, 8), run_kv_secondary(args, 4)]
+        out["w8a8"] = run_w8a8_secondary(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(runner)
     print(json.dumps(out), flush=True)
