@@ -23,7 +23,7 @@
 // the BM x 256-byte tile of codes of X for the next 256 rows of K is copied
 // global -> LDS by direct 16-byte loads (XOR-swizzled by row, two stages)
 // while the current one is multiplied; each wave streams its packed weight
-// tiles into registers one block ahead. Split-K writes int32 partials that
+// tiles into registers half a block (two 64-row steps) ahead. Split-K writes int32 partials that
 // a second kernel adds (exactly) and scales.
 #include <stdlib.h>
 
@@ -196,14 +196,16 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
                 r, (lds_void *)(lds + stage * STAGE + (i * WAVES + wave) * 1024), 16, xoff, b * kW8Block, 0, 0);
         }
     };
-    typedef u32x4 WBlk[NSW][4];
-    auto load_w = [&](int b, WBlk &w) {
+    // packed weights in half blocks (two 64-row steps): the next half is in
+    // flight while the current one is multiplied
+    typedef u32x4 WHalf[NSW][2];
+    auto load_w = [&](int h, WHalf &w) {  // half block h = 2 * block + (0 or 1)
 #pragma unroll
         for (int j = 0; j < NSW; ++j)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < 2; ++s)
                 w[j][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        rw, lane * 16u, ((size_t)sstrip[j] * (K / 64) + 4 * b + s) * kW8Tile, 0));
+                                                        rw, lane * 16u, ((size_t)sstrip[j] * (K / 64) + 2 * h + s) * kW8Tile, 0));
     };
 
     int32x4 acc[MTW][NSW];
@@ -212,17 +214,18 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
 #pragma unroll
         for (int j = 0; j < NSW; ++j) acc[mt][j] = int32x4{0, 0, 0, 0};
 
-    auto compute = [&](int stage, const WBlk &w) {
+    auto compute = [&](int stage, int half, const WHalf &w) {
         const uint8_t *st = lds + stage * STAGE;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * half + s2;
             int32x4 a[MTW];
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt)
                 a[mt] = *reinterpret_cast<const int32x4 *>(st + (mt * 16 + col) * kW8Block + (((4 * s + kq) ^ col) * 16));
 #pragma unroll
             for (int j = 0; j < NSW; ++j) {
-                const int32x4 bq = __builtin_bit_cast(int32x4, w[j][s]);
+                const int32x4 bq = __builtin_bit_cast(int32x4, w[j][s2]);
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt)
                     acc[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt], bq, acc[mt][j], 0, 0, 0);
@@ -231,24 +234,20 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
     };
 
     if (bb < be) {
-        WBlk wc, wn;
+        WHalf w0, w1;
         issue_x(bb, 0);
-        load_w(bb, wc);
+        load_w(2 * bb, w0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int b = bb; b < be; ++b) {
             const int cur = (b - bb) & 1;
-            if (b + 1 < be) {
-                issue_x(b + 1, cur ^ 1);
-                load_w(b + 1, wn);
-            }
-            compute(cur, wc);
+            if (b + 1 < be) issue_x(b + 1, cur ^ 1);
+            load_w(2 * b + 1, w1);
+            compute(cur, 0, w0);
+            if (b + 1 < be) load_w(2 * b + 2, w0);
+            compute(cur, 1, w1);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-#pragma unroll
-            for (int j = 0; j < NSW; ++j)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) wc[j][s] = wn[j][s];
         }
     }
 
@@ -292,18 +291,23 @@ inline unsigned grid_for(int64_t items) {
 }
 
 struct W8Plan {
-    int big;  // 1: 64-row tiles, 0: 16-row tiles
+    int bm;  // workgroup rows: 16 or 64
     int splits, slice_blocks;
 };
 
-// 16-row tiles up to M = 16, 64-row tiles above; split K until the tiles
-// times splits fill the GPU's resident slots (eight waves per CU), keeping
-// at least two blocks of K per split.
+// 16-row tiles up to M = 16, 64-row tiles above (128-row tiles need one
+// wave per SIMD for their registers and measured slower: 416 against 367 us
+// at 2048 x 4096 x 28672); split K until the tiles times splits fill the
+// GPU's resident slots (two 4-wave workgroups per CU), keeping at least two
+// blocks of K per split.
 W8Plan w8_plan(int M, int N, int K, int num_cus) {
     W8Plan p;
-    p.big = M > 16;
-    if (const char *e = getenv("W4A16_W8A8_TILE")) p.big = atoi(e) == 64;
-    const int BM = p.big ? 64 : 16;
+    p.bm = M <= 16 ? 16 : 64;
+    if (const char *e = getenv("W4A16_W8A8_TILE")) {
+        const int v = atoi(e);
+        if (v == 16 || v == 64) p.bm = v;
+    }
+    const int BM = p.bm;
     const int tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
     const int nblk = K / kW8Block;
     const int slots = num_cus * 2;  // two 4-wave workgroups per CU
@@ -341,10 +345,9 @@ hipError_t launch_w8a8_gemm(const int8_t *xq, const float *xs, const uint8_t *pa
                             int K, uint16_t *Y, void *workspace, int num_cus, hipStream_t stream) {
     const W8Plan p = w8_plan(M, N, K, num_cus);
     int32_t *part = p.splits > 1 ? static_cast<int32_t *>(workspace) : nullptr;
-    const int BM = p.big ? 64 : 16;
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + 255) / 256;
+    const int tiles_m = (M + p.bm - 1) / p.bm, tiles_n = (N + 255) / 256;
     const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.splits);
-    if (p.big)
+    if (p.bm == 64)
         hipLaunchKernelGGL((w8a8_gemm_kernel<4, 4, 2>), grid, dim3(256), 0, stream, xq, xs, packed, ws, Y, part, M, N,
                            K, tiles_m, p.splits, p.slice_blocks);
     else
