@@ -203,10 +203,11 @@ def kernel_name(inst):
     return "decode path"
 
 
-def cpu_baseline(runner, max_macs=4e9, repeats=3):
-    """The CPU oracle timed on the step's GEMMs (median of `repeats` passes).
-    Instances larger than `max_macs` multiply-adds are sampled by their
-    leading columns (a multiple of 16), and the sampled sub-problem's
+def cpu_baseline(runner, max_macs=4e9, min_seconds=10.0, max_passes=200):
+    """The CPU oracle timed on the step's GEMMs: whole passes over the step
+    until at least `min_seconds` of CPU work (at least three passes), median
+    pass time. Instances larger than `max_macs` multiply-adds are sampled by
+    their leading columns (a multiple of 16), and the sampled sub-problem's
     algorithmic bytes are credited."""
     import dataclasses
 
@@ -214,7 +215,8 @@ def cpu_baseline(runner, max_macs=4e9, repeats=3):
     oracle.load()
     cores = oracle.max_threads()
     times, b_total, sampled = [], 0, []
-    for rep in range(repeats):
+    rep = 0
+    while rep < max_passes and (rep < 3 or sum(times) < min_seconds):
         t_total = 0.0
         for inst in runner.insts:
             X, q, z, s = runner.host[inst.name]
@@ -229,6 +231,8 @@ def cpu_baseline(runner, max_macs=4e9, repeats=3):
             if rep == 0:
                 b_total += dataclasses.replace(inst, N=cols).alg_bytes()
         times.append(t_total)
+        rep += 1
+    repeats = len(times)
     t = sorted(times)[len(times) // 2]
     what = f"one step ({len(runner.insts)} GEMMs)"
     if sampled:
@@ -238,7 +242,8 @@ def cpu_baseline(runner, max_macs=4e9, repeats=3):
         "unit": "TB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{what}, float64 C oracle, median of {repeats} passes, {t:.2f} s per pass",
+        "sample": f"{what}, float64 C oracle, median of {repeats} passes ({sum(times):.1f} s in all), "
+                  f"{t:.2f} s per pass",
     }
 
 

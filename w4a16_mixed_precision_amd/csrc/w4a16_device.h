@@ -131,6 +131,15 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 <
 // s_waitcnt immediate that waits for all LDS (and scalar memory) operations
 constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 
+// Rounding to an integer in float32: adding 1.5 * 2^23 rounds any |x| <
+// 2^22 to the nearest integer (ties to even) and lands in the binade
+// [2^23, 2^24), whose bit pattern is kRoundMagicBits + that integer; a fused
+// multiply-add with it rounds an exact product once. Used by the quantizers.
+constexpr float kRoundMagic = 12582912.0f;         // 1.5 * 2^23
+constexpr uint32_t kRoundMagicBits = 0x4B400000u;  // its bit pattern
+// Smallest normal fp16 (2^-14): the floor of the quantizers' scales.
+constexpr float kScaleFloor = 6.103515625e-05f;
+
 // A raw buffer load whose offset reaches past the descriptor's byte count
 // returns zeros and makes no memory request. Kernels point loads they do not
 // need at this offset instead of branching around them, so every path

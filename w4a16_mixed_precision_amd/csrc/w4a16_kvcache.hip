@@ -54,9 +54,6 @@ namespace {
 constexpr int kHD = 128;    // head dimension
 constexpr int kBS = 64;     // tokens per cache block
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRoundMagic = 12582912.0f;         // 1.5 * 2^23
-constexpr uint32_t kRoundMagicBits = 0x4B400000u;
-constexpr float kScaleFloor = 6.103515625e-05f;    // 2^-14
 
 template <int BITS>
 struct KvGeom {

@@ -42,9 +42,6 @@ namespace w4a16 {
 namespace {
 
 constexpr int kQThreads = 256;
-constexpr float kRoundMagic = 12582912.0f;         // 1.5 * 2^23
-constexpr uint32_t kRoundMagicBits = 0x4B400000u;  // its bit pattern
-constexpr float kScaleFloor = 6.103515625e-05f;    // 2^-14, the smallest normal fp16
 
 // Per (group, column) parameters of the code decision.
 struct QParams {

@@ -34,8 +34,6 @@ namespace w4a16 {
 namespace {
 
 typedef int int32x4 __attribute__((ext_vector_type(4)));
-constexpr float kRoundMagic = 12582912.0f;         // 1.5 * 2^23
-constexpr uint32_t kRoundMagicBits = 0x4B400000u;
 constexpr int kW8Tile = 1024;   // 16 columns x 64 k
 constexpr int kW8Block = 256;   // rows of K per pipeline stage (4 MFMA steps)
 
