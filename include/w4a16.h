@@ -253,7 +253,8 @@ size_t w4a16_kv_attention_workspace_bytes(int64_t B, int64_t kv_heads, int64_t m
  *   workspace    at least w4a16_kv_attention_workspace_bytes(B, kv_heads,
  *                max_blocks) bytes of device memory (any contents)
  * q_heads must be a multiple of kv_heads, at most 16 query heads per KV
- * head. Asynchronous on `stream`; calls sharing a workspace must be ordered.
+ * head; max_blocks <= 2^24, B * kv_heads <= 2^26, B * q_heads <= 2^30.
+ * Asynchronous on `stream`; calls sharing a workspace must be ordered.
  */
 int w4a16_kv_attention(const uint16_t *q, const void *cache, int64_t num_blocks,
                        const int32_t *block_table, int64_t max_blocks, const int32_t *lengths,

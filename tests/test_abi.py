@@ -129,6 +129,9 @@ def test_kv_and_w8a8_validation_before_any_hip_call():
     args = lambda hq, hkv: L.w4a16_kv_attention(FAKE, FAKE, 1, FAKE, 1, FAKE, 1, hq, hkv, 8,
                                                  ctypes.c_float(0.1), FAKE, FAKE, 1 << 20, None)
     assert args(12, 8) == w4.W4A16_ERR_SHAPE and args(17, 1) == w4.W4A16_ERR_SHAPE
+    big = L.w4a16_kv_attention(FAKE, FAKE, 1, FAKE, (1 << 24) + 1, FAKE, 1, 8, 8, 8, ctypes.c_float(0.1),
+                               FAKE, FAKE, 1 << 20, None)
+    assert big == w4.W4A16_ERR_SHAPE and w4.w4a16_kv_attention_workspace_bytes(1 << 20, 128, 4) == 0
     assert w4.w4a16_w8a8_packed_bytes(512, 64) == 512 * 64
     assert w4.w4a16_w8a8_packed_bytes(320, 64) == 0 and w4.w4a16_w8a8_packed_bytes(1 << 18, 16) == 0
     assert L.w4a16_w8a8_gemm(FAKE, FAKE, FAKE, FAKE, 1, 64, 320, FAKE, None, 0, None) == w4.W4A16_ERR_SHAPE

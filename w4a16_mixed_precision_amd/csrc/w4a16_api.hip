@@ -300,7 +300,9 @@ int w4a16_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, 
 }
 
 size_t w4a16_kv_attention_workspace_bytes(int64_t B, int64_t kv_heads, int64_t max_blocks) {
-    if (B < 1 || B > kMaxDim || kv_heads < 1 || kv_heads > 65535 || max_blocks < 1 || max_blocks > kMaxDim) return 0;
+    if (B < 1 || B > kMaxDim || kv_heads < 1 || kv_heads > 65535 || max_blocks < 1 || max_blocks > (1 << 24) ||
+        B * kv_heads > (1 << 26))
+        return 0;
     int cus = 256, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
         int v = 0;
@@ -316,9 +318,10 @@ int w4a16_kv_attention(const uint16_t *q, const void *cache, int64_t num_blocks,
     if (!q || !cache || !block_table || !lengths || !out)
         return fail(W4A16_ERR_NULL, "q, cache, block_table, lengths and out must be non-NULL");
     if (bits != 4 && bits != 8) return fail(W4A16_ERR_ARG, "bits must be 4 or 8 (got %d)", bits);
+    // (max_blocks * 64 and the per-(sequence, KV head) work count stay in int)
     if (B < 1 || B > kMaxDim || kv_heads < 1 || kv_heads > 65535 || q_heads < kv_heads ||
-        q_heads % kv_heads != 0 || q_heads / kv_heads > 16 || max_blocks < 1 || max_blocks > kMaxDim ||
-        num_blocks < 1 || B * q_heads > kMaxDim)
+        q_heads % kv_heads != 0 || q_heads / kv_heads > 16 || max_blocks < 1 || max_blocks > (1 << 24) ||
+        num_blocks < 1 || B * q_heads > kMaxDim || B * kv_heads > (1 << 26))
         return fail(W4A16_ERR_SHAPE,
                     "bad KV attention shape B=%lld q_heads=%lld kv_heads=%lld max_blocks=%lld num_blocks=%lld "
                     "(need q_heads a multiple of kv_heads, at most 16 query heads per KV head)",
