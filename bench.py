@@ -333,13 +333,20 @@ def run_kv_secondary(args, bits, reps=20):
     slots = (table[:, :, None] * 64 + torch.arange(64, dtype=torch.int32, device="cuda")).reshape(B, -1)[:, :T]
     slots = slots.reshape(-1).contiguous()
     caches = []
-    for _ in range(copies):
+    append_ms = []
+    for i in range(copies + 1):
         c = torch.empty(cache_bytes, dtype=torch.uint8, device="cuda")
         k = torch.randn((B * T, hkv, D), generator=gen, device="cuda", dtype=torch.float32).half()
         v = torch.randn((B * T, hkv, D), generator=gen, device="cuda", dtype=torch.float32).half()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record()
         w4.w4a16_kv_append(k, v, slots, bits, c)
+        eb.record()
+        eb.synchronize()
+        append_ms.append(ea.elapsed_time(eb))
         del k, v
-        caches.append(c)
+        if i:  # the first fill only warms the append up
+            caches.append(c)
     q = torch.randn((B, hq, D), generator=gen, device="cuda", dtype=torch.float32).half()
     out = torch.empty_like(q)
     lengths = torch.full((B,), T, dtype=torch.int32, device="cuda")
@@ -358,6 +365,9 @@ def run_kv_secondary(args, bits, reps=20):
     calls = reps * copies
     ms = a.elapsed_time(b) / calls
     nbytes = B * hkv * T * (2 * D * bits // 8 + 8) + 2 * q.numel() * 2
+    # append of all B * T tokens: fp16 K and V in, codes and parameters out
+    append_bytes = B * T * hkv * (2 * D * 2) + B * hkv * T * (2 * D * bits // 8 + 8)
+    append = sorted(append_ms[1:])[len(append_ms[1:]) // 2]
     del caches, ws
     torch.cuda.empty_cache()
     return {
@@ -369,6 +379,10 @@ def run_kv_secondary(args, bits, reps=20):
         "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "rotation_copies": copies,
         "timing": "eager calls (attention + chunk merge kernels), HIP events around %d calls" % calls,
+        "append": {"tokens": B * T, "kv_heads": hkv, "us": append * 1e3,
+                   "GBps": append_bytes / (append * 1e-3) / 1e9,
+                   "timing": "one call filling the whole cache, median of %d fills after a warm-up fill"
+                             % (len(append_ms) - 1)},
     }
 
 

@@ -211,12 +211,15 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
  * (b * kv_heads + h) * (w4a16_kv_block_bytes / kv_heads). Inside a region,
  * KC = 64 * 128 * bits / 8:
  *   [0, KC)          K codes, token-major rows of 128 codes
- *   [KC, 2 KC)       V codes, rows d = 0..127 of the 64 tokens at positions
- *                    p(t) = 16 ((t % 16) / 4) + 8 (t / 32) + 4 ((t / 16) % 2) + t % 4
+ *   [KC, 2 KC)       V codes, rows of 64 bytes, token t's byte at position
+ *                    p(t) = 16 ((t % 16) / 4) + 8 (t / 32) + 4 ((t / 16) % 2) + t % 4;
+ *                    8-bit: row d = 0..127 holds dimension d; 4-bit: row
+ *                    r = 0..63 holds dimension r (low nibble) and r + 64
+ *                    (high nibble)
  *   [2 KC, +256)     K parameters, 4 bytes per token: fp16 scale, zero, 0
  *   [2 KC + 256, +256) V parameters
- * 4-bit codes are two per byte, the even index in the low nibble. Token i of
- * a sequence lives in block block_table[b][i / 64] at offset i % 64.
+ * 4-bit K codes are two per byte, the even index in the low nibble. Token i
+ * of a sequence lives in block block_table[b][i / 64] at offset i % 64.
  * ---------------------------------------------------------------------------
  */
 

@@ -34,9 +34,11 @@ of ``head_block_bytes(bits)`` bytes, region (b, kh) at byte
 
 * [0, KC): K codes, token-major: token t's row of 128 codes at t * 128 *
   bits / 8; 4-bit codes two per byte, the even index in the low nibble.
-* [KC, 2 KC): V codes, index-major: row d (0..127) holds the 64 tokens in the
-  position order p(t) = 16 * ((t % 16) // 4) + 8 * (t // 32) + 4 * ((t // 16)
-  % 2) + t % 4 (same packing of 4-bit codes).
+* [KC, 2 KC): V codes, index-major, rows of 64 bytes, one byte per token at
+  position p(t) = 16 * ((t % 16) // 4) + 8 * (t // 32) + 4 * ((t // 16) % 2)
+  + t % 4 of the row. 8-bit: row d (0..127) holds dimension d. 4-bit: row r
+  (0..63) holds dimension r in the low nibble and dimension r + 64 in the
+  high nibble, so that each byte belongs to one token.
 * [2 KC, 2 KC + 256): K parameters, 4 bytes per token: fp16 scale (bytes 0-1),
   zero code (byte 2), byte 3 zero.
 * [2 KC + 256, 2 KC + 512): V parameters, likewise.
@@ -124,13 +126,13 @@ def cache_write(cache, slots, kc, ks, kz, vc, vs, vz, Hkv: int, bits: int):
             cache[base + t * row.size: base + (t + 1) * row.size] = row
             p = int(v_position(t))
             vrow = base + kcb  # V codes region
-            for d in range(HEAD_DIM):
-                if bits == 8:
+            if bits == 8:
+                for d in range(HEAD_DIM):
                     cache[vrow + d * BLOCK + p] = vc[i, h, d]
-                else:
-                    byte = vrow + d * (BLOCK // 2) + p // 2
-                    sh = 4 * (p % 2)
-                    cache[byte] = (cache[byte] & (0xF0 >> sh)) | (int(vc[i, h, d]) << sh)
+            else:
+                half = HEAD_DIM // 2
+                for r in range(half):
+                    cache[vrow + r * BLOCK + p] = int(vc[i, h, r]) | (int(vc[i, h, r + half]) << 4)
             for (arr_s, arr_z, off) in ((ks, kz, 2 * kcb), (vs, vz, 2 * kcb + 4 * BLOCK)):
                 sb = np.array([arr_s[i, h]], np.float16).view(np.uint8)
                 cache[base + off + 4 * t: base + off + 4 * t + 4] = [sb[0], sb[1], arr_z[i, h], 0]
@@ -154,9 +156,9 @@ def cache_read(cache, block_table_row, length: int, Hkv: int, bits: int):
         for h in range(Hkv):
             base = (blk * Hkv + h) * hb
             kc[i, h] = _unpack_row(cache[base + t * rowb: base + (t + 1) * rowb], bits)
-            vrows = cache[base + kcb: base + 2 * kcb].reshape(HEAD_DIM, -1)
-            vr = _unpack_row(vrows, bits)  # [D][64 positions]
-            vc[i, h] = vr[:, pos[t]]
+            vrows = cache[base + kcb: base + 2 * kcb].reshape(-1, BLOCK)  # [rows][64 positions]
+            vb = vrows[:, pos[t]]
+            vc[i, h] = vb if bits == 8 else np.concatenate([vb & 15, vb >> 4])
             kp = cache[base + 2 * kcb + 4 * t: base + 2 * kcb + 4 * t + 4]
             vp = cache[base + 2 * kcb + 4 * BLOCK + 4 * t: base + 2 * kcb + 4 * BLOCK + 4 * t + 4]
             ks[i, h] = kp[:2].view(np.float16)[0]

@@ -104,6 +104,41 @@ def test_append_skips_negative_and_out_of_range_slots(bits):
     assert np.array_equal(host(cache), ref)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_append_slot_patterns(bits):
+    # units of 4 input tokens take the word store when their slots are a
+    # 4-aligned run inside one block and the byte store otherwise: aligned
+    # runs, misaligned runs, a reversed run, runs across a block boundary, a
+    # skipped slot inside a run and a ragged tail (13 tokens), byte for byte
+    import torch
+    hkv = 2
+    slots = np.array([0, 1, 2, 3,          # aligned run, block 0
+                      65, 66, 67, 68,      # misaligned run, block 1
+                      135, 134, 133, 132,  # reversed run, block 2
+                      62, 63, 64, 61,      # crosses blocks 0 and 1
+                      200, -1, 202, 203,   # skipped slot inside a would-be run
+                      188, 189, 190, 191,  # aligned run at the end of block 2
+                      4, 5, 6, 7,          # aligned run, block 0
+                      8, 9, 10, 11,        # aligned, but the last unit below is short
+                      12, 13, 14, 15, 16], np.int32)
+    ntok = slots.size
+    k, v = _kv_inputs(ntok, hkv, 21)
+    bb = w4.w4a16_kv_block_bytes(bits, hkv)
+    init = np.random.default_rng(22).integers(0, 256, 4 * bb, dtype=np.uint8)
+    for n in (ntok, 30, 5, 4, 1):
+        cache = dev(init)
+        w4.w4a16_kv_append(dev(k[:n]), dev(v[:n]), dev(slots[:n]), bits, cache)
+        torch.cuda.synchronize()
+        keep = np.flatnonzero(slots[:n] >= 0)
+        kc, ks, kz = kv.kv_quantize(k[:n], bits)
+        vc, vs, vz = kv.kv_quantize(v[:n], bits)
+        ref = init.copy()
+        kv.cache_write(ref, slots[keep], kc[keep], ks[keep], kz[keep], vc[keep], vs[keep], vz[keep], hkv, bits)
+        got = host(cache)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (n, bad[:10])
+
+
 def _reference(q, table, lengths, k, v, slots, hkv, bits, sm):
     """Oracle output per sequence from the oracle's own quantization."""
     kc, ks, kz = kv.kv_quantize(k, bits)

@@ -114,6 +114,27 @@ def test_cache_bytes_hand_checked():
     assert cache[:hb].sum() == 0
 
 
+def test_cache_bytes_hand_checked_four_bit():
+    # one token at slot 64 + 5, Hkv = 1, 4-bit: K row 5 packs two codes per
+    # byte (even index low); V row r packs dimensions r (low) and r + 64 (high)
+    hb = kv.head_block_bytes(4)
+    cache = np.zeros(2 * hb, np.uint8)
+    kc = (np.arange(D) % 16).astype(np.uint8)[None, None]
+    vc = (np.arange(D) // 8).astype(np.uint8)[None, None]
+    one = np.ones((1, 1), np.float16)
+    kv.cache_write(cache, [69], kc, one, np.full((1, 1), 7, np.uint8), vc, one,
+                   np.full((1, 1), 9, np.uint8), 1, 4)
+    base = hb
+    assert cache[base + 5 * 64 + 5] == 0xBA                          # K codes 10 and 11
+    p = int(kv.v_position(5))
+    assert cache[base + 4096 + 3 * 64 + p] == 0x80                   # V dims 3 and 67
+    assert cache[base + 4096 + 10 * 64 + p] == 0x91                  # V dims 10 and 74
+    assert cache[base + 4096 + 63 * 64 + p] == 0xF7                  # V dims 63 and 127
+    assert np.count_nonzero(cache[base + 4096: base + 8192]) == np.count_nonzero(
+        (np.arange(64) // 8) | ((np.arange(64, 128) // 8) << 4))
+    assert cache[:hb].sum() == 0
+
+
 # ------------------------------------------------------------ attention
 
 def _rand_cache(T, Hkv, bits, seed):

@@ -292,8 +292,10 @@ int w4a16_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, 
                     (long long)kv_heads, (long long)num_blocks);
     if (!aligned16(k) || !aligned16(v) || !aligned16(slots) || !aligned16(cache))
         return fail(W4A16_ERR_ALIGN, "k, v, slots and cache must be 16-byte aligned");
+    int dev = 0, cus = 0, rc;
+    if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
     hipError_t e = w4a16::launch_kv_append(k, v, slots, (int)ntok, (int)kv_heads, bits, num_blocks, (uint8_t *)cache,
-                                           (hipStream_t)stream);
+                                           cus, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "KV append launch");
     g_last_error[0] = 0;
     return W4A16_OK;

@@ -33,7 +33,7 @@ struct KvPlan {
 KvPlan kv_plan(int B, int Hkv, int max_blocks, int num_cus, int bits);
 size_t kv_workspace_bytes(int B, int Hkv, int max_blocks, int num_cus);
 hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int ntok, int Hkv, int bits,
-                            int64_t num_blocks, uint8_t *cache, hipStream_t stream);
+                            int64_t num_blocks, uint8_t *cache, int num_cus, hipStream_t stream);
 hipError_t launch_kv_attention(const uint16_t *q, const uint8_t *cache, const int32_t *block_table, int max_blocks,
                                const int32_t *lengths, int B, int Hq, int Hkv, int bits, int64_t num_blocks,
                                float sm_scale, uint16_t *out, void *workspace, int num_cus, hipStream_t stream);

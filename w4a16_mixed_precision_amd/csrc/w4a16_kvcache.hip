@@ -59,7 +59,7 @@ template <int BITS>
 struct KvGeom {
     static constexpr int kCodeBytes = kBS * kHD * BITS / 8;  // K (or V) codes of one region
     static constexpr int kRowBytes = kHD * BITS / 8;         // one K row
-    static constexpr int kVRowBytes = kBS * BITS / 8;        // one V row (64 positions)
+    static constexpr int kVRowBytes = kBS;                   // one V row: a byte per position
     static constexpr int kKPar = 2 * kCodeBytes;
     static constexpr int kVPar = 2 * kCodeBytes + 4 * kBS;
     static constexpr int kRegion = 2 * kCodeBytes + 8 * kBS;
@@ -67,80 +67,170 @@ struct KvGeom {
 
 __device__ inline int v_position(int t) { return 16 * ((t & 15) >> 2) + 8 * (t >> 5) + 4 * ((t >> 4) & 1) + (t & 3); }
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+// Maximum and minimum of a wave's 128 fp16 values, two per lane, as the
+// fp16 pair (max, -min): one packed maximum per step, exchanging through
+// DPP inside each row of 16 lanes (lanes i ^ 1, i ^ 2, then the half-row
+// and row mirrors), then folding the four row results into lane 63 with
+// the row broadcasts. The result is read from lane 63 (uniform).
+template <int CTRL, int ROW_MASK>
+__device__ inline half2v dpp_step(half2v v) {
+    const int b = __builtin_bit_cast(int, v);
+    // rows the mask leaves out keep their own value (max with itself)
+    const int m = ROW_MASK == 0xF ? __builtin_amdgcn_mov_dpp(b, CTRL, 0xF, 0xF, false)
+                                  : __builtin_amdgcn_update_dpp(b, b, CTRL, ROW_MASK, 0xF, false);
+    return __builtin_elementwise_maximum(v, __builtin_bit_cast(half2v, m));
 }
-__device__ inline float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = __builtin_fminf(v, __shfl_xor(v, o, 64));
-    return v;
+__device__ inline void wave_range(uint32_t pair, float &xmax, float &xmin) {
+    const half2v p = as_h2(pair);
+    half2v v = __builtin_elementwise_maximum(half2v{p.x, -p.x}, half2v{p.y, -p.y});
+    v = dpp_step<0xB1, 0xF>(v);   // quad_perm 1 0 3 2
+    v = dpp_step<0x4E, 0xF>(v);   // quad_perm 2 3 0 1
+    v = dpp_step<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_step<0x140, 0xF>(v);  // row_mirror: every lane holds its row's result
+    v = dpp_step<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+    v = dpp_step<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+    const half2v r = __builtin_bit_cast(half2v, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    xmax = (float)r.x;
+    xmin = -(float)r.y;
 }
 
 // ------------------------------------------------------------------ append
-// One wave per (token, KV head): lane l owns dimensions 2l and 2l + 1 of the
-// key and of the value. Tokens with a negative slot, or a slot past the
-// cache, are skipped.
-template <int BITS>
-__global__ void __launch_bounds__(64)
-kv_append_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int32_t *__restrict__ slots,
-                 int Hkv, int64_t num_blocks, uint8_t *__restrict__ cache) {
-    typedef KvGeom<BITS> Geo;
-    constexpr int L = (1 << BITS) - 1;
-    const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-    const int slot = slots[i];
-    if (slot < 0 || slot / kBS >= num_blocks) return;
-    const int blk = slot / kBS, t = slot % kBS;
-    uint8_t *region = cache + ((size_t)blk * Hkv + h) * Geo::kRegion;
+// One wave per unit of (KV head, 4 consecutive input tokens): lane l owns
+// dimensions 2l and 2l + 1 of each key and dimensions l and l + 64 of each
+// value (the two nibbles of one 4-bit V byte, so every byte of the cache
+// has one writer). Tokens with a negative slot, or a slot past the cache,
+// are skipped. Tokens t .. t + 3 of a block (t % 4 == 0) sit in 4
+// consecutive bytes of every V row, so when the unit's 4 slots are such a
+// run the wave stores one 32-bit word per V row instead of 4 bytes.
+
+constexpr int kAppendQuad = 4;  // input tokens per unit
+
+// The inputs of one unit, fetched one unit ahead of their use.
+struct AppendIn {
+    int slot[kAppendQuad];
+    int h, n;                              // KV head, tokens present (1..4)
+    uint32_t kp[kAppendQuad], vp[kAppendQuad];  // this lane's fp16 key pair (2l, 2l + 1), value pair (l, l + 64)
+};
+
+__device__ inline void kv_append_fetch(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                       const int32_t *__restrict__ slots, int ntok, int quads, int Hkv, int64_t u,
+                                       int lane, AppendIn &in) {
+    const int h = (int)(u / quads), i0 = (int)(u % quads) * kAppendQuad;
+    in.h = h;
+    in.n = ntok - i0 < kAppendQuad ? ntok - i0 : kAppendQuad;
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const uint16_t *src = (which ? v : k) + ((size_t)i * Hkv + h) * kHD;
-        const uint32_t pair = *reinterpret_cast<const uint32_t *>(src + 2 * lane);
-        const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFF));
-        const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
-        const float xmax = wave_max(__builtin_fmaxf(x0, x1));
-        const float xmin = wave_min(__builtin_fminf(x0, x1));
-        const float s32 = __builtin_fmaxf((xmax - xmin) / (float)L, kScaleFloor);
-        const _Float16 s16 = (_Float16)s32;
-        const float inv = 1.0f / (float)s16;
-        const double zr = __builtin_rint(-(double)xmin * (double)inv);  // exact product
-        const int z = zr < 0.0 ? 0 : (zr > (double)L ? L : (int)zr);
-        const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
-        const float y0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0, inv, kRoundMagic), lo, hi);
-        const float y1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1, inv, kRoundMagic), lo, hi);
-        const uint32_t c0 = __builtin_bit_cast(uint32_t, y0) - kRoundMagicBits + z;
-        const uint32_t c1 = __builtin_bit_cast(uint32_t, y1) - kRoundMagicBits + z;
-        if (which == 0) {
-            uint8_t *row = region + t * Geo::kRowBytes;
-            if constexpr (BITS == 8)
-                *reinterpret_cast<uint16_t *>(row + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
-            else
-                row[lane] = (uint8_t)(c0 | (c1 << 4));
+    for (int j = 0; j < kAppendQuad; ++j) {
+        const int i = i0 + j < ntok ? i0 + j : ntok - 1;  // a short last unit re-reads its last token
+        const size_t row = ((size_t)i * Hkv + h) * kHD;
+        in.slot[j] = slots[i];
+        in.kp[j] = *reinterpret_cast<const uint32_t *>(k + row + 2 * lane);
+        in.vp[j] = (uint32_t)v[row + lane] | ((uint32_t)v[row + lane + kHD / 2] << 16);
+    }
+}
+
+// Codes of this lane's two values of one vector, and the vector's scale and
+// zero (the weight quantizer's reading with L = 2^BITS - 1).
+template <int BITS>
+__device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c1, uint32_t &par) {
+    constexpr int L = (1 << BITS) - 1;
+    const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFF));
+    const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+    float xmax, xmin;
+    wave_range(pair, xmax, xmin);
+    const float s32 = __builtin_fmaxf((xmax - xmin) / (float)L, kScaleFloor);
+    const _Float16 s16 = (_Float16)s32;
+    const float inv = 1.0f / (float)s16;
+    const double zr = __builtin_rint(-(double)xmin * (double)inv);  // exact product
+    const int z = zr < 0.0 ? 0 : (zr > (double)L ? L : (int)zr);
+    const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
+    const float y0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0, inv, kRoundMagic), lo, hi);
+    const float y1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1, inv, kRoundMagic), lo, hi);
+    c0 = __builtin_bit_cast(uint32_t, y0) - kRoundMagicBits + z;
+    c1 = __builtin_bit_cast(uint32_t, y1) - kRoundMagicBits + z;
+    par = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)z << 16);
+}
+
+template <int BITS>
+__device__ inline void kv_append_store(const AppendIn &in, int Hkv, int64_t num_blocks, int lane,
+                                       uint8_t *__restrict__ cache) {
+    typedef KvGeom<BITS> Geo;
+    const int s0 = in.slot[0];
+    bool run = in.n == kAppendQuad && s0 >= 0 && (s0 & 3) == 0 && s0 / kBS < num_blocks;
+#pragma unroll
+    for (int j = 1; j < kAppendQuad; ++j) run = run && in.slot[j] == s0 + j;
+    uint32_t vw0 = 0, vw1 = 0;  // V code bytes of a run: rows l and l + 64 (8-bit) or row l (4-bit)
+#pragma unroll
+    for (int j = 0; j < kAppendQuad; ++j) {
+        const int slot = in.slot[j];
+        if (j >= in.n || slot < 0 || slot / kBS >= num_blocks) continue;
+        const int blk = slot / kBS, t = slot % kBS;
+        uint8_t *region = cache + ((size_t)blk * Hkv + in.h) * Geo::kRegion;
+        uint32_t c0, c1, kpar, vpar;
+        kv_quantize_pair<BITS>(in.kp[j], c0, c1, kpar);
+        uint8_t *row = region + t * Geo::kRowBytes;
+        if constexpr (BITS == 8)
+            *reinterpret_cast<uint16_t *>(row + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+        else
+            row[lane] = (uint8_t)(c0 | (c1 << 4));
+        kv_quantize_pair<BITS>(in.vp[j], c0, c1, vpar);
+        if (run) {
+            if constexpr (BITS == 8) {
+                vw0 |= c0 << (8 * j);
+                vw1 |= c1 << (8 * j);
+            } else {
+                vw0 |= (c0 | (c1 << 4)) << (8 * j);
+            }
         } else {
             uint8_t *vrows = region + Geo::kCodeBytes;
             const int p = v_position(t);
             if constexpr (BITS == 8) {
-                vrows[(2 * lane) * kBS + p] = (uint8_t)c0;
-                vrows[(2 * lane + 1) * kBS + p] = (uint8_t)c1;
+                vrows[lane * kBS + p] = (uint8_t)c0;
+                vrows[(lane + kHD / 2) * kBS + p] = (uint8_t)c1;
             } else {
-                // two tokens share a byte: update this token's nibble of the
-                // containing word with atomics (other tokens of the same call
-                // may update the other nibble)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int byte = (2 * lane + e) * Geo::kVRowBytes + p / 2;
-                    uint32_t *word = reinterpret_cast<uint32_t *>(vrows + (byte & ~3));
-                    const uint32_t sh = 8 * (byte & 3) + 4 * (p & 1);
-                    atomicAnd(word, ~(15u << sh));
-                    atomicOr(word, (e ? c1 : c0) << sh);
-                }
+                vrows[lane * kBS + p] = (uint8_t)(c0 | (c1 << 4));
             }
         }
         if (lane == 0) {
-            const uint32_t par = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)z << 16);
-            *reinterpret_cast<uint32_t *>(region + (which ? Geo::kVPar : Geo::kKPar) + 4 * t) = par;
+            *reinterpret_cast<uint32_t *>(region + Geo::kKPar + 4 * t) = kpar;
+            *reinterpret_cast<uint32_t *>(region + Geo::kVPar + 4 * t) = vpar;
         }
+    }
+    if (run) {
+        uint8_t *vrows = cache + ((size_t)(s0 / kBS) * Hkv + in.h) * Geo::kRegion + Geo::kCodeBytes;
+        const int p = v_position(s0 % kBS);  // positions p .. p + 3 hold the run's tokens
+        *reinterpret_cast<uint32_t *>(vrows + lane * kBS + p) = vw0;
+        if constexpr (BITS == 8) *reinterpret_cast<uint32_t *>(vrows + (lane + kHD / 2) * kBS + p) = vw1;
+    }
+}
+
+constexpr int kAppendWaves = 4;     // waves per workgroup
+constexpr int kAppendWgPerCu = 8;   // resident workgroups per CU (8 waves per SIMD)
+
+// A resident grid: each wave loops over units u = h * quads + i / 4
+// (head-major), fetching the next unit's inputs before it quantizes and
+// stores the current one. Workgroups are dealt to the 8 XCDs round-robin,
+// so workgroup w takes position (w % 8)-th share start + w / 8 of each
+// grid-sized round: every XCD runs a contiguous range of units, and the
+// tokens of one cache block and head run on one XCD, where their V stores
+// meet in its L2 as whole lines.
+template <int BITS>
+__global__ void __launch_bounds__(64 * kAppendWaves)
+kv_append_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int32_t *__restrict__ slots,
+                 int ntok, int Hkv, int64_t num_blocks, uint8_t *__restrict__ cache) {
+    const int lane = threadIdx.x & 63;
+    const int quads = (ntok + kAppendQuad - 1) / kAppendQuad;
+    const int64_t units = (int64_t)quads * Hkv;
+    const uint32_t grid = gridDim.x, w = blockIdx.x, x = w % 8, q = grid / 8, rem = grid % 8;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t stride = (int64_t)grid * kAppendWaves;
+    int64_t u = (int64_t)(x * q + (x < rem ? x : rem) + w / 8) * kAppendWaves + wave;
+    if (u >= units) return;
+    AppendIn cur, nxt;
+    kv_append_fetch(k, v, slots, ntok, quads, Hkv, u, lane, cur);
+    for (; u < units; u += stride) {
+        if (u + stride < units) kv_append_fetch(k, v, slots, ntok, quads, Hkv, u + stride, lane, nxt);
+        kv_append_store<BITS>(cur, Hkv, num_blocks, lane, cache);
+        cur = nxt;
     }
 }
 
@@ -151,7 +241,9 @@ struct KvStage {
     u32x4 kc[2][BITS == 8 ? 2 : 1];  // K codes of the two 16-token tiles, 32 dims per lane
     u32x4 kp[2];                     // K parameters of tokens 16 tt + 4 kq + 0..3
     u32x4 vp[2];                     // V parameters of the same tokens
-    uint32_t vc[8][BITS == 8 ? 2 : 1];  // V codes: d tile, 8 positions
+    // V codes, 8 positions per row: 8-bit, d tiles 0..7; 4-bit, row tiles
+    // 0..3 (low nibbles: d tile r, high nibbles: d tile r + 4)
+    uint32_t vc[BITS == 8 ? 8 : 4][2];
 };
 
 // fp16 pair (1024 + byte 2i, 1024 + byte 2i + 1) of the 8-bit codes in w:
@@ -260,15 +352,11 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
             S.vp[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(Geo::kVPar + 4 * t4), 0, 0));
         }
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const uint32_t off = (uint32_t)(Geo::kCodeBytes + (16 * dt + c) * Geo::kVRowBytes + (16 * kq + 8 * hf) * BITS / 8);
-            if constexpr (BITS == 8) {
-                const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-                S.vc[dt][0] = (uint32_t)w2[0];
-                S.vc[dt][1] = (uint32_t)w2[1];
-            } else {
-                S.vc[dt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-            }
+        for (int dt = 0; dt < (BITS == 8 ? 8 : 4); ++dt) {
+            const uint32_t off = (uint32_t)(Geo::kCodeBytes + (16 * dt + c) * Geo::kVRowBytes + 16 * kq + 8 * hf);
+            const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            S.vc[dt][0] = (uint32_t)w2[0];
+            S.vc[dt][1] = (uint32_t)w2[1];
         }
     };
 
@@ -349,8 +437,10 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
                 const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)(S.vp[u][e] & 0xFFFFu));
                 const _Float16 pv = (_Float16)(x[u][e] == -__builtin_inff() ? 0.f : p * vs);
                 const int j = 4 * u + e;
-                // 4-bit V: the nibble extraction yields slots 0 4 1 5 2 6 3 7
-                const int slot = BITS == 8 ? j : (j < 4 ? 2 * j : 2 * (j - 4) + 1);
+                // 4-bit V: each 16-bit half of a code word yields the tokens
+                // e and e + 2 of a 4-token group, so the slots of tokens
+                // e = 0 1 2 3 are 0 2 1 3
+                const int slot = BITS == 8 ? j : 4 * u + 2 * (e & 1) + (e >> 1);
                 pb[slot] = pv;
             }
         l_run += psum;
@@ -358,34 +448,43 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
             // slot pair (2 pr, 2 pr + 1): 8-bit tokens j = 2 pr, 2 pr + 1;
-            // 4-bit tokens j = pr, pr + 4
-            const int ja = BITS == 8 ? 2 * pr : pr, jb = BITS == 8 ? 2 * pr + 1 : pr + 4;
+            // 4-bit tokens j = 4 (pr / 2) + pr % 2 and that + 2
+            const int ja = BITS == 8 ? 2 * pr : 4 * (pr >> 1) + (pr & 1), jb = BITS == 8 ? ja + 1 : ja + 2;
             const uint32_t za = S.vp[ja / 4][ja % 4] >> 16 & 0xFFu;
             const uint32_t zb = S.vp[jb / 4][jb % 4] >> 16 & 0xFFu;
-            // -(1024 + z) for 8-bit codes and low nibbles, -(64 + z) for the
-            // high nibbles of 4-bit codes (slot pairs 1 and 3)
-            const uint32_t lo = 0xE400u | za, hi = 0xE400u | zb;
-            const uint32_t pair = lo | (hi << 16);
-            vzn[pr] = BITS == 4 && (pr & 1) ? neg_bias64_from_1024(pair) : pair;
+            vzn[pr] = (0xE400u | za) | ((0xE400u | zb) << 16);
         }
         // ---- O^T += V^T . P^T over the 8 tiles of 16 dimensions with the
         // exact integers c - z (the outputs are averages much smaller than
         // the codes, so the zero is not deferred as it is for the scores)
+        if constexpr (BITS == 8) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            half8 a;
-            if constexpr (BITS == 8) {
+            for (int dt = 0; dt < 8; ++dt) {
                 const uint32_t w0 = S.vc[dt][0], w1 = S.vc[dt][1];
-                a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(vzn[0]), as_h2(bytes_to_h2(w0, 1)) + as_h2(vzn[1]),
-                            as_h2(bytes_to_h2(w1, 0)) + as_h2(vzn[2]), as_h2(bytes_to_h2(w1, 1)) + as_h2(vzn[3]));
-            } else {
-                const uint32_t w = S.vc[dt][0], w8 = w >> 8;
-                a = pack_h8(as_h2(and_or(w, kLoMask, kMagic)) + as_h2(vzn[0]),
-                            as_h2(and_or(w, kHiMask, kMagic64)) + as_h2(vzn[1]),
-                            as_h2(and_or(w8, kLoMask, kMagic)) + as_h2(vzn[2]),
-                            as_h2(and_or(w8, kHiMask, kMagic64)) + as_h2(vzn[3]));
+                const half8 a = pack_h8(as_h2(bytes_to_h2(w0, 0)) + as_h2(vzn[0]), as_h2(bytes_to_h2(w0, 1)) + as_h2(vzn[1]),
+                                        as_h2(bytes_to_h2(w1, 0)) + as_h2(vzn[2]), as_h2(bytes_to_h2(w1, 1)) + as_h2(vzn[3]));
+                o[dt] = mfma16x16x32(a, pb, o[dt]);
             }
-            o[dt] = mfma16x16x32(a, pb, o[dt]);
+        } else {
+            // low nibbles enter as 1024 + c (d tile r), high nibbles as
+            // 64 + c with no shift (d tile r + 4)
+            uint32_t vzh[4];
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) vzh[pr] = neg_bias64_from_1024(vzn[pr]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const uint32_t w0 = S.vc[rt][0], w1 = S.vc[rt][1], w0s = w0 >> 8, w1s = w1 >> 8;
+                const half8 lo = pack_h8(as_h2(and_or(w0, kLoMask, kMagic)) + as_h2(vzn[0]),
+                                         as_h2(and_or(w0s, kLoMask, kMagic)) + as_h2(vzn[1]),
+                                         as_h2(and_or(w1, kLoMask, kMagic)) + as_h2(vzn[2]),
+                                         as_h2(and_or(w1s, kLoMask, kMagic)) + as_h2(vzn[3]));
+                o[rt] = mfma16x16x32(lo, pb, o[rt]);
+                const half8 hi = pack_h8(as_h2(and_or(w0, kHiMask, kMagic64)) + as_h2(vzh[0]),
+                                         as_h2(and_or(w0s, kHiMask, kMagic64)) + as_h2(vzh[1]),
+                                         as_h2(and_or(w1, kHiMask, kMagic64)) + as_h2(vzh[2]),
+                                         as_h2(and_or(w1s, kHiMask, kMagic64)) + as_h2(vzh[3]));
+                o[rt + 4] = mfma16x16x32(hi, pb, o[rt + 4]);
+            }
         }
     };
 
@@ -443,13 +542,17 @@ kv_combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ p
 size_t kv_region_bytes(int bits) { return bits == 8 ? KvGeom<8>::kRegion : KvGeom<4>::kRegion; }
 
 hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int ntok, int Hkv, int bits,
-                            int64_t num_blocks, uint8_t *cache, hipStream_t stream) {
+                            int64_t num_blocks, uint8_t *cache, int num_cus, hipStream_t stream) {
     if (ntok == 0) return hipSuccess;
-    const dim3 grid((unsigned)ntok, (unsigned)Hkv);
+    const int64_t units = (int64_t)((ntok + kAppendQuad - 1) / kAppendQuad) * Hkv;
+    const int64_t wgs = (units + kAppendWaves - 1) / kAppendWaves;
+    const int64_t resident = (int64_t)num_cus * kAppendWgPerCu;
+    const dim3 grid((unsigned)(wgs < resident ? wgs : resident));
+    const dim3 block(64 * kAppendWaves);
     if (bits == 8)
-        hipLaunchKernelGGL(kv_append_kernel<8>, grid, dim3(64), 0, stream, k, v, slots, Hkv, num_blocks, cache);
+        hipLaunchKernelGGL(kv_append_kernel<8>, grid, block, 0, stream, k, v, slots, ntok, Hkv, num_blocks, cache);
     else
-        hipLaunchKernelGGL(kv_append_kernel<4>, grid, dim3(64), 0, stream, k, v, slots, Hkv, num_blocks, cache);
+        hipLaunchKernelGGL(kv_append_kernel<4>, grid, block, 0, stream, k, v, slots, ntok, Hkv, num_blocks, cache);
     return hipGetLastError();
 }
 
