@@ -31,6 +31,8 @@ Prints ONE JSON line:
                step (sampled by columns where an instance is large)
   secondary    (default run) TFLOP/s of the Llama-3-8B-shaped prefill GEMM,
                M=2048, K=4096, N=28672
+  fp16_library (default run, context) the same shapes as dense fp16 GEMMs
+               through torch.matmul, and the W4A16 speedup over them
 """
 from __future__ import annotations
 
@@ -68,6 +70,8 @@ def parse_args(argv=None):
                    help="time only the offline quantizer (fp16 W -> packed) and print its line")
     p.add_argument("--w8a8-only", action="store_true",
                    help="time only the W8A8 GEMM legs and print their lines")
+    p.add_argument("--fp16-only", action="store_true",
+                   help="time only the dense fp16 library GEMMs of the workload's shapes (context) and print them")
     p.add_argument("--kv-only", action="store_true",
                    help="time only the low-bit KV cache decode attention (int8 and int4) and print its lines")
     return p.parse_args(argv)
@@ -386,6 +390,50 @@ def run_kv_secondary(args, bits, reps=20):
     }
 
 
+def run_fp16_library(args, rows, prefill_ms, reps=10):
+    """Context, not a target: the same shapes as a dense fp16 GEMM through
+    torch.matmul (the ROCm BLAS libraries), the yardstick of the pages'
+    4-bit-versus-fp16 claims. fp16 weights [K][N] in rotated copies (at
+    least --rotate-gib GiB per shape, so they stream from HBM), calls
+    captured in one HIP graph per shape, HIP events around `reps` replays."""
+    import torch
+    out = []
+    shapes = [(r["instance"], r["M"], r["K"], r["N"], r["us"]) for r in rows]
+    shapes.append(("llama3_8b_prefill/gate_up/M2048", 2048, 4096, 28672, prefill_ms * 1e3))
+    for name, M, K, N, w4_us in shapes:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(M * 7 + N)
+        wbytes = K * N * 2
+        copies = max(1, int(math.ceil(args.rotate_gib * 2 ** 30 / wbytes))) if M <= 64 else 1
+        Ws = [(torch.randn((K, N), generator=gen, device="cuda", dtype=torch.float32) * 0.02).half()
+              for _ in range(copies)]
+        X = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).half()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        for W in Ws:  # library set-up and kernel selection outside the capture
+            torch.matmul(X, W, out=Y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for W in Ws:
+                torch.matmul(X, W, out=Y)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        b.synchronize()
+        us = a.elapsed_time(b) / (reps * copies) * 1e3
+        out.append({"instance": name, "M": M, "K": K, "N": N, "fp16_us": us,
+                    "fp16_TBps": (K * N * 2 + M * K * 2 + M * N * 2) / (us * 1e-6) / 1e12,
+                    "fp16_TFLOPs": 2 * M * N * K / (us * 1e-6) / 1e12,
+                    "w4a16_us": w4_us, "w4a16_speedup": us / w4_us})
+        del Ws, X, Y, g
+        torch.cuda.empty_cache()
+    return {"kernel": "torch.matmul fp16 (ROCm BLAS), HIP graph replay", "shapes": out}
+
+
 def run_w8a8_secondary(args, reps=20):
     """W8A8 GEMM (int8 codes on the int8 matrix cores) on Llama-3-8B shapes:
     the QKV decode block (M=16, K=4096, N=6144; weight copies rotated so
@@ -497,6 +545,10 @@ def main(argv=None):
         if args.detail:
             print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
 
+    if args.fp16_only:
+        sec = run_prefill_secondary(args)
+        print(json.dumps(run_fp16_library(args, rows, sec["ms_per_launch"])), flush=True)
+        return 0
     if prefill:
         value = total_flops / (ms_step * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -552,6 +604,7 @@ def main(argv=None):
         out["quantizer"] = run_quantize_secondary(args)
         out["kv_attention"] = [run_kv_secondary(args, 8), run_kv_secondary(args, 4)]
         out["w8a8"] = run_w8a8_secondary(args)
+        out["fp16_library"] = run_fp16_library(args, rows, out["secondary"]["ms_per_launch"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(runner)
     print(json.dumps(out), flush=True)
