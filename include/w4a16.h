@@ -298,7 +298,9 @@ int w4a16_w8a8_quantize_act(const uint16_t *X, int64_t M, int64_t K, int8_t *xq,
                             void *stream);
 
 /* Workspace bytes of w4a16_w8a8_gemm (int32 partial sums when K is split
- * across workgroups; depends on the current device's CU count; 0 if none). */
+ * across workgroups, which happens only above 16 rows: up to M = 16 one
+ * launch sums K inside each workgroup; depends on the current device's CU
+ * count; 0 if none). */
 size_t w4a16_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Y[M][N] (fp16) from the codes and scales above. Asynchronous on `stream`;

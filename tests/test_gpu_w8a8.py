@@ -67,6 +67,32 @@ def test_forced_tile_shapes_agree(monkeypatch):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("ns,wk", [(1, 4), (1, 8), (1, 16), (2, 4), (2, 8), (2, 16)])
+def test_decode_kernel_shapes_bit_exact(monkeypatch, ns, wk):
+    # the single-launch kernel for M <= 16 in every instantiated shape:
+    # K with fewer tiles than waves (256: 4 tiles), K tiles not a multiple
+    # of the batch, an odd strip count (the last workgroup of NS = 2 holds
+    # one strip), every row count 1..16 across the cases, against the
+    # oracle and against the tiled split-K kernel
+    import torch
+    monkeypatch.setenv("W4A16_W8A8_DNS", str(ns))
+    monkeypatch.setenv("W4A16_W8A8_DWK", str(wk))
+    for M, K, N in ((1, 256, 16), (5, 320 * 4, 48), (16, 4096, 272), (9, 1536, 80), (12, 768, 16)):
+        say(f"w8a8 decode ns={ns} wk={wk} M={M} K={K} N={N}")
+        X, W = _inputs(M, K, N, 3 * M + K + N + ns + wk)
+        Y = _gpu(X, W)[-1]
+        qw, sw = w8a8.quantize_weights(W)
+        qx, sx = w8a8.quantize_activations(X)
+        ref = w8a8.gemm(qx, sx, qw, sw)
+        bad = np.argwhere(Y.view(np.uint16) != ref.view(np.uint16))
+        assert bad.size == 0, (M, K, N, bad[:5])
+        monkeypatch.setenv("W4A16_W8A8_TILE", "16")
+        Yt = _gpu(X, W)[-1]
+        monkeypatch.delenv("W4A16_W8A8_TILE")
+        assert np.array_equal(Y.view(np.uint16), Yt.view(np.uint16))
+    torch.cuda.synchronize()
+
+
 def test_full_size_llama3_8b_sampled():
     # gate/up of the Llama-3-8B prefill (M = 2048, K = 4096, N = 28672) and
     # a decode row block (M = 16), sampled on column windows

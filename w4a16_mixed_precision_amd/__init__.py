@@ -268,12 +268,17 @@ def w4a16_w8a8_quantize_weights(W, stream=None):
     return packed, ws
 
 
-def w4a16_w8a8_quantize_act(X, stream=None):
-    """fp16 X [M][K] (device) -> (xq int8 [M][K], x_scales float32 [M]). Asynchronous."""
+def w4a16_w8a8_quantize_act(X, stream=None, xq=None, xs=None):
+    """fp16 X [M][K] (device) -> (xq int8 [M][K], x_scales float32 [M]),
+    into xq / xs when given. Asynchronous."""
     import torch
     M, K = X.shape
-    xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
-    xs = torch.empty(M, dtype=torch.float32, device=X.device)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if xs is None:
+        xs = torch.empty(M, dtype=torch.float32, device=X.device)
+    if tuple(xq.shape) != (M, K) or xs.numel() < M:
+        raise ValueError("xq must be [M][K] and xs hold M floats")
     _check(lib().w4a16_w8a8_quantize_act(_dev_ptr(X, torch.float16, "X"), M, K, xq.data_ptr(), xs.data_ptr(),
                                          _stream(stream, X.device)))
     return xq, xs

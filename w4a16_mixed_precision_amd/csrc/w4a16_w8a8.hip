@@ -282,6 +282,96 @@ w8a8_reduce_kernel(const int32_t *__restrict__ part, const float *__restrict__ x
     }
 }
 
+// ------------------------------------------------------------ decode GEMM
+// Small M (<= 16 rows, one 16-row tile): one workgroup per NS strips of 16
+// columns over the whole of K, WK waves splitting the K tiles. Each wave
+// streams its weight tiles and the matching codes of X straight into
+// operand registers (lane (m, kq) of tile t holds X codes [m][64 t + 16 kq,
+// +16); rows at or past M lie outside the codes' descriptor and read zeros), with
+// the next batch of tiles in flight, and the waves' exact int32 partial
+// tiles are added in LDS: no split-K partials in memory and no second
+// launch.
+template <int NS, int WK>
+__global__ void __launch_bounds__(WK * 64)
+w8a8_decode_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, const uint8_t *__restrict__ packed,
+                   const float *__restrict__ ws, uint16_t *__restrict__ Y, int M, int N, int K) {
+    static_assert(NS <= WK, "one wave per strip in the epilogue");
+    constexpr int TB = 4;  // tiles per batch
+    __shared__ int32x4 red[WK][NS][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = lane & 15, kq = lane >> 4;
+    const int kt = K / 64;
+    const int nstrip = N / 16;
+    const int strip0 = blockIdx.x * NS;
+    const int per = (kt + WK - 1) / WK;
+    const int t0 = wave * per;
+    const int t1 = t0 + per < kt ? t0 + per : kt;
+    // one descriptor over the M x K codes: lanes of rows at or past M fall
+    // outside it and read zeros
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)(M * K));
+    const uint32_t xrow = (uint32_t)(row * K + 16 * kq);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(packed, (uint32_t)((size_t)K * N));
+    int sstrip[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) sstrip[j] = strip0 + j < nstrip ? strip0 + j : nstrip - 1;
+
+    struct Batch {
+        int32x4 x[TB];
+        int32x4 w[TB][NS];
+    };
+    // tiles past the wave's range load the wave's last tile again (in
+    // bounds) and are not multiplied
+    auto load = [&](int t, Batch &B) {
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+            const int tile = t + i < t1 ? t + i : t1 - 1;
+            B.x[i] = __builtin_bit_cast(int32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xrow + (uint32_t)(tile * 64), 0, 0));
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+                B.w[i][j] = __builtin_bit_cast(int32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            rw, lane * 16u, ((size_t)sstrip[j] * kt + tile) * kW8Tile, 0));
+        }
+    };
+    int32x4 acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j] = int32x4{0, 0, 0, 0};
+    auto compute = [&](int t, const Batch &B) {
+#pragma unroll
+        for (int i = 0; i < TB; ++i) {
+            if (t + i >= t1) break;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(B.x[i], B.w[i][j], acc[j], 0, 0, 0);
+        }
+    };
+    if (t0 < t1) {
+        Batch b0, b1;
+        load(t0, b0);
+        for (int t = t0; t < t1; t += 2 * TB) {
+            if (t + TB < t1) load(t + TB, b1);
+            compute(t, b0);
+            if (t + TB >= t1) break;
+            if (t + 2 * TB < t1) load(t + 2 * TB, b0);
+            compute(t + TB, b1);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    if (wave < NS && strip0 + wave < nstrip) {
+        int32x4 sum = red[0][wave][lane];
+#pragma unroll
+        for (int w = 1; w < WK; ++w) sum += red[w][wave][lane];
+        const int n = (strip0 + wave) * 16 + row;
+        const float swn = ws[n];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * kq + e;
+            if (m < M) Y[(size_t)m * N + n] = scale_out(sum[e], xs[m], swn);
+        }
+    }
+}
+
 inline unsigned grid_for(int64_t items) {
     int64_t blocks = (items + 255) / 256;
     if (blocks > 65536) blocks = 65536;
@@ -291,6 +381,7 @@ inline unsigned grid_for(int64_t items) {
 struct W8Plan {
     int bm;  // workgroup rows: 16 or 64
     int splits, slice_blocks;
+    int decode, ns, wk;  // the decode kernel (M <= 16): strips per workgroup, waves along K
 };
 
 // 16-row tiles up to M = 16, 64-row tiles above (128-row tiles need one
@@ -301,9 +392,34 @@ struct W8Plan {
 W8Plan w8_plan(int M, int N, int K, int num_cus) {
     W8Plan p;
     p.bm = M <= 16 ? 16 : 64;
-    if (const char *e = getenv("W4A16_W8A8_TILE")) {
+    p.decode = M <= 16;
+    if (const char *e = getenv("W4A16_W8A8_TILE")) {  // forces the tiled kernel
         const int v = atoi(e);
-        if (v == 16 || v == 64) p.bm = v;
+        if (v == 16 || v == 64) {
+            p.bm = v;
+            p.decode = 0;
+        }
+    }
+    // decode kernel: at most one workgroup per CU where two strips per
+    // workgroup get there (every workgroup reads all of X's codes, so two
+    // on one CU read them twice; graph-timed at M = 16, K = 4096, N = 6144:
+    // 10.9 us per call with two strips, 12.3-12.7 with one, waves along K
+    // 4, 8 or 16 within 2%). W4A16_W8A8_DNS (1, 2) and W4A16_W8A8_DWK (4,
+    // 8, 16) override the shape (tuning).
+    p.ns = N / 16 > num_cus ? 2 : 1;
+    p.wk = 8;
+    if (const char *e = getenv("W4A16_W8A8_DNS")) {
+        const int v = atoi(e);
+        if (v == 1 || v == 2) p.ns = v;
+    }
+    if (const char *e = getenv("W4A16_W8A8_DWK")) {
+        const int v = atoi(e);
+        if (v == 4 || v == 8 || v == 16) p.wk = v;
+    }
+    if (p.decode) {
+        p.splits = 1;
+        p.slice_blocks = K / kW8Block;
+        return p;
     }
     const int BM = p.bm;
     const int tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
@@ -342,6 +458,16 @@ hipError_t launch_w8a8_quant_weights(const uint16_t *W, int K, int N, uint8_t *p
 hipError_t launch_w8a8_gemm(const int8_t *xq, const float *xs, const uint8_t *packed, const float *ws, int M, int N,
                             int K, uint16_t *Y, void *workspace, int num_cus, hipStream_t stream) {
     const W8Plan p = w8_plan(M, N, K, num_cus);
+    if (p.decode) {
+        const dim3 grid((unsigned)((N / 16 + p.ns - 1) / p.ns));
+#define W8_DECODE(NS_, WK_)                                                                                          \
+    if (p.ns == NS_ && p.wk == WK_)                                                                                  \
+        hipLaunchKernelGGL((w8a8_decode_kernel<NS_, WK_>), grid, dim3(WK_ * 64), 0, stream, xq, xs, packed, ws, Y, M, \
+                           N, K);
+        W8_DECODE(1, 4) W8_DECODE(1, 8) W8_DECODE(1, 16) W8_DECODE(2, 4) W8_DECODE(2, 8) W8_DECODE(2, 16)
+#undef W8_DECODE
+        return hipGetLastError();
+    }
     int32_t *part = p.splits > 1 ? static_cast<int32_t *>(workspace) : nullptr;
     const int tiles_m = (M + p.bm - 1) / p.bm, tiles_n = (N + 255) / 256;
     const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.splits);
