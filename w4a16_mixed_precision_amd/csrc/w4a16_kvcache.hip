@@ -256,7 +256,9 @@ __device__ inline uint32_t bytes_to_h2(uint32_t w, int i) {
 // one half block in flight, 8-bit stages fit two waves and 4-bit stages
 // three without the compiler reusing registers of loads still in flight).
 template <int BITS>
-constexpr int kv_waves_per_simd() { return BITS == 8 ? 2 : 3; }
+constexpr bool kv_deep() { return BITS == 4; }
+template <int BITS>
+constexpr int kv_waves_per_simd() { return BITS == 8 ? 2 : (kv_deep<BITS>() ? 2 : 3); }
 
 template <int BITS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kv_waves_per_simd<BITS>(), kv_waves_per_simd<BITS>())))
@@ -488,9 +490,29 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
         }
     };
 
-    // Two stages: the next half block is in flight while one is multiplied
-    // (the pages' double-buffered KV loading).
-    if (h0 < h1) {
+    // The pages' double-buffered KV loading: 8-bit, the next half block is
+    // in flight while one is multiplied; 4-bit (smaller stages), the next
+    // two half blocks are in flight while two are multiplied.
+    if constexpr (kv_deep<BITS>()) {
+        if (h0 < h1) {
+            Stage s0, s1, s2, s3;
+            load(h0, s0);
+            load(h0 + 1, s1);
+            for (int hb = h0; hb < h1; hb += 4) {
+                load(hb + 2, s2);
+                load(hb + 3, s3);
+                compute(hb, s0);
+                if (hb + 1 >= h1) break;
+                compute(hb + 1, s1);
+                if (hb + 2 >= h1) break;
+                load(hb + 4, s0);
+                load(hb + 5, s1);
+                compute(hb + 2, s2);
+                if (hb + 3 >= h1) break;
+                compute(hb + 3, s3);
+            }
+        }
+    } else if (h0 < h1) {
         Stage s0, s1;
         load(h0, s0);
         for (int hb = h0; hb < h1; hb += 2) {
