@@ -251,6 +251,25 @@ def cpu_baseline(runner, max_macs=4e9, min_seconds=10.0, max_passes=200):
     }
 
 
+def copy_rate(nbytes=2 ** 30, reps=10):
+    """GB/s (bytes read + bytes written) of a plain device-to-device copy."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def run_prefill_secondary(args):
     import torch
 
@@ -590,6 +609,10 @@ def main(argv=None):
                 "launches_per_step": len(sel), "bytes_per_launch": b / len(sel),
                 "avg_launch_us": t / len(sel) * 1e6}
 
+    if not prefill:
+        # context for the HBM roofline: what a plain 1 GiB device-to-device
+        # copy (read + write) reaches on this GPU
+        roof["achievable_copy_GBps"] = copy_rate()
     out = {
         "metric": METRIC,
         "value": value,

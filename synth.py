@@ -80,8 +80,9 @@ def _inst(workload, matrix, Ms, K, N, G, outliers):
     return [Instance(workload, matrix, M, K, N, G, outliers) for M in Ms]
 
 
-# The five synthetic workloads: a tiny case, and layer shapes of Llama-3-8B,
-# Llama-3-70B and Qwen-2.5-72B (the models the pages serve).
+# The synthetic workloads: a tiny case, layer shapes of Llama-3-8B,
+# Llama-3-70B and Qwen-2.5-72B (the models the pages serve), and one GPU's
+# tensor-parallel shard of the Llama-3-70B layer.
 WORKLOADS = {
     "tiny": _inst("tiny", "tiny", [4], 256, 256, 128, False),
     "llama3_8b_decode": (
@@ -96,6 +97,12 @@ WORKLOADS = {
     "qwen25_72b_mixed": (
         _inst("qwen25_72b_mixed", "qkv", [512], 8192, 10240, 64, False)
         + _inst("qwen25_72b_mixed", "down", [512], 29568, 8192, 64, False)
+    ),
+    # one GPU's shard of the Llama-3-70B layer under 8-way tensor
+    # parallelism: gate/up split over N (57344 / 8), down over K (28672 / 8)
+    "llama3_70b_tp8_shard": (
+        _inst("llama3_70b_tp8_shard", "gate_up", [1, 16, 1024], 8192, 7168, 128, True)
+        + _inst("llama3_70b_tp8_shard", "down", [1, 16, 1024], 3584, 8192, 128, True)
     ),
 }
 

@@ -1,4 +1,4 @@
-"""Full-size parity: every instance of the five synthetic workloads, run in
+"""Full-size parity: every instance of the synthetic workloads, run in
 the launch configuration bench.py times (automatic plan through the C ABI),
 checked against the oracle on sampled column windows (the oracle computes a
 column slice exactly as it would inside the full product).

@@ -536,6 +536,22 @@ int plan_tiles(const Plan &p, int N) { return (N / kStripCols + p.ns - 1) / p.ns
 Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     Plan p = base_plan(M, N, K);
     const int nblk = K / kBlockK;
+    // Wider workgroups (more strips, to cut each CU's X reads) rely on
+    // splitting K to keep every CU busy; where K is too short to split
+    // that far, narrow them back until the workgroups cover the CUs
+    // (graph-timed, K = 3584, N = 8192, M = 16: 4 strips unsplit 9.0 us,
+    // 2 strips 6.9 us). The shape does not depend on the requested split
+    // count, so a plan asked for with its own automatic count is the same.
+    if (!p.fixed_splits && env_int("W4A16_DECODE_NS", 0) == 0) {
+        auto reach = [&](const Plan &q) {
+            const long t = plan_tiles(q, N);
+            int cap = nblk / (2 * q.wk);
+            if (cap < 1) cap = 1;
+            const long sp = t < num_cus ? ((num_cus + t - 1) / t < cap ? (num_cus + t - 1) / t : cap) : 1;
+            return t * sp;
+        };
+        while (p.ns > 1 && reach(p) < num_cus) p.ns /= 2;
+    }
     const int tiles = plan_tiles(p, N);
     if (splits <= 0 && p.fixed_splits) splits = 1;
     if (splits <= 0) {
