@@ -255,10 +255,14 @@ __device__ inline uint32_t bytes_to_h2(uint32_t w, int i) {
 // Waves per SIMD the attention kernel is built for (register budget: with
 // one half block in flight, 8-bit stages fit two waves and 4-bit stages
 // three without the compiler reusing registers of loads still in flight).
+// Half blocks in flight per wave, and waves per SIMD the kernel is built
+// for (measured at 50 x 4000 tokens: 8-bit, one half block at
+// two waves 88.7 us per call, two at one wave 92.6, three at one wave 105.5;
+// 4-bit, two at two waves 54.9, one at three waves 57).
 template <int BITS>
-constexpr bool kv_deep() { return BITS == 4; }
+constexpr int kv_depth() { return BITS == 8 ? 1 : 2; }
 template <int BITS>
-constexpr int kv_waves_per_simd() { return BITS == 8 ? 2 : (kv_deep<BITS>() ? 2 : 3); }
+constexpr int kv_waves_per_simd() { return 2; }
 
 template <int BITS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kv_waves_per_simd<BITS>(), kv_waves_per_simd<BITS>())))
@@ -490,37 +494,30 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
         }
     };
 
-    // The pages' double-buffered KV loading: 8-bit, the next half block is
-    // in flight while one is multiplied; 4-bit (smaller stages), the next
-    // two half blocks are in flight while two are multiplied.
-    if constexpr (kv_deep<BITS>()) {
-        if (h0 < h1) {
-            Stage s0, s1, s2, s3;
-            load(h0, s0);
-            load(h0 + 1, s1);
-            for (int hb = h0; hb < h1; hb += 4) {
-                load(hb + 2, s2);
-                load(hb + 3, s3);
-                compute(hb, s0);
-                if (hb + 1 >= h1) break;
-                compute(hb + 1, s1);
-                if (hb + 2 >= h1) break;
-                load(hb + 4, s0);
-                load(hb + 5, s1);
-                compute(hb + 2, s2);
-                if (hb + 3 >= h1) break;
-                compute(hb + 3, s3);
+    // The pages' double-buffered KV loading, D half blocks deep: while D
+    // half blocks are multiplied the next D are in flight.
+    if (h0 < h1) {
+        constexpr int D = kv_depth<BITS>();
+        Stage st[2][D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) load(h0 + i, st[0][i]);
+        for (int hb = h0; hb < h1; hb += 2 * D) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) load(hb + D + i, st[1][i]);
+            bool more = true;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                if (hb + i >= h1) more = false;
+                if (more) compute(hb + i, st[0][i]);
             }
-        }
-    } else if (h0 < h1) {
-        Stage s0, s1;
-        load(h0, s0);
-        for (int hb = h0; hb < h1; hb += 2) {
-            load(hb + 1, s1);
-            compute(hb, s0);
-            if (hb + 1 >= h1) break;
-            load(hb + 2, s0);
-            compute(hb + 1, s1);
+            if (hb + D >= h1) break;
+#pragma unroll
+            for (int i = 0; i < D; ++i) load(hb + 2 * D + i, st[0][i]);
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                if (hb + D + i >= h1) more = false;
+                if (more) compute(hb + D + i, st[1][i]);
+            }
         }
     }
 
