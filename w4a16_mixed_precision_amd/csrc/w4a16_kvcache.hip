@@ -534,24 +534,43 @@ kv_attention_kernel(const uint16_t *__restrict__ q, const uint8_t *__restrict__ 
 
 // O[b][h] = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i over the chunks of
 // (b, h / g); one workgroup of 128 threads per (b, h), thread = dimension.
+// The chunks' (max, sum) records and outputs are loaded 8 chunks at a time,
+// all loads of a batch in flight together, and merged with a running
+// maximum (for 8 chunks or fewer that is one pass with the global maximum).
 __global__ void __launch_bounds__(128)
 kv_combine_kernel(const float *__restrict__ part_o, const float2 *__restrict__ part_ml, int Hq, int Hkv,
                   int nchunks, uint16_t *__restrict__ out) {
+    constexpr int CB = 8;
     const int bh = blockIdx.x, d = threadIdx.x;
     const int b = bh / Hq, h = bh % Hq, g = Hq / Hkv;
     const int kh = h / g, c = h % g;
     const size_t u0 = ((size_t)b * Hkv + kh) * nchunks;
-    float M = -__builtin_inff();
-    for (int i = 0; i < nchunks; ++i) M = __builtin_fmaxf(M, part_ml[(u0 + i) * 16 + c].x);
-    float num = 0.f, den = 0.f;
-    if (M != -__builtin_inff()) {
-        for (int i = 0; i < nchunks; ++i) {
-            const float2 ml = part_ml[(u0 + i) * 16 + c];
-            if (ml.x == -__builtin_inff()) continue;
-            const float w = __builtin_amdgcn_exp2f(ml.x - M);
-            num += w * part_o[((u0 + i) * 16 + c) * kHD + d];
-            den += w * ml.y;
+    float M = -__builtin_inff(), num = 0.f, den = 0.f;
+    for (int i0 = 0; i0 < nchunks; i0 += CB) {
+        float2 ml[CB];
+        float o[CB];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const bool in = i0 + j < nchunks;
+            const size_t r = (u0 + (in ? i0 + j : 0)) * 16 + c;
+            ml[j] = in ? part_ml[r] : float2{-__builtin_inff(), 0.f};
+            o[j] = in ? part_o[r * kHD + d] : 0.f;
         }
+        float mb = M;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) mb = __builtin_fmaxf(mb, ml[j].x);
+        if (mb == -__builtin_inff()) continue;  // no tokens so far
+        const float sc = __builtin_amdgcn_exp2f(M - mb);  // 0 while M is -inf
+        num *= sc;
+        den *= sc;
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            if (ml[j].x == -__builtin_inff()) continue;
+            const float w = __builtin_amdgcn_exp2f(ml[j].x - mb);
+            num += w * o[j];
+            den += w * ml[j].y;
+        }
+        M = mb;
     }
     out[(size_t)bh * kHD + d] = f32_to_f16_bits(den > 0.f ? num / den : 0.f);
 }
