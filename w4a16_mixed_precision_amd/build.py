@@ -38,7 +38,11 @@ def _run(cmd, verbose):
 
 def build_library(verbose: bool = False, extra_flags=None) -> str:
     # -packed-fp32-ops: keep hipcc from emitting packed fp32 VALU instructions.
-    flags = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # -amdgpu-kernarg-preload-count: kernel arguments arrive preloaded in
+    # SGPRs (the code object keeps a prologue that loads them itself where
+    # the firmware does not preload), so a wave's first address arithmetic
+    # does not wait for a scalar memory load.
+    flags = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-mllvm", "-amdgpu-kernarg-preload-count=16",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(HERE, "..", "include")] + list(extra_flags or [])
     objdir = os.path.join(HERE, "_build")
