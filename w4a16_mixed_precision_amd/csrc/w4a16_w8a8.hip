@@ -60,20 +60,53 @@ __device__ inline uint16_t scale_out(int32_t acc, float sx, float sw) {
 
 // ------------------------------------------------------------ activations
 // One workgroup of 256 threads per token (row); 8 values per thread per
-// 16-byte load. K % 256 == 0.
+// 16-byte load. K % 256 == 0. Rows of up to 8192 values stay in registers
+// between the maximum and the codes (one read of X); longer rows are read
+// again.
+constexpr int kActRegChunks = 4;  // 16-byte chunks per thread kept in registers
+
+__device__ inline void quant8_store(const u32x4 &v, float inv, int8_t *dst) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t c0 = (uint32_t)code8(h2f((uint16_t)(v[d] & 0xFFFF)), inv) & 0xFFu;
+        const uint32_t c1 = (uint32_t)code8(h2f((uint16_t)(v[d] >> 16)), inv) & 0xFFu;
+        const uint32_t pair = c0 | (c1 << 8);
+        if (d < 2)
+            lo |= pair << (16 * d);
+        else
+            hi |= pair << (16 * (d - 2));
+    }
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+}
+
+__device__ inline float absmax8(const u32x4 &v, float amax) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f((uint16_t)(v[d] & 0xFFFF))));
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f((uint16_t)(v[d] >> 16))));
+    }
+    return amax;
+}
+
 __global__ void __launch_bounds__(256)
 w8a8_quant_act_kernel(const uint16_t *__restrict__ X, int K, int8_t *__restrict__ xq, float *__restrict__ xs) {
     __shared__ float red[4];
     const int m = blockIdx.x, tid = threadIdx.x;
     const uint16_t *row = X + (size_t)m * K;
+    const bool held = K <= kActRegChunks * 256 * 8;
+    u32x4 keep[kActRegChunks];
     float amax = 0.f;
-    for (int k = tid * 8; k < K; k += 256 * 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
+    if (held) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f((uint16_t)(v[d] & 0xFFFF))));
-            amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f((uint16_t)(v[d] >> 16))));
+        for (int i = 0; i < kActRegChunks; ++i) {
+            const int k = (i * 256 + tid) * 8;
+            keep[i] = k < K ? *reinterpret_cast<const u32x4 *>(row + k) : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int i = 0; i < kActRegChunks; ++i) amax = absmax8(keep[i], amax);
+    } else {
+        for (int k = tid * 8; k < K; k += 256 * 8) amax = absmax8(*reinterpret_cast<const u32x4 *>(row + k), amax);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, 64));
@@ -84,20 +117,14 @@ w8a8_quant_act_kernel(const uint16_t *__restrict__ X, int K, int8_t *__restrict_
     const float inv = 1.0f / s;
     if (tid == 0) xs[m] = s;
     int8_t *out = xq + (size_t)m * K;
-    for (int k = tid * 8; k < K; k += 256 * 8) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(row + k);
-        uint32_t lo = 0, hi = 0;
+    if (held) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t c0 = (uint32_t)code8(h2f((uint16_t)(v[d] & 0xFFFF)), inv) & 0xFFu;
-            const uint32_t c1 = (uint32_t)code8(h2f((uint16_t)(v[d] >> 16)), inv) & 0xFFu;
-            const uint32_t pair = c0 | (c1 << 8);
-            if (d < 2)
-                lo |= pair << (16 * d);
-            else
-                hi |= pair << (16 * (d - 2));
+        for (int i = 0; i < kActRegChunks; ++i) {
+            const int k = (i * 256 + tid) * 8;
+            if (k < K) quant8_store(keep[i], inv, out + k);
         }
-        *reinterpret_cast<uint2 *>(out + k) = make_uint2(lo, hi);
+    } else {
+        for (int k = tid * 8; k < K; k += 256 * 8) quant8_store(*reinterpret_cast<const u32x4 *>(row + k), inv, out + k);
     }
 }
 
