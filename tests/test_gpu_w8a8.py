@@ -93,6 +93,25 @@ def test_decode_kernel_shapes_bit_exact(monkeypatch, ns, wk):
     torch.cuda.synchronize()
 
 
+def test_decode_kernel_at_maximum_k():
+    # K = 131072, the largest the boundary accepts: the decode kernel's X
+    # offsets reach 16 K, and Y[2][3] sums K products 127 * 127 =
+    # 2,114,060,288, just under 2^31, exactly in int32
+    import torch
+    M, K, N = 16, 131072, 32
+    X, W = _inputs(M, K, N, 5)
+    X[2] = np.float16(1.0)   # token 2: code 127 everywhere
+    W[:, 3] = np.float16(0.25)  # column 3: code 127 everywhere (Y[2][3] = 32768, finite)
+    Y = _gpu(X, W)[-1]
+    qw, sw = w8a8.quantize_weights(W)
+    qx, sx = w8a8.quantize_activations(X)
+    assert int(w8a8.gemm_int(qx[2:3], qw[:, 3:4])[0, 0]) == K * 127 * 127
+    ref = w8a8.gemm(qx, sx, qw, sw)
+    bad = np.argwhere(Y.view(np.uint16) != ref.view(np.uint16))
+    assert bad.size == 0, bad[:5]
+    torch.cuda.synchronize()
+
+
 def test_full_size_llama3_8b_sampled():
     # gate/up of the Llama-3-8B prefill (M = 2048, K = 4096, N = 28672) and
     # a decode row block (M = 16), sampled on column windows
