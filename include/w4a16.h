@@ -33,7 +33,8 @@
  *   - Return value: W4A16_OK (0) or a negative W4A16_ERR_* code;
  *     w4a16_last_error() gives a message for the calling thread.
  *   - Shapes: K % 128 == 0, N % 16 == 0, G in {32, 64, 128, 256} with
- *     K % G == 0, 1 <= M <= 2^30, K and N <= 2^22. Anything else is
+ *     K % G == 0, 1 <= M <= 2^30, K and N <= 2^22, and K * N / 2 < 2^31
+ *     (the 4-bit weights of one matrix stay below 2 GiB). Anything else is
  *     W4A16_ERR_SHAPE.
  *
  * Packed layout, version 2 (bytes, little-endian):
@@ -68,8 +69,10 @@ extern "C" {
 #define W4A16_ERR_NULL (-1)      /* a required pointer is NULL */
 #define W4A16_ERR_SHAPE (-2)     /* M, N, K or G outside the supported set */
 #define W4A16_ERR_ALIGN (-3)     /* a device pointer is not 16-byte aligned */
-#define W4A16_ERR_RANGE (-4)     /* pack: a q or z code is larger than 15;
-                                    quantize: a weight is Inf or NaN */
+#define W4A16_ERR_RANGE (-4)     /* pack: a q or z code is larger than 15, or a
+                                    dequantized weight is not a finite fp16;
+                                    quantize: a weight is Inf or NaN, or a
+                                    group's codes dequantize beyond fp16 */
 #define W4A16_ERR_HIP (-5)       /* a HIP runtime call or kernel launch failed */
 #define W4A16_ERR_WORKSPACE (-6) /* workspace missing or smaller than required */
 #define W4A16_ERR_ARG (-7)       /* path or split selector out of range */
@@ -94,9 +97,15 @@ size_t w4a16_packed_bytes(int64_t K, int64_t N, int64_t G);
  *   zeros   uint8 [K/G][N]   codes 0..15
  *   scales  fp16  [K/G][N]
  * into `packed` (w4a16_packed_bytes(K, N, G) bytes, caller-allocated).
- * Enqueued on `stream`, then synchronizes that stream (the pass is offline)
- * to report W4A16_ERR_RANGE if any code exceeds 15; on that error the packed
- * contents are unspecified.
+ * The dequantized weight (q - z) * s is an fp16 value on the pages (the
+ * formula above), so every one must be finite in fp16: W4A16_ERR_RANGE if
+ * any code exceeds 15, a scale is Inf or NaN, or |(q - z) * s| >= 65520
+ * (which rounds to infinity); on that error the packed contents are
+ * unspecified. With this rule neither GEMM path can overflow while
+ * dequantizing.
+ * Enqueued on `stream` (so that it is ordered after the caller's writes of
+ * q, zeros and scales on that stream), then synchronizes that stream (the
+ * pass is offline) to report the status.
  */
 int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales,
                int64_t K, int64_t N, int64_t G, void *packed, void *stream);
@@ -142,7 +151,8 @@ int w4a16_quantize_pack(const uint16_t *W, int64_t K, int64_t N, int64_t G,
 
 /*
  * Exact inverse of w4a16_pack: recovers q, zeros and scales (same layouts as
- * the inputs of w4a16_pack) from a packed buffer. Synchronizes `stream`.
+ * the inputs of w4a16_pack) from a packed buffer. Enqueued on `stream`, then
+ * synchronizes it.
  */
 int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G,
                  uint8_t *q, uint8_t *zeros, uint16_t *scales, void *stream);
@@ -159,7 +169,12 @@ int w4a16_unpack(const void *packed, int64_t K, int64_t N, int64_t G,
  * plan splits K across workgroups (see w4a16_workspace_bytes), a per-device
  * library workspace is allocated with hipMalloc on first need and reused;
  * calls that need it must therefore not run concurrently on two streams of
- * one device (use w4a16_gemm_ex with separate workspaces for that).
+ * one device (use w4a16_gemm_ex with separate workspaces for that). When a
+ * larger plan outgrows the workspace, a new one is allocated and the old one
+ * is kept (never freed) so that enqueued or graph-captured work stays valid;
+ * growing it while `stream` is being captured is refused with
+ * W4A16_ERR_WORKSPACE (run the shape once before capturing, or capture
+ * w4a16_gemm_ex with a caller-owned workspace).
  */
 int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
                int64_t G, uint16_t *Y, void *stream);
@@ -184,8 +199,14 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int pat
  *            the fp32 partial sums of the K splits between the GEMM kernel
  *            and the reduce kernel, so calls sharing one workspace must be
  *            ordered (same stream).
- * The result does not depend on `path` or `splits` beyond fp32 rounding
- * order; for a fixed plan it is bitwise reproducible.
+ * Rounding depends on the plan, the exact result does not: the decode path
+ * multiplies the exact integers (q - z) by X and applies each group's scale
+ * to the group's fp32 partial sum; the prefill path rounds every dequantized
+ * weight (q - z) * s to fp16 once before multiplying; both accumulate in fp32
+ * (in an order that depends on `splits`) and round Y to fp16 once. Results
+ * of different plans therefore differ by a few fp16 units at most, within
+ * max|dY| <= 4e-3 max|Y| and ||dY||_F <= 1e-3 ||Y||_F of the exact product;
+ * for a fixed plan the result is bitwise reproducible.
  */
 int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
                   int64_t G, uint16_t *Y, void *workspace, size_t workspace_bytes,

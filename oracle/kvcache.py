@@ -16,10 +16,10 @@ quantization):
   reading is the one the weight quantizer uses (``quantize.py``) with L =
   2^bits - 1 steps over the vector's range:
       s   = float16(max(float32(max - min) / L, 2**-14))
-      inv = float32(1 / s)
-      z   = min(max(rint(-min * inv), 0), L)
-      c   = min(max(rint(x * inv) + z, 0), L)
-  (products exact, rint = round half to even).
+      z   = min(max(rint(-min / s), 0), L)
+      c   = min(max(rint(x / s) + z, 0), L)
+  with rint the nearest integer to the exact quotient, ties to even (a
+  float64 division decides it exactly for fp16 operands; see quantize.py).
 * Decode attention for one new query token per sequence, with grouped heads
   (query head h reads KV head h // (Hq / Hkv)):
       O[h] = softmax(sm_scale * q[h] . K^T) . V
@@ -83,9 +83,9 @@ def kv_quantize(x, bits: int):
     f = x.astype(np.float32)
     xmax, xmin = f.max(axis=-1), f.min(axis=-1)
     s = np.maximum((xmax - xmin) / L, _FLOOR).astype(np.float16)
-    inv = (np.float32(1) / s.astype(np.float32)).astype(np.float64)
-    z = np.minimum(np.maximum(np.rint(-xmin.astype(np.float64) * inv), 0.0), float(L))
-    c = np.minimum(np.maximum(np.rint(f.astype(np.float64) * inv[..., None]) + z[..., None], 0.0), float(L))
+    s64 = s.astype(np.float64)
+    z = np.minimum(np.maximum(np.rint(-xmin.astype(np.float64) / s64), 0.0), float(L))
+    c = np.minimum(np.maximum(np.rint(f.astype(np.float64) / s64[..., None]) + z[..., None], 0.0), float(L))
     return c.astype(np.uint8), s, z.astype(np.uint8)
 
 

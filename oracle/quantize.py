@@ -17,39 +17,47 @@ and why it beats naive RTN INT4; AWQ's own step, scaling salient input
 channels before this quantizer, needs calibration activations and is not
 part of it). They give no formula for s and z. The reading taken here is the
 plain asymmetric one: the group's own range [min, max] is spread over the 16
-codes, the zero is the code of the value 0, and every weight goes to the
-nearest code.
-
-The scale is float32 arithmetic, each operation rounded to nearest even
-(numpy float32 ufuncs); the codes round an exact product once:
+codes, the zero is the code nearest to the value 0, and every weight goes to
+the nearest code:
 
     wmax, wmin = largest and smallest weight of the group       (exact)
     s32 = max((wmax - wmin) / 15, 2**-14)                        (float32)
     s   = float16(s32)                                           (stored scale)
-    inv = 1 / float32(s)                                         (float32)
-    z   = min(max(rint(-wmin * inv), 0), 15)
-    q   = min(max(rint(w * inv) + z, 0), 15)                     (each weight)
+    z   = min(max(rint(-wmin / s), 0), 15)
+    q   = min(max(rint(w / s) + z, 0), 15)                       (each weight)
 
-where w * inv is the exact product of an fp16 and a float32 number (at most
-35 significant bits, so float64 holds it exactly) and rint rounds it to the
-nearest integer, ties to even: one rounding, as round-to-nearest reads. The
-floor 2**-14 (the smallest normal fp16) gives a group whose weights are all
-equal a usable scale: all zeros quantize to q = z = 0 exactly; a constant
+The range is taken in float32 with each operation rounded to nearest even
+(numpy float32 ufuncs), then rounded to the stored fp16 scale. rint is the
+nearest integer to the EXACT quotient, ties to even: round-to-nearest read
+plainly, and the codes belong to the scale actually stored. The quotients
+are evaluated as float64 divisions, which decide rint exactly for these
+operands: with w = a 2^x and s = b 2^y (a, b integers below 2^11, s normal),
+w/s - (n + 1/2) = (2w - (2n + 1) s) / (2s) is either 0 (an exact tie, which
+float64 represents exactly) or at least 2^min(x+1, y) / 2^(y+12) >= 2^-12 in
+magnitude, while the float64 quotient is within 2^-52 |w/s| of the exact one
+(and |w/s| < 2^31 for fp16 w and s >= 2^-14); when x + 1 < y, |w/s| < 1/2 -
+2^-12 and rint gives 0 either way.
+
+The floor 2**-14 (the smallest normal fp16) gives a group whose weights are
+all equal a usable scale: all zeros quantize to q = z = 0 exactly; a constant
 c != 0 saturates to the code 15 or 0. Where the range excludes 0 the zero
 code saturates too, and weights beyond the representable end saturate; both
-are properties of the method, not of this code. Codes are decided with the
-reciprocal of the stored fp16 scale, so they are the codes of the scale
-actually stored.
+are properties of the method, not of this code.
 
-Inputs must be finite (a non-finite weight raises ValueError).
+Errors (ValueError): a non-finite weight; and a group whose codes
+dequantize beyond the fp16 range, |(q - z) * s| >= 65520 (which rounds to
+infinity): the dequantized weight is an fp16 value on the pages, so such a
+group has no valid encoding under this reading (it needs weights within a
+factor two of the fp16 maximum).
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["quantize", "SCALE_FLOOR"]
+__all__ = ["quantize", "SCALE_FLOOR", "FP16_OVERFLOW"]
 
 SCALE_FLOOR = np.float32(2.0 ** -14)
+FP16_OVERFLOW = 65520.0  # the smallest magnitude that rounds to an fp16 infinity
 
 
 def quantize(W, G: int):
@@ -68,7 +76,9 @@ def quantize(W, G: int):
     wmin = Wg.min(axis=1)
     s32 = np.maximum((wmax - wmin) / f32(15), SCALE_FLOOR)
     s = s32.astype(np.float16)
-    inv = (f32(1) / s.astype(f32)).astype(np.float64)   # float32 value, held exactly
-    z = np.minimum(np.maximum(np.rint(-wmin.astype(np.float64) * inv), 0.0), 15.0)
-    q = np.minimum(np.maximum(np.rint(Wg.astype(np.float64) * inv[:, None, :]) + z[:, None, :], 0.0), 15.0)
+    s64 = s.astype(np.float64)
+    z = np.minimum(np.maximum(np.rint(-wmin.astype(np.float64) / s64), 0.0), 15.0)
+    q = np.minimum(np.maximum(np.rint(Wg.astype(np.float64) / s64[:, None, :]) + z[:, None, :], 0.0), 15.0)
+    if np.any(np.abs((q - z[:, None, :]) * s64[:, None, :]) >= FP16_OVERFLOW):
+        raise ValueError("a group's codes dequantize beyond the fp16 range (|(q - z) * s| >= 65520)")
     return (q.reshape(K, N).astype(np.uint8), z.astype(np.uint8), s)

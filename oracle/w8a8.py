@@ -20,14 +20,18 @@ taken here is the plain symmetric one that lets the matrix cores multiply
 * Y[m][n] = fp16(acc[m][n] * s_x[m] * s_w[n]) with acc the exact integer
   sum over k of q_x[m][k] * q_w[k][n].
 
-Precision of each step (the kernel's, so that both sides take the integer
-decisions identically): the scales are float32 (max|.| as float32 divided
-by 127 in float32, correctly rounded; a zero row or column gets the scale
-1), the codes round the exact product of the fp16 value and the float32
-reciprocal of the scale once (half to even), and the output is
-fp16(float32(float32(acc) * s_x) * s_w) with each product rounded to
-nearest even. SmoothQuant's calibrated smoothing (moving activation
-outliers into the weights) needs calibration data and is not part of it.
+Precision of each step (part of the reading, since the pages fix none):
+the scales are stored as float32 numbers, max|.| / 127 rounded once to
+float32 (a zero row or column gets the scale 1); a code is the nearest
+integer to the exact quotient of the fp16 value and its stored scale, ties
+to even, clamped to +-127 (float64 division decides it exactly: with
+x = a 2^p, s = b 2^r, a < 2^11, b < 2^24, a quotient that is not a
+half-integer lies at least 2^-25 from every half-integer, or below 1/2,
+while |x / s| <= 128 keeps the float64 error below 2^-45); and the output
+dequantizes in the scales' own precision, fp16(float32(float32(acc) * s_x)
+* s_w), each product rounded to nearest even. SmoothQuant's calibrated
+smoothing (moving activation outliers into the weights) needs calibration
+data and is not part of it.
 """
 from __future__ import annotations
 
@@ -48,9 +52,8 @@ def quantize_symmetric(x, axis: int):
     f = x.astype(np.float32)
     amax = np.abs(f).max(axis=axis)
     s = np.where(amax > 0, amax / np.float32(127), np.float32(1)).astype(np.float32)
-    inv = (np.float32(1) / s).astype(np.float64)  # float32 value, held exactly
-    invb = np.expand_dims(inv, axis)
-    q = np.clip(np.rint(f.astype(np.float64) * invb), -127, 127)
+    sb = np.expand_dims(s.astype(np.float64), axis)
+    q = np.clip(np.rint(f.astype(np.float64) / sb), -127, 127)
     return q.astype(np.int8), s
 
 

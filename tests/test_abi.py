@@ -152,3 +152,41 @@ def test_python_binding_refuses_host_tensors():
     packed = torch.zeros(w4.w4a16_packed_bytes(256, 256, 128), dtype=torch.uint8)
     with pytest.raises(ValueError):
         w4.w4a16_gemm(X, packed, 256, 256, 128)
+
+
+def test_weight_bytes_bound_rejects_shapes_the_prefill_descriptors_cannot_address():
+    """The prefill kernel reaches the whole packed weight region through one
+    buffer descriptor with a 32-bit byte count, so the boundary refuses
+    K * N / 2 >= 2^31 (e.g. K = N = 65536, and K = N = 131072, whose 8 GiB
+    would wrap a 32-bit count to 0 and read zeros)."""
+    L = w4.lib()
+    for K, N in [(65536, 65536), (131072, 131072), (1 << 22, 1024)]:
+        assert w4.w4a16_packed_bytes(K, N, 128) == 0
+        assert L.w4a16_gemm(FAKE, FAKE, 1, N, K, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+        assert "2^31" in w4.w4a16_last_error()
+        assert L.w4a16_pack(FAKE, FAKE, FAKE, K, N, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+        assert L.w4a16_quantize_pack(FAKE, K, N, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    # just below the bound is accepted: 65536 x 65520 / 2 < 2^31
+    assert w4.w4a16_packed_bytes(65536, 65520, 128) == oracle.packed_bytes(65536, 65520, 128)
+
+
+def test_python_binding_checks_the_packed_size_before_any_launch():
+    """A packed tensor one byte short of w4a16_packed_bytes(K, N, G) is refused
+    in the binding (the kernels size their reads from K, N and G, not from the
+    allocation); the check runs before the tensors are even looked at as
+    device pointers, so it holds without a GPU."""
+    torch = pytest.importorskip("torch")
+    K, N, G = 256, 256, 128
+    need = w4.w4a16_packed_bytes(K, N, G)
+    X = torch.zeros((1, K), dtype=torch.float16)
+    short = torch.zeros(need - 1, dtype=torch.uint8)
+    for call in (lambda: w4.w4a16_gemm(X, short, N, K, G),
+                 lambda: w4.w4a16_gemm_ex(X, short, N, K, G),
+                 lambda: w4.w4a16_unpack(short, K, N, G)):
+        with pytest.raises(ValueError, match="needs"):
+            call()
+    q = torch.zeros((K, N), dtype=torch.uint8)
+    z = torch.zeros((K // G, N), dtype=torch.uint8)
+    s = torch.zeros((K // G, N), dtype=torch.float16)
+    with pytest.raises(ValueError, match="needs"):
+        w4.w4a16_pack(q, z, s, G, packed=short)

@@ -55,6 +55,52 @@ def test_pack_rejects_codes_above_15():
     assert e.value.status == w4.W4A16_ERR_RANGE
 
 
+def test_pack_rejects_weights_beyond_fp16_and_both_paths_agree_at_the_edge():
+    """The dequantized weight (q - z) * s is an fp16 value: pack refuses a
+    non-finite scale and a product |q - z| |s| >= 65520 (it rounds to
+    infinity), so neither GEMM path ever overflows while dequantizing. At the
+    edge that stays finite (15 * 4352 = 65280) both paths match the oracle.
+    [0, 65504] quantized by the library's own rule gives s = 4368, z = 0,
+    q = 15, the product 65520: refused by pack and by the quantizer."""
+    import torch
+    K, N, G = 256, 64, 128
+    q, z, s, _ = _weights(K, N, G, seed=5)
+    for bad in (np.inf, -np.inf, np.nan):
+        sb = s.copy()
+        sb[1, 9] = bad
+        with pytest.raises(w4.W4A16Error) as e:
+            pack_dev(q, z, sb, G)
+        assert e.value.status == w4.W4A16_ERR_RANGE
+    qe, ze, se = q.copy(), z.copy(), s.copy()
+    qe[:, 0], ze[:, 0], se[:, 0] = 15, 0, np.float16(4368.0)     # 15 * 4368 = 65520: infinite
+    with pytest.raises(w4.W4A16Error) as e:
+        pack_dev(qe, ze, se, G)
+    assert e.value.status == w4.W4A16_ERR_RANGE and "65520" in str(e.value)
+    qe[:, 0], ze[:, 0], se[:, 0] = 0, 15, np.float16(-4368.0)    # |0 - 15| * 4368 as well
+    with pytest.raises(w4.W4A16Error):
+        pack_dev(qe, ze, se, G)
+    # the largest finite edge: 15 * 4352 = 65280, in a column whose X-weighted
+    # sum stays finite (X is tiny there), through both paths
+    qe[:, 0], ze[:, 0], se[:, 0] = 15, 0, np.float16(4352.0)
+    packed = pack_dev(qe, ze, se, G)
+    M = 16
+    X = np.random.default_rng(6).standard_normal((M, K)).astype(np.float16)
+    X *= np.float16(1e-3)
+    Yref = oracle.gemm(X, qe, ze, se, G)
+    for path in (w4.W4A16_PATH_DECODE, w4.W4A16_PATH_PREFILL):
+        Y = run_gemm(X, packed, N, K, G, path=path, splits=1)
+        assert_parity(Y, Yref, f"edge path={path}")
+    # the quantizer refuses a group whose codes would dequantize to infinity
+    W = np.zeros((K, N), np.float16)
+    W[0, :16] = 65504.0
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_quantize(dev(W), G)
+    assert e.value.status == w4.W4A16_ERR_RANGE
+    with pytest.raises(ValueError):
+        oracle.quantize(W, G)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ exact cases
 
 @pytest.mark.parametrize("G", [32, 64, 128, 256])

@@ -7,10 +7,10 @@ bytes that the oracle's layout writer (and w4a16_pack) makes of them.
 
 Inputs: ``synth.draw_fp16_weights`` (N(0, 0.02) with 1% of the rows x4),
 plus groups built by hand for the method's degenerate cases (all zeros,
-constant, a range that excludes zero, exact ties, a product just above one
-half). The quantizer works column by column, so at full size the oracle
-runs on column windows and the device output is compared on the same
-windows.
+constant, a range that excludes zero, exact ties of the quotient w / s,
+including ties that a float32-reciprocal product would misplace, fp16
+subnormals and extremes), and groups whose codes would dequantize beyond
+fp16, which both sides refuse.
 """
 import numpy as np
 import pytest
@@ -57,7 +57,7 @@ def test_quantize_matches_oracle(K, N, G):
 
 def _edge_matrix(G):
     """Columns of hand-built groups, one case per 16-column strip."""
-    K, N = 2 * max(G, 128), 128
+    K, N = 2 * max(G, 128), 144
     rng = np.random.default_rng(G)
     W = rng.normal(0, 0.02, (K, N))
     w = 0.00843048095703125
@@ -71,12 +71,16 @@ def _edge_matrix(G):
         W[rows, 48:64] = grid[:, None]                        # exact grid
         W[g0 + 2: g0 + 7, 48:64] = np.array([0.0625, 0.1875, -0.0625, -0.1875, 0.3125])[:, None]
         W[rows, 64:80] = 0.0                                  # product just above 1/2
-        W[g0: g0 + 4, 64:80] = np.array([-0.125, 0.1279296875, w, -w])[:, None]
+        W[g0: g0 + 4, 64:80] = np.array([-0.125, 0.1279296875, w, -w])[:, None]   # w = s/2: ties
+        W[rows, 128:144] = 0.0                                # s = 3/64, 0.1171875 = 2.5 s: a tie
+        W[g0: g0 + 3, 128:144] = np.array([0.0, 0.703125, 0.1171875])[:, None]
         W[rows, 80:96] = -1e-7                                # fp16 subnormals: scale
         W[g0, 80:96] = 3e-7                                   # floored, 1/s = 16384, and
         W[g0 + 1, 80:96] = 5e-5                               # 5e-5 * 16384 = 0.82 -> code 1
         W[rows, 96:112] = 65504.0 * np.sign(rng.standard_normal((G, 16)))   # extremes
     W[:, 112:128] *= 1e3                                      # large ordinary weights
+    # exact ties of the quotient (w / s = c + 1/2) whose float32-reciprocal
+    # product lands on the other side: the codes must follow the quotient
     return W.astype(np.float16)
 
 
@@ -100,6 +104,29 @@ def test_non_finite_weight_is_reported():
             w4.w4a16_quantize_pack(dev(Wb), 128)
     # the status word is cleared per call: a good call afterwards succeeds
     _check_plain(W, 128)
+
+
+def test_groups_beyond_fp16_are_reported():
+    # [0, 65504] -> s = 4368, z = 0, 65504 -> code 15: 15 * 4368 = 65520
+    # rounds to infinity; [-65504, 0] likewise with z = 15, code 0. The
+    # oracle refuses both, and the device returns W4A16_ERR_RANGE.
+    for lo, hi in ((0.0, 65504.0), (-65504.0, 0.0)):
+        W = synth.draw_fp16_weights(256, 64, seed=8)
+        W[128:256, 32] = np.float16(lo / 2 + hi / 2)
+        W[128, 32], W[129, 32] = lo, hi
+        with pytest.raises(ValueError):
+            oracle.quantize(W, 128)
+        for fn in (w4.w4a16_quantize, w4.w4a16_quantize_pack):
+            with pytest.raises(w4.W4A16Error) as ei:
+                fn(dev(W), 128)
+            assert ei.value.status == w4.W4A16_ERR_RANGE
+    # a group at the finite edge, [0, 65280] (s = 4352, 15 s = 65280), is fine
+    W = synth.draw_fp16_weights(256, 64, seed=8)
+    W[128:256, 32] = 1.0
+    W[128, 32], W[129, 32] = 0.0, 65280.0
+    q, z, s = _check_plain(W, 128)
+    assert s[1, 32] == np.float16(4352.0) and q[129, 32] == 15
+    _check_packed(W, 128, q, z, s)
 
 
 def test_quantize_pack_equals_pack_of_quantize():

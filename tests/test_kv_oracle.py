@@ -57,13 +57,49 @@ def test_codes_are_nearest(bits):
     L = 2 ** bits - 1
     s64, z64 = s.astype(np.float64)[:, None], z.astype(np.float64)[:, None]
     w = x.astype(np.float64)
-    err = np.abs(w - (codes - z64) * s64)
+    # every quantity is exact in float64: no slack; equally near codes
+    # resolve to an even (c - z)
+    d = codes - z64
+    err = np.abs(w - d * s64)
     allc = np.arange(L + 1, dtype=np.float64)[:, None, None]
-    best = np.abs(w[None] - (allc - z64[None]) * s64[None]).min(axis=0)
-    assert np.all(err <= best + 1e-6 * s64 * (1 + np.abs(w / s64)))
+    errs = np.abs(w[None] - (allc - z64[None]) * s64[None])
+    best = errs.min(axis=0)
+    assert np.all(err == best)
+    tie = (errs == best[None]).sum(axis=0) > 1
+    assert np.all(d[tie] % 2 == 0)
     # scale = range / L to fp16 rounding
     rngx = w.max(axis=1) - w.min(axis=1)
     assert np.all(np.abs(s.astype(np.float64) - rngx / L) <= 2.0 ** -11 * rngx / L * 1.001)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_exact_tie_goes_to_even_not_where_a_reciprocal_puts_it(bits):
+    # range 45/64 (4-bit, 15 steps) or 765/64 (8-bit, 255 steps): s = 3/64
+    # exactly, zero code 0; 0.1171875 / s = 2.5 is a tie -> 2. fp32(64 / 3)
+    # is above 64/3, so the reciprocal product (2.50000007...) would give 3.
+    from fractions import Fraction
+    top = 0.703125 if bits == 4 else 11.953125
+    x = np.zeros((1, D), np.float16)
+    x[0, :3] = [0.0, top, 0.1171875]
+    codes, s, z = kv.kv_quantize(x, bits)
+    assert s[0] == np.float16(0.046875) and z[0] == 0
+    assert Fraction(0.1171875) * Fraction(float(np.float32(1) / np.float32(0.046875))) > Fraction(5, 2)
+    assert codes[0, 2] == 2 and codes[0, 1] == 2 ** bits - 1
+
+
+def test_planted_reciprocal_rule_is_caught(monkeypatch):
+    def reciprocal_rule(x, bits):
+        L = np.float32(2 ** bits - 1)
+        f = x.astype(np.float32)
+        xmax, xmin = f.max(axis=-1), f.min(axis=-1)
+        s = np.maximum((xmax - xmin) / L, np.float32(2.0 ** -14)).astype(np.float16)
+        inv = (np.float32(1) / s.astype(np.float32)).astype(np.float64)
+        z = np.minimum(np.maximum(np.rint(-xmin.astype(np.float64) * inv), 0.0), float(L))
+        c = np.minimum(np.maximum(np.rint(f.astype(np.float64) * inv[..., None]) + z[..., None], 0.0), float(L))
+        return c.astype(np.uint8), s, z.astype(np.uint8)
+    monkeypatch.setattr(kv, "kv_quantize", reciprocal_rule)
+    with pytest.raises(AssertionError):
+        test_exact_tie_goes_to_even_not_where_a_reciprocal_puts_it(4)
 
 
 # ------------------------------------------------------------ layout

@@ -2,8 +2,10 @@
 
 The pages print no worked example of the quantizer, so it is tied down by
 hand-worked groups whose codes follow from the definition by mental
-arithmetic, by the property that defines round-to-nearest (every code is the
-nearest of the 16, checked by brute force in float64), by the range the 16
+arithmetic (including exact ties whose quotient a float32 reciprocal would
+misplace), by the property that defines round-to-nearest (every code is the
+nearest of the 16, exactly, checked by brute force in float64, where every
+quantity involved is exact), by the range the 16
 codes must cover, by exact invariants (power-of-two scaling, round trip of
 already-quantized weights) and by the tie rule of the conversions it relies
 on. ``test_planted_mistakes_are_caught`` checks that each plausible slip,
@@ -48,25 +50,54 @@ def test_ties_round_to_even():
     assert list(q[:7, 3]) == [0, 15, 8, 10, 8, 6, 10]
 
 
-def test_codes_round_the_exact_product_once():
-    # range 0.1279296875 - (-0.125) = 0.2529296875; / 15 -> fp16 0x2451
-    # (0.016860961914...), whose float32 reciprocal is 59.308597564697266.
-    # The zero is rint(0.125 * 59.3086) = rint(7.41) = 7. The weight
-    # 0.00843048095703125 times that reciprocal is 0.50000000236 exactly
-    # (Fraction below): just above one half, so its code is 7 + 1 = 8, and
-    # its negative gets 7 - 1 = 6. Rounding the product to float32 first
-    # would land on exactly 0.5 and round to even (code 7).
+def test_codes_are_nearest_to_the_exact_quotient():
+    # range 0.1279296875 - (-0.125) = 0.2529296875; / 15 -> fp16 0x2451 =
+    # 1105 * 2^-16. The zero is rint(0.125 / s) = rint(7.41) = 7. The weight
+    # w = 1105 * 2^-17 is exactly s / 2: w / s = 1/2, a tie, rounds to even
+    # (0), so w gets code 7 + 0 = 7, and -w (-1/2 -> -0) gets 7 as well.
+    # Multiplying by the float32 reciprocal of s instead (59.308597564697266,
+    # rounded up) lands the product just above one half and would give 8 and
+    # 6: the rule is the quotient, not a reciprocal product.
     from fractions import Fraction
     w = 0.00843048095703125
     vals = [-0.125, 0.1279296875, w, -w] + [0.0] * 28
     q, z, s = oracle.quantize(_col(vals), 32)
     assert np.all(s.view(np.uint16) == 0x2451)
+    assert Fraction(w) / Fraction(float(s[0, 0])) == Fraction(1, 2)
     inv = np.float32(1) / np.float32(s[0, 0])
-    assert float(inv) == 59.308597564697266
     assert Fraction(w) * Fraction(float(inv)) > Fraction(1, 2)
-    assert float(np.float32(w * float(inv))) == 0.5
     assert np.all(z == 7)
-    assert list(q[:4, 5]) == [0, 15, 8, 6]
+    assert list(q[:4, 5]) == [0, 15, 7, 7]
+
+
+def test_exact_tie_with_an_inexact_reciprocal():
+    # group [0, 0.703125, 0.1171875, 0, ...]: range 45/64 over 15 steps is
+    # s = 3/64 = 0.046875 exactly (fp32 and fp16), zero code 0. The weight
+    # 0.1171875 = 15/128 is 2.5 steps: a tie, code 2 (even). 1/s = 64/3 has
+    # no exact float32 form; its float32 value is above 64/3, so
+    # 0.1171875 * fp32(1/s) = 2.50000007... would round to 3.
+    from fractions import Fraction
+    vals = [0.0, 0.703125, 0.1171875] + [0.0] * 29
+    q, z, s = oracle.quantize(_col(vals), 32)
+    assert np.all(s == np.float16(0.046875)) and np.all(z == 0)
+    assert Fraction(0.1171875) / Fraction(0.046875) == Fraction(5, 2)
+    inv = np.float32(1) / np.float32(0.046875)
+    assert Fraction(0.1171875) * Fraction(float(inv)) > Fraction(5, 2)
+    assert list(q[:3, 0]) == [0, 15, 2]
+
+
+def test_groups_that_dequantize_beyond_fp16_are_refused():
+    # [0, 65504]: s = fp16(65504 / 15 = 4366.93) = 4368 (fp16 spacing 4 at
+    # 4096..8192), z = 0, and 65504 / 4368 = 14.996 -> code 15: (15 - 0) *
+    # 4368 = 65520 rounds to infinity in fp16, so the group has no valid
+    # encoding. [0, 65280] (s = 4352, 15 s = 65280) is fine.
+    with pytest.raises(ValueError, match="fp16"):
+        oracle.quantize(_col([0.0, 65504.0] + [1.0] * 30), 32)
+    q, z, s = oracle.quantize(_col([0.0, 65280.0] + [1.0] * 30), 32)
+    assert np.all(s == np.float16(4352.0)) and np.all(z == 0) and list(q[:2, 0]) == [0, 15]
+    # negative side: [-65504, 0] -> s = 4368, z = rint(14.996) = 15, code 0
+    with pytest.raises(ValueError, match="fp16"):
+        oracle.quantize(_col([-65504.0, 0.0] + [-1.0] * 30), 32)
 
 
 def test_all_zero_group():
@@ -114,18 +145,24 @@ def _weights(K, N, seed):
 
 @pytest.mark.parametrize("G", [32, 64, 128, 256])
 def test_every_code_is_the_nearest(G):
+    # Brute force over all 16 codes. Every quantity here is exact in float64
+    # (fp16 weights and scales, 4-bit codes: |w - (c - z) s| needs at most
+    # 40 significant bits), so the comparison needs no slack: the chosen
+    # code is at least as near as every other one, and where two codes are
+    # equally near, (q - z) is the even one (ties to even on the quotient).
     W = _weights(512, 48, seed=G)
     q, z, s = oracle.quantize(W, G)
     s64 = np.repeat(s.astype(np.float64), G, axis=0)
     z64 = np.repeat(z.astype(np.float64), G, axis=0)
     w = W.astype(np.float64)
-    err = np.abs(w - (q.astype(np.float64) - z64) * s64)
+    d = q.astype(np.float64) - z64
+    err = np.abs(w - d * s64)
     codes = np.arange(16, dtype=np.float64)[:, None, None]
-    best = np.abs(w[None] - (codes - z64[None]) * s64[None]).min(axis=0)
-    # the code decision uses the float32 reciprocal of s (one rounding of
-    # the exact product): allow a relative slack of a few float32 ulps of
-    # the quotient near ties
-    assert np.all(err <= best + 1e-6 * s64 * (1 + np.abs(w / s64)))
+    errs = np.abs(w[None] - (codes - z64[None]) * s64[None])
+    best = errs.min(axis=0)
+    assert np.all(err == best)
+    tie = (errs == best[None]).sum(axis=0) > 1
+    assert np.all(d[tie] % 2 == 0)
 
 
 @pytest.mark.parametrize("G", [32, 128])
@@ -210,18 +247,25 @@ def _wrong_quantizers():
     f32 = np.float32
     real_quantize = oracle.quantize
 
-    def common(W, G, *, steps=15, zsign=1, rnd=np.rint, coded_scale=True, clamp_z=True, f32_product=False):
+    def common(W, G, *, steps=15, zsign=1, rnd=np.rint, coded_scale=True, clamp_z=True, decide="quotient"):
         K, N = W.shape
         Wg = W.astype(f32).reshape(K // G, G, N)
         wmax, wmin = Wg.max(axis=1), Wg.min(axis=1)
         s32 = np.maximum((wmax - wmin) / f32(steps), SCALE_FLOOR)
         s = s32.astype(np.float16)
-        inv = f32(1) / (s.astype(f32) if coded_scale else s32)
-        if not f32_product:  # exact products, as the oracle takes them
-            inv, wmin, Wg = inv.astype(np.float64), wmin.astype(np.float64), Wg.astype(np.float64)
-        zz = rnd(-zsign * wmin * inv)
+        sd = (s if coded_scale else s32).astype(np.float64)
+        wmin, Wg = wmin.astype(np.float64), Wg.astype(np.float64)
+        if decide == "quotient":
+            ratio = lambda v, t: v / t                                              # noqa: E731
+        else:
+            inv = (f32(1) / sd.astype(f32)).astype(np.float64)
+            if decide == "reciprocal":                  # exact product with fp32(1/s), one rounding
+                ratio = lambda v, t: v * (inv if t is sd else inv[:, None, :])      # noqa: E731
+            else:                                       # product rounded to float32 first
+                ratio = lambda v, t: (v * (inv if t is sd else inv[:, None, :])).astype(f32).astype(np.float64)  # noqa: E731
+        zz = rnd(ratio(-zsign * wmin, sd))
         z = np.minimum(np.maximum(zz, 0), 15) if clamp_z else np.mod(zz, 256)
-        q = np.minimum(np.maximum(rnd(Wg * inv[:, None, :]) + z[:, None, :], 0), 15)
+        q = np.minimum(np.maximum(rnd(ratio(Wg, sd[:, None, :])) + z[:, None, :], 0), 15)
         return q.reshape(K, N).astype(np.uint8), z.astype(np.uint8), s
 
     return [
@@ -232,14 +276,17 @@ def _wrong_quantizers():
         lambda W, G: common(W, G, clamp_z=False),                             # zero not clamped
         lambda W, G: common(W, G, rnd=np.trunc),                              # truncation, not rounding
         lambda W, G: tuple(a.T.copy() for a in real_quantize(W.T.copy(), G)),  # groups along N
-        lambda W, G: common(W, G, f32_product=True),                          # product rounded twice
+        lambda W, G: common(W, G, decide="reciprocal"),                       # w * fp32(1/s) rounded once
+        lambda W, G: common(W, G, decide="f32product"),                       # that product rounded twice
+        lambda W, G: common(W, G),                                            # no fp16 range check
     ]
 
 
 def _pins_fail(fn):
     failures = 0
     checks = [test_exact_grid_group, test_ties_round_to_even, test_constant_group_saturates,
-              test_codes_round_the_exact_product_once,
+              test_codes_are_nearest_to_the_exact_quotient, test_exact_tie_with_an_inexact_reciprocal,
+              test_groups_that_dequantize_beyond_fp16_are_refused,
               test_range_excluding_zero, test_groups_run_along_k, test_quantized_weights_round_trip,
               lambda: test_every_code_is_the_nearest(32)]
     real = oracle.quantize
@@ -248,14 +295,14 @@ def _pins_fail(fn):
         for c in checks:
             try:
                 c()
-            except (AssertionError, ValueError, IndexError):
+            except (AssertionError, ValueError, IndexError, pytest.fail.Exception):
                 failures += 1
     finally:
         oracle.quantize = real
     return failures
 
 
-@pytest.mark.parametrize("idx", range(8))
+@pytest.mark.parametrize("idx", range(10))
 def test_planted_mistakes_are_caught(idx):
     assert _pins_fail(_wrong_quantizers()[idx]) > 0
     assert _pins_fail(oracle.quantize) == 0

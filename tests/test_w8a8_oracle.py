@@ -44,11 +44,34 @@ def test_scale_axes():
 
 
 def test_codes_are_nearest():
+    # Every quantity is exact in float64 (fp16 x, a 7-bit code times a
+    # float32 scale), so no slack: |x - q s| <= s/2, and at exactly s/2 (a
+    # tie) the code is even.
     rng = np.random.default_rng(2)
     X = rng.standard_normal((16, 256)).astype(np.float16)
     q, s = w8a8.quantize_activations(X)
+    half = 0.5 * s.astype(np.float64)[:, None]
     err = np.abs(X.astype(np.float64) - q.astype(np.float64) * s.astype(np.float64)[:, None])
-    assert np.all(err <= 0.5 * s.astype(np.float64)[:, None] * (1 + 1e-6))
+    assert np.all(err <= half)
+    assert np.all(q[err == half] % 2 == 0)
+
+
+def test_codes_follow_the_exact_quotient_not_a_reciprocal_product():
+    # Row [20, -10, 0]: s = fp32(20 / 127) = 0.15748031437397003 (below
+    # 20 / 127). -10 / s = -63.50000024 lies beyond -63.5, so its code is
+    # -64; the product -10 * fp32(1 / s) lands just inside, -63.4999..., and
+    # would give -63. Row [95.25, 1.875]: s = 0.75 exactly, 1.875 / 0.75 =
+    # 2.5 is a tie and goes to 2 (even), while fp32(1 / 0.75) is above 4/3
+    # and the product 2.50000007... would give 3.
+    from fractions import Fraction
+    X = np.array([[20.0, -10.0, 0.0, 0.0], [95.25, 1.875, 0.0, 0.0]], np.float16)
+    q, s = w8a8.quantize_activations(X)
+    assert s[0] == np.float32(np.float32(20.0) / np.float32(127)) and s[1] == np.float32(0.75)
+    assert Fraction(-10.0) / Fraction(float(s[0])) < Fraction(-127, 2)
+    assert Fraction(-10.0) * Fraction(float(np.float32(1) / s[0])) > Fraction(-127, 2)
+    assert Fraction(1.875) * Fraction(float(np.float32(1) / s[1])) > Fraction(5, 2)
+    assert q[0].tolist() == [127, -64, 0, 0]
+    assert q[1].tolist() == [127, 2, 0, 0]
 
 
 def test_integer_product_against_loops():
@@ -104,14 +127,22 @@ def _wrong():
         s = np.where(amax > 0, amax / np.float32(128), np.float32(1)).astype(np.float32)
         q = np.clip(np.rint(f.astype(np.float64) * (np.float32(1) / s).astype(np.float64)[:, None]), -128, 127)
         return q.astype(np.int8), s
-    return [per_tensor, wrong_axis, levels_128]
+
+    def reciprocal_product(X):  # codes from x * fp32(1 / s), rounded once
+        f = X.astype(np.float32)
+        amax = np.abs(f).max(axis=1)
+        s = np.where(amax > 0, amax / np.float32(127), np.float32(1)).astype(np.float32)
+        q = np.clip(np.rint(f.astype(np.float64) * (np.float32(1) / s).astype(np.float64)[:, None]), -127, 127)
+        return q.astype(np.int8), s
+    return [per_tensor, wrong_axis, levels_128, reciprocal_product]
 
 
-@pytest.mark.parametrize("idx", range(3))
+@pytest.mark.parametrize("idx", range(4))
 def test_planted_mistakes_are_caught(idx, monkeypatch):
     monkeypatch.setattr(w8a8, "quantize_activations", _wrong()[idx])
     failed = 0
-    for t in (test_hand_worked_scale_and_ties, test_scale_axes):
+    for t in (test_hand_worked_scale_and_ties, test_scale_axes,
+              test_codes_follow_the_exact_quotient_not_a_reciprocal_product):
         try:
             t()
         except (AssertionError, ValueError, IndexError):

@@ -125,6 +125,26 @@ def _dev_ptr(t, dtype, name):
     return t.data_ptr()
 
 
+def _same_device(*named):
+    """Raise ValueError unless every given tensor sits on one device."""
+    devs = {(n, t.device) for n, t in named if t is not None}
+    if len({d for _, d in devs}) > 1:
+        raise ValueError("tensors on different devices: " +
+                         ", ".join(f"{n} on {d}" for n, d in sorted(devs, key=lambda x: x[0])))
+
+
+def _check_packed(packed, K: int, N: int, G: int, name: str = "packed"):
+    """Raise before any launch if `packed` cannot hold the packed layout of a
+    K x N weight with groups of G: the kernels size their buffer
+    descriptors from K, N and G, not from the allocation."""
+    need = w4a16_packed_bytes(K, N, G)
+    if need == 0:
+        raise ValueError(f"unsupported shape K={K} N={N} G={G}")
+    have = packed.numel() * packed.element_size()
+    if have < need:
+        raise ValueError(f"{name} holds {have} bytes, K={K} N={N} G={G} needs {need}")
+
+
 def _stream(stream, device):
     import torch
     if stream is None:
@@ -171,8 +191,11 @@ def w4a16_pack(q, zeros, scales, G: int, packed=None, stream=None):
     nbytes = w4a16_packed_bytes(K, N, G)
     if packed is None:
         packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    if zeros.shape != (K // G, N) or scales.shape != (K // G, N):
+    if tuple(zeros.shape) != (K // G, N) or tuple(scales.shape) != (K // G, N):
         raise ValueError("zeros and scales must be [K/G][N]")
+    _same_device(("q", q), ("zeros", zeros), ("scales", scales), ("packed", packed))
+    if nbytes:
+        _check_packed(packed, K, N, G)
     _check(lib().w4a16_pack(_dev_ptr(q, torch.uint8, "q"), _dev_ptr(zeros, torch.uint8, "zeros"),
                             _dev_ptr(scales, torch.float16, "scales"), K, N, G,
                             _dev_ptr(packed, torch.uint8, "packed"), _stream(stream, q.device)))
@@ -203,6 +226,9 @@ def w4a16_quantize_pack(W, G: int, packed=None, stream=None):
     nbytes = w4a16_packed_bytes(K, N, G)
     if packed is None:
         packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    _same_device(("W", W), ("packed", packed))
+    if nbytes:
+        _check_packed(packed, K, N, G)
     _check(lib().w4a16_quantize_pack(_dev_ptr(W, torch.float16, "W"), K, N, G,
                                      _dev_ptr(packed, torch.uint8, "packed"), _stream(stream, W.device)))
     return packed
@@ -309,6 +335,8 @@ def w4a16_unpack(packed, K: int, N: int, G: int, stream=None):
     """Inverse of w4a16_pack: (q, zeros, scales) device tensors."""
     import torch
     dev = packed.device
+    if w4a16_packed_bytes(K, N, G):
+        _check_packed(packed, K, N, G)
     q = torch.empty((K, N), dtype=torch.uint8, device=dev)
     z = torch.empty((K // G, N), dtype=torch.uint8, device=dev)
     s = torch.empty((K // G, N), dtype=torch.float16, device=dev)
@@ -327,6 +355,9 @@ def w4a16_gemm(X, packed, N: int, K: int, G: int, Y=None, stream=None):
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     elif tuple(Y.shape) != (M, N):
         raise ValueError("Y must be [M][N]")
+    _same_device(("X", X), ("packed", packed), ("Y", Y))
+    if w4a16_packed_bytes(K, N, G):
+        _check_packed(packed, K, N, G)
     _check(lib().w4a16_gemm(_dev_ptr(X, torch.float16, "X"), _dev_ptr(packed, torch.uint8, "packed"),
                             M, N, K, G, _dev_ptr(Y, torch.float16, "Y"), _stream(stream, X.device)))
     return Y
@@ -344,6 +375,9 @@ def w4a16_gemm_ex(X, packed, N: int, K: int, G: int, Y=None, workspace=None,
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
     elif tuple(Y.shape) != (M, N):
         raise ValueError("Y must be [M][N]")
+    _same_device(("X", X), ("packed", packed), ("Y", Y), ("workspace", workspace))
+    if w4a16_packed_bytes(K, N, G):
+        _check_packed(packed, K, N, G)
     ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib().w4a16_gemm_ex(_dev_ptr(X, torch.float16, "X"), _dev_ptr(packed, torch.uint8, "packed"),

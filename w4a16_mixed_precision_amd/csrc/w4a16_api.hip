@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <vector>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -34,9 +35,14 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // M
 constexpr int64_t kMaxKN = (int64_t)1 << 22;   // K and N (32-bit buffer offsets)
+// The prefill kernel reaches the whole packed weight region through one
+// buffer descriptor with a 32-bit byte count and 32-bit tile offsets, so the
+// 4-bit weights must stay below 2^31 bytes.
+constexpr int64_t kMaxWeightBytes = (int64_t)1 << 31;
 
 bool shape_ok(int64_t K, int64_t N, int64_t G) {
     if (K <= 0 || N <= 0 || K > kMaxKN || N > kMaxKN) return false;
+    if (K * N / 2 >= kMaxWeightBytes) return false;
     if (K % 128 != 0 || N % 16 != 0) return false;
     if (G != 32 && G != 64 && G != 128 && G != 256) return false;
     return K % G == 0;
@@ -46,7 +52,7 @@ int check_shape(int64_t K, int64_t N, int64_t G) {
     if (!shape_ok(K, N, G))
         return fail(W4A16_ERR_SHAPE,
                     "unsupported shape K=%lld N=%lld G=%lld (need K%%128==0, N%%16==0, "
-                    "G in {32,64,128,256}, K%%G==0)",
+                    "G in {32,64,128,256}, K%%G==0, K and N <= 2^22, K*N/2 < 2^31)",
                     (long long)K, (long long)N, (long long)G);
     return W4A16_OK;
 }
@@ -60,6 +66,9 @@ struct DeviceState {
     int *flag = nullptr;       // pack range / quantizer finiteness error word (pinned host memory)
     void *ws = nullptr;        // w4a16_gemm split-K workspace
     size_t ws_bytes = 0;
+    // Workspaces outgrown by a larger plan. They are never freed: work
+    // already enqueued (or captured into a graph) may still use them.
+    std::vector<void *> retired;
 };
 
 DeviceState g_dev[kMaxDevices];
@@ -116,17 +125,25 @@ int run_flagged(hipStream_t st, const char *what, Launch &&launch_fn, bool *rais
     return W4A16_OK;
 }
 
-// Grows the per-device split-K workspace to at least `bytes`.
-int device_workspace(int dev, size_t bytes, void **ws) {
+// Grows the per-device split-K workspace to at least `bytes`. A buffer that a
+// larger plan outgrows is retired, not freed, so that work already enqueued
+// or captured into a HIP graph keeps valid memory; growing is refused while
+// `stream` is being captured (a capture must not allocate).
+int device_workspace(int dev, size_t bytes, void **ws, hipStream_t stream) {
     DeviceState &d = g_dev[dev];
     std::lock_guard<std::mutex> lk(d.mu);
     if (d.ws_bytes < bytes) {
-        if (d.ws) {
-            hipError_t e = hipFree(d.ws);  // synchronizes the device
-            if (e != hipSuccess) return fail_hip(e, "hipFree(workspace)");
-            d.ws = nullptr;
-            d.ws_bytes = 0;
-        }
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t ce = hipStreamIsCapturing(stream, &cs);
+        if (ce != hipSuccess) return fail_hip(ce, "hipStreamIsCapturing");
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(W4A16_ERR_WORKSPACE,
+                        "w4a16_gemm needs a larger library workspace (%zu bytes) during stream capture; "
+                        "run the shape once before capturing, or use w4a16_gemm_ex with a caller workspace",
+                        bytes);
+        if (d.ws) d.retired.push_back(d.ws);
+        d.ws = nullptr;
+        d.ws_bytes = 0;
         size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
         hipError_t e = hipMalloc(&d.ws, want);
         if (e != hipSuccess) return fail_hip(e, "hipMalloc(workspace)");
@@ -204,7 +221,10 @@ int run_quantizer(hipStream_t st, Launch &&launch_fn) {
     bool raised = false;
     int rc = run_flagged(st, "quantize launch", launch_fn, &raised);
     if (rc) return rc;
-    if (raised) return fail(W4A16_ERR_RANGE, "a weight is not finite (Inf or NaN)");
+    if (raised)
+        return fail(W4A16_ERR_RANGE,
+                    "a weight is not finite (Inf or NaN), or a group's codes dequantize beyond the fp16 range "
+                    "(|(q - z) * s| >= 65520)");
     g_last_error[0] = 0;
     return W4A16_OK;
 }
@@ -231,7 +251,10 @@ int w4a16_pack(const uint8_t *q, const uint8_t *zeros, const uint16_t *scales, i
         return w4a16::launch_pack(q, zeros, scales, (int)K, (int)N, (int)G, (uint8_t *)packed, flag, st);
     }, &host_flag);
     if (rc) return rc;
-    if (host_flag) return fail(W4A16_ERR_RANGE, "a q or zero code is larger than 15");
+    if (host_flag)
+        return fail(W4A16_ERR_RANGE,
+                    "a q or zero code is larger than 15, or a dequantized weight (q - z) * s is not a finite "
+                    "fp16 value (non-finite scale, or |(q - z) * s| >= 65520)");
     g_last_error[0] = 0;
     return W4A16_OK;
 }
@@ -448,7 +471,7 @@ int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int6
     if ((rc = make_plan(M, N, K, G, W4A16_PATH_AUTO, 0, cus, &p))) return rc;
     void *ws = nullptr;
     const size_t need = plan_workspace(p, M, N, K, G, cus);
-    if (need && (rc = device_workspace(dev, need, &ws))) return rc;
+    if (need && (rc = device_workspace(dev, need, &ws, (hipStream_t)stream))) return rc;
     return launch(X, packed, M, N, K, G, Y, ws, p, cus, (hipStream_t)stream);
 }
 

@@ -140,6 +140,30 @@ constexpr uint32_t kRoundMagicBits = 0x4B400000u;  // its bit pattern
 // Smallest normal fp16 (2^-14): the floor of the quantizers' scales.
 constexpr float kScaleFloor = 6.103515625e-05f;
 
+// 1.5 * 2^23 + rint(x / s): the nearest integer to the exact quotient, ties
+// to even, for an fp16 value x and a normal float32 scale s (inv = fp32(1/s),
+// half_s = s / 2), valid while |x / s| < 2^12 (larger quotients only move
+// further past any clamp of the result).
+// The fused multiply-add rounds the exact product x * inv once to an integer
+// c; since |x * inv - x / s| <= |x / s| 2^-24, c is rint(x / s) or its
+// neighbour across a half-integer within that distance (for an fp16 scale
+// only an exact tie qualifies: a quotient of two fp16 numbers that is not a
+// half-integer lies at least 2^-12 from every half-integer). The residual
+// r = x - c s is exact in float32 in every case that matters (|r| < s, and
+// the exponents of x and c s differ by less than the float32 precision
+// unless |x / s| < 1/2, where c = 0 and r = x), so comparing |r| with s / 2
+// settles the decision: beyond it c moves one step towards x / s, at it
+// (an exact tie) the even neighbour wins.
+__device__ inline float round_quotient_magic(float x, float s, float inv, float half_s) {
+    float y = __builtin_fmaf(x, inv, kRoundMagic);
+    const float c = y - kRoundMagic;
+    const float r = __builtin_fmaf(-c, s, x);
+    const float ar = __builtin_fabsf(r);
+    const bool step = ar > half_s || (ar == half_s && (__builtin_bit_cast(uint32_t, y) & 1u));
+    y += step ? __builtin_copysignf(1.0f, r) : 0.0f;
+    return y;
+}
+
 // A raw buffer load whose offset reaches past the descriptor's byte count
 // returns zeros and makes no memory request. Kernels point loads they do not
 // need at this offset instead of branching around them, so every path

@@ -10,7 +10,7 @@ namespace w4a16 {
 
 // Offline relayout (pack) and its inverse (unpack). `bad` is a
 // device-visible int (pinned host memory) that pack sets to 1 when a code is
-// larger than 15.
+// larger than 15 or a dequantized weight (q - z) * s is not a finite fp16.
 hipError_t launch_pack(const uint8_t *q, const uint8_t *z, const uint16_t *s, int K, int N, int G,
                        uint8_t *packed, int *bad, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int G, uint8_t *q, uint8_t *z,

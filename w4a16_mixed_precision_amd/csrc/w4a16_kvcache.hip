@@ -11,9 +11,10 @@
 //
 // Scale and zero of a vector x of D = 128 numbers (L = 2^bits - 1 steps),
 // the reading the weight quantizer uses:
-//   s = fp16(max(fp32(max - min) / L, 2^-14)), inv = fp32(1 / s),
-//   z = clamp(rint(-min * inv), 0, L), c = clamp(rint(x * inv) + z, 0, L)
-// with exact products rounded once (ties to even).
+//   s = fp16(max(fp32(max - min) / L, 2^-14)),
+//   z = clamp(rint(-min / s), 0, L), c = clamp(rint(x / s) + z, 0, L)
+// with rint the nearest integer to the exact quotient, ties to even (the
+// zero by a float64 division, the codes by round_quotient_magic).
 //
 // Cache region of one (block, KV head), KC = 64 * 128 * bits / 8 bytes:
 //   [0, KC)        K codes, token-major rows of 128 codes
@@ -139,12 +140,14 @@ __device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c
     wave_range(pair, xmax, xmin);
     const float s32 = __builtin_fmaxf((xmax - xmin) / (float)L, kScaleFloor);
     const _Float16 s16 = (_Float16)s32;
-    const float inv = 1.0f / (float)s16;
-    const double zr = __builtin_rint(-(double)xmin * (double)inv);  // exact product
+    const float sf = (float)s16;
+    const float inv = 1.0f / sf, half_s = 0.5f * sf;
+    // float64 division decides rint of an fp16 quotient exactly
+    const double zr = __builtin_rint(-(double)xmin / (double)sf);
     const int z = zr < 0.0 ? 0 : (zr > (double)L ? L : (int)zr);
     const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
-    const float y0 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x0, inv, kRoundMagic), lo, hi);
-    const float y1 = __builtin_amdgcn_fmed3f(__builtin_fmaf(x1, inv, kRoundMagic), lo, hi);
+    const float y0 = __builtin_amdgcn_fmed3f(round_quotient_magic(x0, sf, inv, half_s), lo, hi);
+    const float y1 = __builtin_amdgcn_fmed3f(round_quotient_magic(x1, sf, inv, half_s), lo, hi);
     c0 = __builtin_bit_cast(uint32_t, y0) - kRoundMagicBits + z;
     c1 = __builtin_bit_cast(uint32_t, y1) - kRoundMagicBits + z;
     par = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)z << 16);

@@ -24,9 +24,20 @@ namespace {
 __device__ inline int slot_step(int j) { return 2 * (j & 1) + ((j >> 1) & 1); }
 __device__ inline int slot_k(int v, int j) { return 32 * slot_step(j) + 2 * v + (j >> 2); }
 
+// Largest |(q - z) * s| that rounds to a finite fp16 value is just below
+// 65520 (65504 is the largest fp16; 65520 is the midpoint to the next power
+// of two and rounds to infinity, ties to even).
+constexpr float kFp16Overflow = 65520.0f;
+
+// Packs the codes and checks every dequantized weight: the pages define the
+// dequantized weight as an fp16 value ("LMDeploy Guide: Fast Mixed-Precision
+// LLM Inference Engine", section 3, FP16 = (INT4 - ZeroPoint) x Scale), so a
+// code above 15, a non-finite scale or a product |q - z| * |s| that rounds to
+// infinity sets `bad`. The product of a 4-bit difference and an fp16 scale
+// is exact in fp32, and the negated comparison also catches NaN.
 __global__ void __launch_bounds__(256)
-pack_weights_kernel(const uint8_t *__restrict__ q, int K, int N, u32x4 *__restrict__ out,
-                    int *__restrict__ bad) {
+pack_weights_kernel(const uint8_t *__restrict__ q, const uint8_t *__restrict__ z, const uint16_t *__restrict__ s,
+                    int K, int N, int G, u32x4 *__restrict__ out, int *__restrict__ bad) {
     const int64_t slots = (int64_t)K * N / 32;
     const int nblk = K / kBlockK;
     for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < slots;
@@ -39,6 +50,7 @@ pack_weights_kernel(const uint8_t *__restrict__ q, int K, int N, u32x4 *__restri
         const int kbase = blk * kBlockK + 8 * (lane >> 4);
         u32x4 v;
         uint32_t over = 0;
+        bool out_of_range = false;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             uint32_t word = 0;
@@ -46,13 +58,17 @@ pack_weights_kernel(const uint8_t *__restrict__ q, int K, int N, u32x4 *__restri
             for (int j = 0; j < 8; ++j) {
                 const int k = kbase + slot_k(w, j);
                 const uint32_t c = q[(int64_t)k * N + n];
+                const int64_t gi = (int64_t)(k / G) * N + n;
+                const float sc = (float)__builtin_bit_cast(_Float16, s[gi]);
+                const float d = (float)((int)(c & 15u) - (int)(z[gi] & 15u));
+                out_of_range |= !(__builtin_fabsf(d * sc) < kFp16Overflow);
                 over |= c;
                 word |= (c & 15u) << (4 * j);
             }
             v[w] = word;
         }
         out[idx] = v;
-        if (over > 15u) *bad = 1;
+        if (over > 15u || out_of_range) *bad = 1;
     }
 }
 
@@ -137,7 +153,7 @@ hipError_t launch_pack(const uint8_t *q, const uint8_t *z, const uint16_t *s, in
     uint16_t *sout = reinterpret_cast<uint16_t *>(packed + weight_bytes(K, N));
     uint8_t *zout = packed + weight_bytes(K, N) + scale_bytes(K, N, G);
     const int64_t slots = (int64_t)K * N / 32;
-    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(slots)), dim3(256), 0, stream, q, K, N,
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(grid_for(slots)), dim3(256), 0, stream, q, z, s, K, N, G,
                        wout, bad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -10,31 +10,41 @@
 // ("LMDeploy Guide: Fast Mixed-Precision LLM Inference Engine", section 3),
 // and call the plain form round-to-nearest ("LMDeploy" interview notes, the
 // answer on AWQ versus naive RTN INT4). The scale and zero follow the plain
-// asymmetric reading: the group's range [min, max] spread over 15 steps.
+// asymmetric reading: the group's range [min, max] spread over 15 steps, and
+// every weight goes to the code nearest to it.
 //   s   = fp16(max(fp32(fp32(max - min) / 15), 2^-14))
-//   inv = fp32(1 / s)
-//   z   = clamp(rint(-min * inv), 0, 15)      (exact product, one rounding)
-//   q   = clamp(rint(w * inv) + z, 0, 15)     (exact product, one rounding)
-// rint rounds to nearest, ties to even.
+//   z   = clamp(rint(-min / s), 0, 15)
+//   q   = clamp(rint(w / s) + z, 0, 15)
+// rint is the nearest integer to the exact quotient, ties to even. A group
+// whose codes dequantize beyond fp16 (|(q - z) s| >= 65520) has no valid
+// encoding and sets the status word, as a non-finite weight does.
 //
 // One pass over W, bound by HBM: a workgroup stages a KB x CB tile of W in
 // LDS (KB = max(128, G) rows, CB columns), takes each column's group minimum
 // and maximum with packed fp16 min/max over row slices, turns them into
-// (s, inv, z) per group and column, and then either
+// (s, 1/s, z) per group and column (z and the range check by float64
+// division, which decides rint exactly for these operands), and then either
 //   - packed output: each wave builds the 1 KiB tiles of its 16-column
 //     strips (one 16-byte store per lane, the bytes the GEMM's lane loads)
 //     and the scale and zero records, or
 //   - plain output: q[K][N] (one byte per code), z[K/G][N], s[K/G][N].
 //
-// Code decision in three VALU operations per weight. Adding 1.5 * 2^23 in
-// float32 rounds any |x| < 2^22 to an integer with ties to even, so
-// y = fma(w, inv, 1.5 * 2^23) is 1.5 * 2^23 + rint(w * inv) with the exact
-// product rounded once; larger |w * inv| move y monotonically past the clamp
-// bounds. y is clamped to [1.5 * 2^23 - z, 1.5 * 2^23 - z + 15]; in that
-// binade the float's bit pattern is bits(1.5 * 2^23) - z + code, so the
-// packed word is the sum of bits(y) << shift over its eight nibbles plus one
-// per-lane constant that removes bits(1.5 * 2^23) - z from every nibble
-// (all modulo 2^32, the nibbles never carry into each other).
+// Code decision per weight (code_float below). Adding 1.5 * 2^23 in float32
+// rounds any |x| < 2^22 to an integer with ties to even, so
+// y = fma(w, fp32(1/s), 1.5 * 2^23) is 1.5 * 2^23 + c with c the exact
+// product w * fp32(1/s) rounded once. With w = a 2^x and s = b 2^y (a, b
+// below 2^11, s normal), a quotient w / s that is not a half-integer lies at
+// least 2^-12 from every half-integer, and |w * fp32(1/s) - w / s| <=
+// |w / s| 2^-24 < 2^-12 wherever the code is not saturated (|w / s| < 2^12),
+// so c = rint(w / s) except at an exact tie, where the inexact reciprocal
+// may land on either side. The residual w - c s is exact in float32 there
+// (at most 12 significant bits above the lower of the two exponents), equals
+// +-s/2 exactly at a tie, and then the even neighbour of c wins. y is then
+// clamped to [1.5 * 2^23 - z, 1.5 * 2^23 - z + 15]; in that binade the
+// float's bit pattern is bits(1.5 * 2^23) - z + code, so the packed word is
+// the sum of bits(y) << shift over its eight nibbles plus one per-lane
+// constant that removes bits(1.5 * 2^23) - z from every nibble (all modulo
+// 2^32, the nibbles never carry into each other).
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -45,11 +55,20 @@ constexpr int kQThreads = 256;
 
 // Per (group, column) parameters of the code decision.
 struct QParams {
-    float inv;    // 1 / s
-    float lo;     // 1.5 * 2^23 - z
-    float hi;     // lo + 15
-    uint32_t zb;  // z - bits(1.5 * 2^23)
+    float inv;     // fp32(1 / s)
+    float lo;      // 1.5 * 2^23 - z
+    float hi;      // lo + 15
+    uint32_t zb;   // z - bits(1.5 * 2^23)
+    float s;       // the stored scale, in float32
+    float half_s;  // s / 2 (exact)
 };
+
+// 1.5 * 2^23 + clamp(rint(w / s) + z, 0, 15) as a float (see the header
+// comment: one fused multiply-add gives rint of the reciprocal product, and
+// the exact residual moves an exact tie to its even neighbour).
+__device__ inline float code_float(float w, const QParams &p) {
+    return __builtin_amdgcn_fmed3f(round_quotient_magic(w, p.s, p.inv, p.half_s), p.lo, p.hi);
+}
 
 template <int KB, int CB>
 struct QuantGeom {
@@ -149,15 +168,24 @@ quantize_kernel(const uint16_t *__restrict__ W, int K, int N, uint8_t *__restric
             if (!__builtin_isfinite(wmax) || !__builtin_isfinite(wmin)) *bad = 1;
             const float s32 = __builtin_fmaxf((wmax - wmin) / 15.0f, kScaleFloor);
             const _Float16 s16 = (_Float16)s32;
-            const float inv = 1.0f / (float)s16;
-            // -wmin * inv is exact in double (11 + 24 significant bits)
-            const double zr = __builtin_rint(-(double)wmin * (double)inv);
+            const float sf = (float)s16;
+            const double sd = (double)sf;
+            // float64 division decides rint of these quotients exactly (see the
+            // header comment; |w / s| < 2^31 for fp16 w and s >= 2^-14)
+            const double zr = __builtin_rint(-(double)wmin / sd);
             const int z = zr < 0.0 ? 0 : (zr > 15.0 ? 15 : (int)zr);
+            // codes are monotone in w: the group's extremes bound |q - z|
+            const double qlo = __builtin_fmin(__builtin_fmax(__builtin_rint((double)wmin / sd) + z, 0.0), 15.0);
+            const double qhi = __builtin_fmin(__builtin_fmax(__builtin_rint((double)wmax / sd) + z, 0.0), 15.0);
+            const double dmax = __builtin_fmax(__builtin_fabs(qlo - z), __builtin_fabs(qhi - z));
+            if (!(dmax * sd < 65520.0)) *bad = 1;
             QParams pr;
-            pr.inv = inv;
+            pr.inv = 1.0f / sf;
             pr.lo = kRoundMagic - (float)z;
             pr.hi = pr.lo + 15.0f;
             pr.zb = (uint32_t)z - kRoundMagicBits;
+            pr.s = sf;
+            pr.half_s = 0.5f * sf;
             prm[g][c] = pr;
             zl[g][c] = (uint8_t)z;
             const int n = c0 + c;
@@ -212,8 +240,7 @@ quantize_kernel(const uint16_t *__restrict__ W, int K, int N, uint8_t *__restric
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
                             const _Float16 h = *reinterpret_cast<const _Float16 *>(src + j * Geo::kStride);
-                            float y = __builtin_fmaf((float)h, pt[t].inv, kRoundMagic);
-                            y = __builtin_amdgcn_fmed3f(y, pt[t].lo, pt[t].hi);
+                            const float y = code_float((float)h, pt[t]);
                             word[j >> 1] += __builtin_bit_cast(uint32_t, y) << nibble_shift(t, j & 1);
                         }
                     }
@@ -239,8 +266,7 @@ quantize_kernel(const uint16_t *__restrict__ W, int K, int N, uint8_t *__restric
                         const int c = cc + 4 * d + b;
                         const QParams pr = prm[g][c];
                         const _Float16 h = *reinterpret_cast<const _Float16 *>(src + (4 * d + b) * 2);
-                        float y = __builtin_fmaf((float)h, pr.inv, kRoundMagic);
-                        y = __builtin_amdgcn_fmed3f(y, pr.lo, pr.hi);
+                        const float y = code_float((float)h, pr);
                         word |= ((__builtin_bit_cast(uint32_t, y) + pr.zb) & 15u) << (8 * b);
                     }
                     out[d] = word;

@@ -6,9 +6,9 @@
 //
 // Reading (no formula on the pages): symmetric scales, one per output
 // channel for the weights (offline) and one per token for the activations
-// (per call): s = max|v| / 127 in float32 (1 for an all-zero vector),
-// code = clamp(rint(v * (1 / s)), -127, 127) with the exact product of the
-// fp16 value and the float32 reciprocal rounded once (ties to even).
+// (per call): s = max|v| / 127 rounded once to float32 (1 for an all-zero
+// vector), code = clamp(rint(v / s), -127, 127) with rint the nearest integer
+// to the exact quotient, ties to even (round_quotient_magic).
 // Y[m][n] = fp16(float32(float32(acc) * s_x[m]) * s_w[n]) with acc the exact
 // int32 sum of code products.
 //
@@ -37,11 +37,18 @@ typedef int int32x4 __attribute__((ext_vector_type(4)));
 constexpr int kW8Tile = 1024;   // 16 columns x 64 k
 constexpr int kW8Block = 256;   // rows of K per pipeline stage (4 MFMA steps)
 
-// code of v with reciprocal inv: rint of the exact product, clamped to
-// [-127, 127] (adding 1.5 * 2^23 rounds once; the clamp keeps the result in
-// that binade, whose bit pattern is bits(1.5 * 2^23) + code)
-__device__ inline int code8(float v, float inv) {
-    const float y = __builtin_amdgcn_fmed3f(__builtin_fmaf(v, inv, kRoundMagic), kRoundMagic - 127.f,
+// Per-vector quantities of the code decision: the scale, its float32
+// reciprocal and half of it.
+struct Q8 {
+    float s, inv, half_s;
+};
+__device__ inline Q8 q8_params(float s) { return Q8{s, 1.0f / s, 0.5f * s}; }
+
+// code of v: rint(v / s) clamped to [-127, 127] (round_quotient_magic gives
+// 1.5 * 2^23 + rint; the clamp keeps the result in that binade, whose bit
+// pattern is bits(1.5 * 2^23) + code)
+__device__ inline int code8(float v, const Q8 &p) {
+    const float y = __builtin_amdgcn_fmed3f(round_quotient_magic(v, p.s, p.inv, p.half_s), kRoundMagic - 127.f,
                                             kRoundMagic + 127.f);
     return (int)(__builtin_bit_cast(uint32_t, y) - kRoundMagicBits);
 }
@@ -65,7 +72,7 @@ __device__ inline uint16_t scale_out(int32_t acc, float sx, float sw) {
 // again.
 constexpr int kActRegChunks = 4;  // 16-byte chunks per thread kept in registers
 
-__device__ inline void quant8_store(const u32x4 &v, float inv, int8_t *dst) {
+__device__ inline void quant8_store(const u32x4 &v, const Q8 &inv, int8_t *dst) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -114,7 +121,7 @@ w8a8_quant_act_kernel(const uint16_t *__restrict__ X, int K, int8_t *__restrict_
     __syncthreads();
     amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
     const float s = amax > 0.f ? amax / 127.0f : 1.0f;
-    const float inv = 1.0f / s;
+    const Q8 inv = q8_params(s);
     if (tid == 0) xs[m] = s;
     int8_t *out = xq + (size_t)m * K;
     if (held) {
@@ -152,7 +159,7 @@ w8a8_weight_pack_kernel(const uint16_t *__restrict__ W, int K, int N, const floa
         const int strip = (int)(tile / kt), kb = (int)(tile % kt);
         const int n = strip * 16 + (lane & 15);
         const int k0 = kb * 64 + 16 * (lane >> 4);
-        const float inv = 1.0f / ws[n];
+        const Q8 inv = q8_params(ws[n]);
         u32x4 v;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
