@@ -190,3 +190,19 @@ def test_python_binding_checks_the_packed_size_before_any_launch():
     s = torch.zeros((K // G, N), dtype=torch.float16)
     with pytest.raises(ValueError, match="needs"):
         w4.w4a16_pack(q, z, s, G, packed=short)
+
+
+def test_binding_loads_the_library_on_torchs_hip_runtime():
+    """ROCm wheels of torch carry their own libamdhip64 (same soname as the
+    system one): loading libw4a16.so first would put two HIP runtimes in the
+    process and torch would see no GPU. The binding imports torch first, so
+    only torch's copy is mapped (checked in a fresh interpreter)."""
+    import subprocess
+    import sys
+    pytest.importorskip("torch")
+    code = ("import w4a16_mixed_precision_amd as w4; w4.lib(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    mapped = eval(out.stdout.strip().splitlines()[-1])
+    assert len(mapped) == 1 and "torch" in mapped[0], mapped

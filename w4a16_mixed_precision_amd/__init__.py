@@ -7,6 +7,14 @@ functions carry the C names and follow the C argument order; shapes are
 taken from the tensors where the C call needs them explicitly.
 
 If the library is not built, every call raises: there is no fallback.
+
+PyTorch wheels for ROCm carry their own HIP runtime (libamdhip64.so, the
+same soname as the system one libw4a16.so links against). Whichever copy is
+loaded first serves the whole process; if the system copy came first, the
+wheel's runtime would load beside it and torch would find no GPU. ``lib()``
+therefore imports torch before it loads libw4a16.so, so the library binds
+to torch's runtime: one HIP runtime per process, shared with the tensors
+and streams it is handed.
 """
 from __future__ import annotations
 
@@ -56,6 +64,10 @@ def lib():
     if not os.path.exists(library_path):
         raise RuntimeError(
             f"{library_path} is missing: build it with `python -m w4a16_mixed_precision_amd.build`")
+    try:  # torch's HIP runtime first (see the module docstring)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(library_path)
     P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
     L.w4a16_packed_bytes.argtypes = [I64, I64, I64]
@@ -384,3 +396,4 @@ def w4a16_gemm_ex(X, packed, N: int, K: int, G: int, Y=None, workspace=None,
                                M, N, K, G, _dev_ptr(Y, torch.float16, "Y"), ws_ptr, ws_bytes,
                                path, splits, _stream(stream, X.device)))
     return Y
+

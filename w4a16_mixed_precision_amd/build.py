@@ -58,6 +58,12 @@ def build_library(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     # every kernel's host launch stub must resolve: load the library once
+    # (after torch, whose HIP runtime the binding uses: loading the system
+    # runtime first would leave two in this process)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     try:
         ctypes.CDLL(tmp)
     except OSError as exc:
