@@ -213,6 +213,27 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
                   int path, int splits, void *stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * w4a16_gemm with the same automatic plan and kernels (results bitwise equal
+ * to w4a16_gemm's), whose split-K partials go to a fixed scratch array
+ * inside the library instead of an allocated workspace:
+ * W4A16_NOALLOC_SCRATCH_BYTES per GPU, placed when the library's code object
+ * is loaded on that GPU and held until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's address of the array. Returns
+ * W4A16_ERR_WORKSPACE, launching nothing, if the plan's partials exceed the
+ * scratch (every automatic plan fits on a 256-CU MI355X). All calls on one
+ * GPU share its scratch, which keeps the last call's partials (every plan
+ * writes each partial before reading it, so nothing needs clearing): calls
+ * that overlap on one GPU (two streams, or two threads) race; calls ordered
+ * on one stream are safe. Other arguments and errors as for w4a16_gemm.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (64u << 20)
+int w4a16_gemm_noalloc(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
+                       int64_t G, uint16_t *Y, void *stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Low-bit KV cache and decode attention (the pages' second pipeline:
  * "LMDeploy Guide: Fast Mixed-Precision LLM Inference Engine", architecture

@@ -192,6 +192,16 @@ def test_python_binding_checks_the_packed_size_before_any_launch():
         w4.w4a16_pack(q, z, s, G, packed=short)
 
 
+def test_noalloc_gemm_validation_before_any_hip_call():
+    L = w4.lib()
+    assert w4.W4A16_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert L.w4a16_gemm_noalloc(None, FAKE, 1, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_gemm_noalloc(FAKE, FAKE, 1, 250, 256, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm_noalloc(FAKE, FAKE, 0, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm_noalloc(FAKE, FAKE, 1, 65536, 65536, 128, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_gemm_noalloc(MISALIGNED, FAKE, 1, 256, 256, 128, FAKE, None) == w4.W4A16_ERR_ALIGN
+
+
 def test_binding_loads_the_library_on_torchs_hip_runtime():
     """ROCm wheels of torch carry their own libamdhip64 (same soname as the
     system one): loading libw4a16.so first would put two HIP runtimes in the

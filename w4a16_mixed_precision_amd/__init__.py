@@ -27,7 +27,7 @@ __all__ = [
     "W4A16_ERR_HIP", "W4A16_ERR_WORKSPACE", "W4A16_ERR_ARG",
     "W4A16_PATH_AUTO", "W4A16_PATH_DECODE", "W4A16_PATH_PREFILL",
     "w4a16_packed_bytes", "w4a16_pack", "w4a16_unpack", "w4a16_workspace_bytes",
-    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_status_string", "w4a16_last_error",
+    "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_noalloc", "W4A16_NOALLOC_SCRATCH_BYTES", "w4a16_status_string", "w4a16_last_error",
     "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack",
     "w4a16_kv_block_bytes", "w4a16_kv_append", "w4a16_kv_attention_workspace_bytes", "w4a16_kv_attention",
     "w4a16_w8a8_packed_bytes", "w4a16_w8a8_quantize_weights", "w4a16_w8a8_quantize_act",
@@ -45,6 +45,7 @@ W4A16_ERR_ARG = -7
 W4A16_PATH_AUTO = 0
 W4A16_PATH_DECODE = 1
 W4A16_PATH_PREFILL = 2
+W4A16_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
 _lib = None
@@ -82,6 +83,8 @@ def lib():
     L.w4a16_gemm.restype = I
     L.w4a16_gemm_ex.argtypes = [P, P, I64, I64, I64, I64, P, P, SZ, I, I, P]
     L.w4a16_gemm_ex.restype = I
+    L.w4a16_gemm_noalloc.argtypes = [P, P, I64, I64, I64, I64, P, P]
+    L.w4a16_gemm_noalloc.restype = I
     L.w4a16_status_string.argtypes = [I]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error.argtypes = []
@@ -397,3 +400,20 @@ def w4a16_gemm_ex(X, packed, N: int, K: int, G: int, Y=None, workspace=None,
                                path, splits, _stream(stream, X.device)))
     return Y
 
+
+def w4a16_gemm_noalloc(X, packed, N: int, K: int, G: int, Y, stream=None):
+    """w4a16_gemm whose split-K partials use the library's fixed per-GPU
+    scratch: the call allocates nothing (Y, the output, is the caller's).
+    Calls that overlap on one GPU share that scratch and must be ordered."""
+    import torch
+    M = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be [M][K]")
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [M][N]")
+    _same_device(("X", X), ("packed", packed), ("Y", Y))
+    if w4a16_packed_bytes(K, N, G):
+        _check_packed(packed, K, N, G)
+    _check(lib().w4a16_gemm_noalloc(_dev_ptr(X, torch.float16, "X"), _dev_ptr(packed, torch.uint8, "packed"),
+                                    M, N, K, G, _dev_ptr(Y, torch.float16, "Y"), _stream(stream, X.device)))
+    return Y

@@ -69,6 +69,7 @@ struct DeviceState {
     // Workspaces outgrown by a larger plan. They are never freed: work
     // already enqueued (or captured into a graph) may still use them.
     std::vector<void *> retired;
+    void *scratch = nullptr;   // this device's address of `scratch` (w4a16_gemm_noalloc)
 };
 
 DeviceState g_dev[kMaxDevices];
@@ -150,6 +151,29 @@ int device_workspace(int dev, size_t bytes, void **ws, hipStream_t stream) {
         d.ws_bytes = want;
     }
     *ws = d.ws;
+    return W4A16_OK;
+}
+
+// ------------------------------------------------------------- fixed scratch
+// Split-K partials of w4a16_gemm_noalloc: a fixed array in the library's code
+// object, one copy on every GPU the library runs on, held until the process
+// ends. In host code the name `scratch` is only a stand-in for the symbol:
+// kernels get this device's address of it, looked up once per device by
+// hipGetSymbolAddress with that device current, and every use in host code
+// goes through that address.
+static __device__ __align__(256) uint8_t scratch[W4A16_NOALLOC_SCRATCH_BYTES];
+
+int device_scratch(int dev, void **ptr) {
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lk(d.mu);
+    if (!d.scratch) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(W4A16_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+        d.scratch = p;
+    }
+    *ptr = d.scratch;
     return W4A16_OK;
 }
 
@@ -472,6 +496,26 @@ int w4a16_gemm(const uint16_t *X, const void *packed, int64_t M, int64_t N, int6
     void *ws = nullptr;
     const size_t need = plan_workspace(p, M, N, K, G, cus);
     if (need && (rc = device_workspace(dev, need, &ws, (hipStream_t)stream))) return rc;
+    return launch(X, packed, M, N, K, G, Y, ws, p, cus, (hipStream_t)stream);
+}
+
+int w4a16_gemm_noalloc(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K, int64_t G,
+                       uint16_t *Y, void *stream) {
+    int rc = check_gemm_args(X, packed, M, N, K, G, Y);
+    if (rc) return rc;
+    int dev, cus;
+    if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
+    Plan p;
+    if ((rc = make_plan(M, N, K, G, W4A16_PATH_AUTO, 0, cus, &p))) return rc;
+    const size_t need = plan_workspace(p, M, N, K, G, cus);
+    if (need > (size_t)W4A16_NOALLOC_SCRATCH_BYTES)
+        return fail(W4A16_ERR_WORKSPACE,
+                    "the plan for M=%lld N=%lld K=%lld G=%lld needs %zu bytes of split-K partials; the fixed "
+                    "scratch of w4a16_gemm_noalloc holds %zu (use w4a16_gemm_ex with a caller workspace)",
+                    (long long)M, (long long)N, (long long)K, (long long)G, need,
+                    (size_t)W4A16_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need && (rc = device_scratch(dev, &ws))) return rc;
     return launch(X, packed, M, N, K, G, Y, ws, p, cus, (hipStream_t)stream);
 }
 
