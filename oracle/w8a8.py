@@ -68,7 +68,15 @@ def quantize_activations(X):
 
 
 def gemm_int(qx, qw):
-    """Exact integer product [M][N] (int64)."""
+    """Exact integer product [M][N] (int64).
+
+    When K * 127 * 127 < 2^53 every product and partial sum of int8 codes is
+    an integer below 2^53 in magnitude, so a float64 matrix product (any
+    summation order) is exact and is used (numpy has no BLAS for integers);
+    otherwise the product is taken in int64."""
+    K = qx.shape[1]
+    if K * 127 * 127 < 2 ** 53:
+        return (qx.astype(np.float64) @ qw.astype(np.float64)).astype(np.int64)
     return qx.astype(np.int64) @ qw.astype(np.int64)
 
 

@@ -112,9 +112,12 @@ def test_decode_kernel_at_maximum_k():
     torch.cuda.synchronize()
 
 
-def test_full_size_llama3_8b_sampled():
+def test_full_size_llama3_8b_whole_output():
     # gate/up of the Llama-3-8B prefill (M = 2048, K = 4096, N = 28672) and
-    # a decode row block (M = 16), sampled on column windows
+    # a decode row block (M = 16): every element of Y equals the oracle's
+    # (int32 sums exact in float64 BLAS; the float32 scaling steps and the
+    # fp16 rounding are the reading's), as do the weight and activation
+    # scales and codes
     import torch
     K, N = 4096, 28672
     X, W = _inputs(2048, K, N, 99)
@@ -122,11 +125,14 @@ def test_full_size_llama3_8b_sampled():
     packed, ws = w4.w4a16_w8a8_quantize_weights(Wd)
     qw, sw = w8a8.quantize_weights(W)
     assert np.array_equal(host(ws).view(np.uint32), sw.view(np.uint32))
+    assert np.array_equal(host(packed), w8a8.pack_weights(qw))
     for M in (2048, 16):
         xq, xs = w4.w4a16_w8a8_quantize_act(dev(X[:M]))
         Y = host(w4.w4a16_w8a8_gemm(xq, xs, packed, ws, N))
         torch.cuda.synchronize()
         qx, sx = w8a8.quantize_activations(X[:M])
-        for c0 in (0, 12288, N - 64):
-            ref = w8a8.gemm(qx, sx, qw[:, c0:c0 + 64], sw[c0:c0 + 64])
-            assert np.array_equal(Y[:, c0:c0 + 64].view(np.uint16), ref.view(np.uint16)), (M, c0)
+        assert np.array_equal(host(xq), qx) and np.array_equal(host(xs).view(np.uint32), sx.view(np.uint32))
+        ref = w8a8.gemm(qx, sx, qw, sw)
+        bad = np.argwhere(Y.view(np.uint16) != ref.view(np.uint16))
+        assert bad.size == 0, (M, bad[:5])
+        say(f"  W8A8 M={M}: all {M} x {N} outputs bit-exact")

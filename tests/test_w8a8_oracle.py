@@ -74,6 +74,21 @@ def test_codes_follow_the_exact_quotient_not_a_reciprocal_product():
     assert q[1].tolist() == [127, 2, 0, 0]
 
 
+def test_integer_product_is_exact_at_the_extremes():
+    # all codes +-127 over K = 131072: sums of magnitude K * 127^2 =
+    # 2,114,060,288 and alternating-sign cancellation, exact (float64 path)
+    # and equal to the int64 product
+    K = 131072
+    qx = np.full((2, K), 127, np.int8)
+    qx[1, 1::2] = -127
+    qw = np.full((K, 3), 127, np.int8)
+    qw[::3, 2] = -127
+    got = w8a8.gemm_int(qx, qw)
+    ref = qx.astype(np.int64) @ qw.astype(np.int64)
+    assert got.dtype == np.int64 and np.array_equal(got, ref)
+    assert got[0, 0] == K * 127 * 127 and got[1, 0] == 0
+
+
 def test_integer_product_against_loops():
     rng = np.random.default_rng(3)
     qx = rng.integers(-127, 128, (3, 40)).astype(np.int8)
