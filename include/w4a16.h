@@ -351,6 +351,17 @@ int w4a16_w8a8_gemm(const int8_t *xq, const float *x_scales, const void *packed,
                     int64_t M, int64_t N, int64_t K, uint16_t *Y, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/*
+ * Measurement yardstick, not part of the GEMM: one kernel launch that reads
+ * `bytes` bytes of the device buffer `buf` (16-byte loads, each byte once,
+ * non-temporal) and nothing else, the plainest bound on a launch that
+ * streams that many bytes ("LMDeploy" interview notes: each decode step
+ * streams every weight byte once). Folds the data into one word per lane and
+ * writes it to `sink` (64 uint32, device) only where it equals `never`, so
+ * in practice nothing is written. 0 < bytes < 2^32. Asynchronous on `stream`.
+ */
+int w4a16_stream_read(const void *buf, size_t bytes, uint32_t never, uint32_t *sink, void *stream);
+
 /* Static description of a status code. */
 const char *w4a16_status_string(int status);
 

@@ -1,11 +1,10 @@
 """Randomised parity: seeded random shapes (K a multiple of 128 and of G, N a
 multiple of 16, every G, M from 1 to 600) through the automatic plan and
-both forced paths, checked against the oracle on sampled column windows
-(the oracle computes a column slice exactly as inside the full product).
+both forced paths, checked against the oracle over the whole output.
 
 The shapes are drawn so that every decode X mode and ring size, split and
 unsplit K, narrow and wide N and both sides of the automatic path rule are
-reached, at sizes the oracle finishes in well under a second per window.
+reached, at sizes the oracle finishes in about a second per shape.
 """
 import numpy as np
 import pytest
@@ -34,13 +33,6 @@ def _cases(n=36, seed=2024):
     return out
 
 
-def _windows(N, rng):
-    if N <= 64:
-        return [(0, N)]
-    starts = {0, N - 32, int(rng.integers(0, (N - 32) // 16 + 1)) * 16}
-    return [(c, c + 32) for c in sorted(starts)]
-
-
 @pytest.mark.parametrize("i,M,K,N,G", _cases())
 def test_random_shapes(i, M, K, N, G):
     import torch
@@ -49,8 +41,7 @@ def test_random_shapes(i, M, K, N, G):
     X = synth.draw_x(rng, M, K)
     packed = w4.w4a16_pack(dev(q), dev(z), dev(s), G)
     paths = [AUTO, PREFILL] + ([DECODE] if M <= 64 else [])
-    wins = _windows(N, np.random.default_rng(i))
-    refs = [oracle.gemm(X, q, z, s, G, cols=w) for w in wins]
+    ref = oracle.gemm(X, q, z, s, G)
     Xd = dev(X)
     for path in paths:
         nbytes = w4.w4a16_workspace_bytes(M, N, K, G, path, 0)
@@ -58,14 +49,9 @@ def test_random_shapes(i, M, K, N, G):
         Y = host(w4.w4a16_gemm_ex(Xd, packed, N, K, G, workspace=ws, path=path))
         torch.cuda.synchronize()
         assert np.isfinite(Y.astype(np.float32)).all(), (i, path)
-        dmax = rmax = dsq = rsq = 0.0
-        for (c0, c1), ref in zip(wins, refs):
-            d = Y[:, c0:c1].astype(np.float64) - ref
-            dmax = max(dmax, float(np.abs(d).max()))
-            rmax = max(rmax, float(np.abs(ref).max()))
-            dsq += float((d * d).sum())
-            rsq += float((ref * ref).sum())
-        rel_max, rel_fro = dmax / rmax, (dsq / rsq) ** 0.5
+        d = Y.astype(np.float64) - ref
+        rel_max = float(np.abs(d).max()) / float(np.abs(ref).max())
+        rel_fro = float(np.linalg.norm(d)) / float(np.linalg.norm(ref))
         say(f"  path={path}: rel_max={rel_max:.2e} rel_fro={rel_fro:.2e}")
         assert rel_max <= TOL_MAX, (i, path, rel_max)
         assert rel_fro <= TOL_FRO, (i, path, rel_fro)

@@ -31,7 +31,7 @@ __all__ = [
     "w4a16_layout_version", "w4a16_auto_path", "w4a16_quantize", "w4a16_quantize_pack",
     "w4a16_kv_block_bytes", "w4a16_kv_append", "w4a16_kv_attention_workspace_bytes", "w4a16_kv_attention",
     "w4a16_w8a8_packed_bytes", "w4a16_w8a8_quantize_weights", "w4a16_w8a8_quantize_act",
-    "w4a16_w8a8_workspace_bytes", "w4a16_w8a8_gemm",
+    "w4a16_w8a8_workspace_bytes", "w4a16_w8a8_gemm", "w4a16_stream_read",
 ]
 
 W4A16_OK = 0
@@ -115,6 +115,8 @@ def lib():
     L.w4a16_w8a8_gemm.argtypes = [P, P, P, P, I64, I64, I64, P, P, SZ, P]
     L.w4a16_w8a8_gemm.restype = I
     L.w4a16_auto_path.restype = I
+    L.w4a16_stream_read.argtypes = [P, SZ, ctypes.c_uint32, P, P]
+    L.w4a16_stream_read.restype = I
     _lib = L
     return L
 
@@ -417,3 +419,20 @@ def w4a16_gemm_noalloc(X, packed, N: int, K: int, G: int, Y, stream=None):
     _check(lib().w4a16_gemm_noalloc(_dev_ptr(X, torch.float16, "X"), _dev_ptr(packed, torch.uint8, "packed"),
                                     M, N, K, G, _dev_ptr(Y, torch.float16, "Y"), _stream(stream, X.device)))
     return Y
+
+
+def w4a16_stream_read(buf, sink, nbytes=None, never: int = 0x9E3779B9, stream=None):
+    """Read `nbytes` (default: all) bytes of the device tensor `buf` in one
+    launch and nothing else (the achievable-bandwidth yardstick); `sink` is a
+    device tensor of at least 64 uint32 (written only if the data fold to
+    `never`). Asynchronous."""
+    import torch
+    have = buf.numel() * buf.element_size()
+    n = have if nbytes is None else int(nbytes)
+    if n > have:
+        raise ValueError(f"buf holds {have} bytes, asked to read {n}")
+    if sink.numel() * sink.element_size() < 256:
+        raise ValueError("sink must hold 64 uint32")
+    _same_device(("buf", buf), ("sink", sink))
+    _check(lib().w4a16_stream_read(_dev_ptr(buf, None, "buf"), n, never & 0xFFFFFFFF,
+                                   _dev_ptr(sink, None, "sink"), _stream(stream, buf.device)))

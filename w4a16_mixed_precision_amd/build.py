@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["w4a16_api.hip", "w4a16_pack.hip", "w4a16_quantize.hip", "w4a16_kvcache.hip", "w4a16_w8a8.hip", "w4a16_decode.hip", "w4a16_prefill.hip"]
+SOURCES = ["w4a16_api.hip", "w4a16_pack.hip", "w4a16_quantize.hip", "w4a16_kvcache.hip", "w4a16_w8a8.hip", "w4a16_decode.hip", "w4a16_prefill.hip", "w4a16_read.hip"]
 
 
 def hipcc() -> str:

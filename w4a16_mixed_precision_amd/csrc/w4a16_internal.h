@@ -64,4 +64,7 @@ size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits);
 hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
                           uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 
+// Streaming read of `bytes` bytes of `buf` (measurement yardstick).
+hipError_t launch_stream_read(const uint8_t *buf, size_t bytes, uint32_t never, uint32_t *sink, hipStream_t stream);
+
 }  // namespace w4a16
