@@ -39,6 +39,10 @@ Prints ONE JSON line:
                M=2048, K=4096, N=28672
   fp16_library (default run, context) the same shapes as dense fp16 GEMMs
                through torch.matmul, and the W4A16 speedup over them
+  other_workloads (default run) every instance of the tiny case, the
+               Llama-3-70B layer M sweep, the Qwen2.5-72B-shaped G=64 pair and
+               the 70B tensor-parallel shard, timed the same way, with the
+               fraction of whichever roofline (HBM or fp16 MFMA) bounds it
 """
 from __future__ import annotations
 
@@ -64,6 +68,8 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=0, help="timed steps (default: one rotation, at least 40)")
     p.add_argument("--warmup", type=int, default=0, help="untimed steps (default: one rotation)")
     p.add_argument("--workload", default="llama3_8b_decode")
+    p.add_argument("--instance", default="",
+                   help="comma-separated instance names (workload/matrix/M...): run only these (profiling)")
     p.add_argument("--rotate-gib", type=float, default=1.0,
                    help="minimum bytes of distinct copies per weight matrix that steps cycle through")
     p.add_argument("--eager", action="store_true", help="time Python-driven launches, no graphs")
@@ -86,7 +92,7 @@ def parse_args(argv=None):
 class Runner:
     """Device-resident copies of one workload and its launch sequence."""
 
-    def __init__(self, insts, rotate_bytes):
+    def __init__(self, insts, rotate_bytes, max_copies=None):
         import numpy as np
         import torch
 
@@ -99,15 +105,24 @@ class Runner:
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")  # noqa: E731
         keys, base = [], {}
         self.host = {}
+        drawn = {}
         for inst in insts:
             key = (inst.workload, inst.matrix, inst.K, inst.N, inst.G, inst.outliers, inst.seed)
             keys.append(key)
-            X, q, z, s = synth.draw(inst)
-            self.host[inst.name] = (X, q, z, s)
-            if key not in base:
+            if key not in drawn:
+                # one draw per matrix at the largest M of the run: X of a
+                # smaller M is the leading rows of the same draw (synth.draw
+                # of that instance gives the same values)
+                Mmax = max(i.M for i in insts if (i.workload, i.matrix, i.K, i.N, i.G, i.outliers, i.seed) == key)
+                q, z, s, idx, rng = synth.draw_weights(inst.K, inst.N, inst.G, inst.seed, inst.outliers)
+                drawn[key] = (synth.draw_x(rng, Mmax, inst.K, idx), q, z, s)
                 base[key] = w4.w4a16_pack(to(q), to(z), to(s), inst.G)
+            Xall, q, z, s = drawn[key]
+            self.host[inst.name] = (np.ascontiguousarray(Xall[: inst.M]), q, z, s)
         smallest = min(b.numel() for b in base.values())
         self.copies = max(2, math.ceil(rotate_bytes / smallest))
+        if max_copies:
+            self.copies = min(self.copies, max_copies)
         self.packed = {k: [b] + [b.clone() for _ in range(self.copies - 1)] for k, b in base.items()}
         self.xs, self.ys, self.ws, self.mat_of = [], [], [], []
         for inst, key in zip(insts, keys):
@@ -311,6 +326,55 @@ def copy_rate(nbytes=2 ** 30, reps=10):
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+OTHER_WORKLOADS = ("tiny", "llama3_70b_layer", "qwen25_72b_mixed", "llama3_70b_tp8_shard")
+
+
+def roofline_row(inst, us):
+    """Per-instance figures against both MI355X ceilings: the instance is
+    bound by whichever of HBM (algorithmic bytes at 8 TB/s) and fp16 MFMA
+    (2 M N K at 2.5 PFLOP/s) takes longer; roofline_frac = that time /
+    measured time."""
+    t_hbm = inst.alg_bytes() / (HBM_PEAK_GBS * 1e9)
+    t_mfma = inst.flops() / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {
+        "TBps": inst.alg_bytes() / (us * 1e-6) / 1e12,
+        "TFLOPs": inst.flops() / (us * 1e-6) / 1e12,
+        "frac_of_hbm_peak": t_hbm / (us * 1e-6),
+        "frac_of_mfma_f16_peak": t_mfma / (us * 1e-6),
+        "bound": bound,
+        "roofline_frac": max(t_hbm, t_mfma) / (us * 1e-6),
+    }
+
+
+def run_other_workloads(args):
+    """Every instance of the other synthetic workloads (the tiny case, the
+    Llama-3-70B layer M sweep, the Qwen2.5-72B-shaped G=64 pair, one GPU's
+    8-way tensor-parallel shard of the 70B layer), timed like the step's
+    instances: automatic plan through the C ABI, weight copies rotated over
+    --rotate-gib GiB (at most 64 copies for the tiny case), HIP graph
+    replay, HIP events."""
+    import torch
+
+    import synth
+    out = []
+    for wl in OTHER_WORKLOADS:
+        insts = synth.workload_instances(wl)
+        r = Runner(insts, args.rotate_gib * 2 ** 30, max_copies=64 if wl == "tiny" else None)
+        for k, inst in enumerate(insts):
+            ms = r.time_steps(2 * r.copies, r.copies, args.eager, only=k)
+            row = {"instance": inst.name, "M": inst.M, "K": inst.K, "N": inst.N, "G": inst.G,
+                   "us": ms * 1e3, "kernel": kernel_name(inst), "rotation_copies": r.copies}
+            row.update(roofline_row(inst, ms * 1e3))
+            out.append(row)
+            if args.detail:
+                print(json.dumps(row), file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+    return {"timing": "per instance: HIP graph replay over rotated copies, HIP events, automatic plan",
+            "instances": out}
 
 
 def run_prefill_secondary(args):
@@ -593,6 +657,13 @@ def main(argv=None):
             print(json.dumps(run_kv_secondary(args, bits)), flush=True)
         return 0
     insts = synth.workload_instances(args.workload)
+    if args.instance:
+        want = args.instance.split(",")
+        unknown = [w for w in want if w not in [i.name for i in insts]]
+        if unknown:
+            print(f"unknown instance(s) of {args.workload}: {unknown}", file=sys.stderr)
+            return 2
+        insts = [i for i in insts if i.name in want]
     prefill = all(i.M > 32 for i in insts)
     # The metric is quoted at M = 1..16 (decode) and M >= 2048 (prefill): a
     # step is one pass over the workload's instances in that range; the rest
@@ -706,6 +777,7 @@ def main(argv=None):
         out["kv_attention"] = [run_kv_secondary(args, 8), run_kv_secondary(args, 4)]
         out["w8a8"] = run_w8a8_secondary(args)
         out["fp16_library"] = run_fp16_library(args, rows, out["secondary"]["ms_per_launch"])
+        out["other_workloads"] = run_other_workloads(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(runner, in_metric)
     print(json.dumps(out), flush=True)
