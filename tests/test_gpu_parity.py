@@ -224,6 +224,39 @@ def test_decode_x_modes(monkeypatch, M, K, N, G, splits, xm, ns, wk):
     assert_parity(Y, oracle.gemm(X, q, z, s, G), f"xm={xm} ns={ns} wk={wk} M={M} K={K} N={N} G={G}")
 
 
+# Scale and zero records loaded with each batch of weight tiles (the plans
+# whose runs fit in the two batches issued up front) or staged in LDS per
+# wave: the same arithmetic, so the two agree bit for bit, at every group
+# size and X mode (forced here for every run length).
+RB_CASES = [
+    # (M, K, N, G, splits, xm)
+    (1, 4096, 6144, 128, 0, 1),
+    (1, 1024, 400, 32, 0, 1),
+    (1, 2304, 784, 256, 2, 1),
+    (4, 1152, 272, 64, 0, 1),
+    (8, 4096, 1040, 128, 1, 2),
+    (8, 2048, 512, 32, 3, 2),
+    (13, 640, 336, 64, 0, 2),
+    (16, 4096, 6144, 128, 0, 2),
+    (16, 2304, 784, 256, 1, 2),
+]
+
+
+@pytest.mark.parametrize("M,K,N,G,splits,xm", RB_CASES)
+def test_decode_records_with_batches(monkeypatch, M, K, N, G, splits, xm):
+    monkeypatch.setenv("W4A16_DECODE_XM", str(xm))
+    say(f"decode records with batches: M={M} K={K} N={N} G={G} splits={splits} xm={xm}")
+    q, z, s, rng = _weights(K, N, G, seed=M * 7 + K + N + G)
+    X = synth.draw_x(rng, M, K)
+    packed = pack_dev(q, z, s, G)
+    out = {}
+    for rb in (0, 1):
+        monkeypatch.setenv("W4A16_DECODE_RB", str(rb))
+        out[rb] = run_gemm(X, packed, N, K, G, path=DECODE, splits=splits)
+    assert np.array_equal(out[0].view(np.uint16), out[1].view(np.uint16)), (M, K, N, G, splits, xm)
+    assert_parity(out[1], oracle.gemm(X, q, z, s, G), f"rb M={M} K={K} N={N} G={G}")
+
+
 def test_parity_with_activation_outliers_both_paths():
     K, N, G, M = 2048, 512, 128, 48
     q, z, s, idx, rng = synth.draw_weights(K, N, G, seed=5, outliers=True)

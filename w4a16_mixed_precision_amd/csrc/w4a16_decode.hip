@@ -57,9 +57,14 @@ struct SZ {
     float sc;
 };
 
-template <int NS, int NB>
+// One batch of weight tiles in flight: NB blocks of the wave's NS strips,
+// and with RB the scale and zero-code of every group the batch's blocks
+// start (one fp16 scale and one byte holding the zero nibble per lane).
+template <int NS, int NB, int NF, bool RB>
 struct DecodeBatch {
     u32x4 w[NB][NS];
+    uint32_t sc[RB ? NB : 1][NS][NF];
+    uint32_t zb[RB ? NB : 1][NS][NF];
 };
 
 // Dynamic LDS: one private region per wave, back to back, holding the
@@ -85,12 +90,12 @@ constexpr int kXRun = 1;  // the wave's run of X staged in LDS up front
 // many rows (8 for M <= 8, else 16 per 16-row MFMA tile)
 
 __host__ __device__ inline DecodeLds decode_lds(int M, int MT, int NS, int WK, int slice_blocks, int G,
-                                                 int xm) {
+                                                 int xm, bool rb) {
     DecodeLds l;
     const int per = (slice_blocks + WK - 1) / WK;
     // a run that starts inside a group (G > 128) touches one group more
     l.ngw = (uint32_t)((per * kBlockK + G - 1) / G + (G > kBlockK ? 1 : 0));
-    l.sz_bytes = (uint32_t)(NS * l.ngw * 16 * sizeof(SZ));
+    l.sz_bytes = rb ? 0u : (uint32_t)(NS * l.ngw * 16 * sizeof(SZ));
     l.x_stride = (uint32_t)((per + 3) / 4 * 1024 + 16);
     l.wave_bytes = l.sz_bytes + (xm == kXRun ? (uint32_t)M * l.x_stride : 0u);
     l.red_bytes = (uint32_t)(WK * NS * MT * 64 * 16);
@@ -109,10 +114,14 @@ constexpr int kWeightLoadPolicy = 2;  // nt
 // fp32. rec points at the records of the first strip; strip j's records
 // start rec_stride groups later, and gbase is the group index of the first
 // record.
-template <int MT, int NS, int GS>
+// With RB the records come from the batch (bsc, bzb: [NS][NF] of block b)
+// instead of the LDS region.
+template <int MT, int NS, int GS, bool RB>
 __device__ __forceinline__ void block_mma(const half8 (&a)[4][MT], const u32x4 (&w)[NS], const SZ *rec,
                                           int rec_stride, int b, int gbase, int col, uint32_t m_lo,
-                                          uint32_t m_hi, floatx4 (&acc)[MT][NS]) {
+                                          uint32_t m_hi, const uint32_t (&bsc)[NS][GS < 4 ? 4 / GS : 1],
+                                          const uint32_t (&bzb)[NS][GS < 4 ? 4 / GS : 1],
+                                          floatx4 (&acc)[MT][NS]) {
     constexpr int F = GS < 4 ? GS : 4;  // 32-row k-steps per scale group inside a block
     constexpr int NF = 4 / F;            // scale groups per 128-row block
 #pragma unroll
@@ -122,8 +131,15 @@ __device__ __forceinline__ void block_mma(const half8 (&a)[4][MT], const u32x4 (
         for (int v = 0; v < 4; ++v) w8[v] = w[j][v] >> 8;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            const int g = (b * 4 + f * F) / GS;
-            const SZ sz = rec[(j * rec_stride + (g - gbase)) * 16 + col];
+            SZ sz;
+            if constexpr (RB) {
+                const uint32_t hz = 0xE400u | ((bzb[j][f] >> ((col & 1) * 4)) & 15u);
+                sz.nb = hz | (hz << 16);
+                sz.sc = (float)__builtin_bit_cast(_Float16, (uint16_t)bsc[j][f]);
+            } else {
+                const int g = (b * 4 + f * F) / GS;
+                sz = rec[(j * rec_stride + (g - gbase)) * 16 + col];
+            }
             const DequantConsts dc{sz.nb, neg_bias64_from_1024(sz.nb), m_lo, m_hi};
             floatx4 part[MT];
 #pragma unroll
@@ -160,12 +176,14 @@ __device__ __forceinline__ void store_records(SZ *dst, const u32x4 &sv, uint32_t
     }
 }
 
-template <int MT, int NS, int WK, int NB, int GS, int XM>
+template <int MT, int NS, int WK, int NB, int GS, int XM, bool RB>
 __global__ void __launch_bounds__(WK * 64)
 decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
               uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int S,
               int slice_blocks) {
     constexpr int G = 32 * GS;
+    constexpr int F = GS < 4 ? GS : 4;
+    constexpr int NF = 4 / F;
     constexpr bool kRun = XM == kXRun;
     constexpr bool kRing = XM >= 8;
     static_assert(!kRing || (MT == 1 && XM == 8) || XM == 16 * MT, "ring rows: 8, or 16 per row tile");
@@ -173,7 +191,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     // X copies per block: one ring copy per 4 rows (the staged run has none)
     constexpr int kXLoads = kRing ? XM / 4 : 0;
     // loads of one batch and of the two batches issued ahead of the loop
-    constexpr int kBatchLoads = NB * (NS + kXLoads);
+    constexpr int kBatchLoads = NB * (NS * (RB ? 1 + 2 * NF : 1) + kXLoads);
     static_assert(2 * kBatchLoads <= 63, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // Ring mode: slot i of ring0 (ring1) holds X rows [0, XM) of block i of
@@ -204,7 +222,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
     const int gw0 = wb * kBlockK / G;  // groups overlapping the wave's run
     const int ngw = (we * kBlockK + G - 1) / G - gw0;
 
-    const DecodeLds L = decode_lds(M, MT, NS, WK, slice_blocks, G, XM);
+    const DecodeLds L = decode_lds(M, MT, NS, WK, slice_blocks, G, XM, RB);
     SZ *szl = reinterpret_cast<SZ *>(lds + wk * L.wave_bytes);
     uint8_t *xl = lds + wk * L.wave_bytes + L.sz_bytes;
     uint8_t *xr0 = ring0 + wk * NB * kSlot;
@@ -246,7 +264,15 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[mt][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    typedef DecodeBatch<NS, NB> Batch;
+    // scale and zero-code records of the workgroup's strips (strips past N
+    // lie past the descriptors and read as zeros)
+    const int nsv = nstrip - strip0 < NS ? nstrip - strip0 : NS;  // strips that exist
+    const uint8_t *srec = packed + weight_bytes(K, N) + (size_t)strip0 * ngrp * 32;
+    const uint8_t *zrec = packed + weight_bytes(K, N) + scale_bytes(K, N, G) + (size_t)strip0 * ngrp * 8;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(srec, (uint32_t)(nsv * ngrp * 32));
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zrec, (uint32_t)(nsv * ngrp * 8));
+
+    typedef DecodeBatch<NS, NB, NF, RB> Batch;
     // Blocks at or past the end of the wave's run load from the out-of-range
     // offset: no branch, no memory traffic, and the same instruction count
     // on every path. X rows >= M are out of range of X's descriptor too.
@@ -266,9 +292,22 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                                                              (b0 + i) * kBlockK * 2 + (xi >> 2) * 32 * K, 0, 0);
             }
 #pragma unroll
-            for (int j = 0; j < NS; ++j)
+            for (int j = 0; j < NS; ++j) {
+                if constexpr (RB) {
+                    // this lane's column: its fp16 scale and the byte holding
+                    // its zero code, for each group the block starts
+#pragma unroll
+                    for (int f = 0; f < NF; ++f) {
+                        const uint32_t rec = (uint32_t)(j * ngrp + ((b0 + i) * 4 + f * F) / GS);
+                        bt.sc[i][j][f] = __builtin_amdgcn_raw_buffer_load_b16(rs, in ? rec * 32u + col * 2u : kOobOffset,
+                                                                              0, 0);
+                        bt.zb[i][j][f] = __builtin_amdgcn_raw_buffer_load_b8(rz, in ? rec * 8u + (col >> 1) : kOobOffset,
+                                                                             0, 0);
+                    }
+                }
                 bt.w[i][j] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw[j], wo, (b0 + i) * kTileBytes, kWeightLoadPolicy));
+            }
         }
     };
     auto compute = [&](int b0, const Batch &bt, const uint8_t *xr) {
@@ -288,7 +327,8 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
                         a[t][mt] = *reinterpret_cast<const half8 *>(
                             xr + i * kSlot + xoff[mt] + (((4 * t + kq) ^ col) * 16));
                 }
-            block_mma<MT, NS, GS>(a, bt.w[i], szl, (int)L.ngw, b, gw0, col, m_lo, m_hi, acc);
+            block_mma<MT, NS, GS, RB>(a, bt.w[i], szl, (int)L.ngw, b, gw0, col, m_lo, m_hi, bt.sc[RB ? i : 0],
+                                      bt.zb[RB ? i : 0], acc);
         }
     };
 
@@ -299,12 +339,10 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         // loads in flight (vector loads complete in order). A record unit is
         // half a group record (8 columns: 16 bytes of scales, 4 bytes of zero
         // codes), one per lane; units past the first 64 (long runs only)
-        // follow after a full wait.
-        const int nsv = nstrip - strip0 < NS ? nstrip - strip0 : NS;  // strips that exist
-        const uint8_t *srec = packed + weight_bytes(K, N) + (size_t)strip0 * ngrp * 32;
-        const uint8_t *zrec = packed + weight_bytes(K, N) + scale_bytes(K, N, G) + (size_t)strip0 * ngrp * 8;
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(srec, (uint32_t)(nsv * ngrp * 32));
-        const __amdgpu_buffer_rsrc_t rz = make_rsrc(zrec, (uint32_t)(nsv * ngrp * 8));
+        // follow after a full wait. With RB (plans whose runs fit in the two
+        // batches issued up front) the records travel with the batches
+        // instead: no staging round trip before the first tile, at the cost
+        // of two small loads per strip and group.
         const int su_n = NS * ngw * 2;
 
         auto sz_load = [&](int u, u32x4 &sv, uint32_t &zv) {
@@ -324,7 +362,7 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
 
         u32x4 sv0;
         uint32_t zv0;
-        sz_load(lane, sv0, zv0);
+        if constexpr (!RB) sz_load(lane, sv0, zv0);
         if constexpr (kRun) {
             // row r, chunk c: blocks [wb + 4c, wb + 4c + 4) of row r; lanes
             // past the run read zeros into the slot's spare bytes
@@ -344,19 +382,22 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         asm volatile("" ::: "memory");  // keep the two batches apart in issue order
         load(b + NB, b1, xr1);
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBatchLoads));  // staging loads landed
-
-        sz_store(lane, sv0, zv0);
-        for (int u = 64 + lane; u - lane < su_n; u += 64) {
-            u32x4 a;
-            uint32_t z;
-            sz_load(u, a, z);
-            sz_store(u, a, z);
+        if constexpr (!RB || kRun) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBatchLoads));  // staging loads landed
+            if constexpr (!RB) {
+                sz_store(lane, sv0, zv0);
+                for (int u = 64 + lane; u - lane < su_n; u += 64) {
+                    u32x4 a;
+                    uint32_t z;
+                    sz_load(u, a, z);
+                    sz_store(u, a, z);
+                }
+            }
+            // the region is private to the wave: order its writes before its reads
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        // the region is private to the wave: order its writes before its reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // Two batches in flight: consume one, refill it two batches ahead.
         // All rounds but the last refill unconditionally (only the final
@@ -441,6 +482,7 @@ struct Plan {
     int xm;             // decode_kernel X mode: kXRun, or ring rows (8, 16, 32, 64)
     bool fixed_splits;  // automatic plan keeps K unsplit
     int splits, slice_blocks;
+    bool rb;            // records loaded with each batch (runs of at most two batches)
 };
 
 int env_int(const char *name, int dflt) {
@@ -494,6 +536,7 @@ Plan base_plan(int M, int N, int K) {
     if (p.xm == 64) p.wk = 4;  // two 64-row slots per wave: 128 KiB of LDS at 4 waves
     p.splits = 1;
     p.slice_blocks = 0;
+    p.rb = false;
     // no more waves than blocks of K (idle waves would still hold LDS)
     while (p.wk > 4 && p.wk > nblk) p.wk /= 2;
     // the cross-wave reduction buffer must leave room for the staged records
@@ -514,13 +557,21 @@ int slice_for(int K, int G, int splits) {
 // without an LDS ring (the ring holds one block per batch).
 constexpr int decode_nb(int MT, int NS, int XM) { return (NS == 1 && MT == 1 && XM <= kXRun) ? 2 : 1; }
 
+// Records with the batches need 2 (NF) more loads per strip and block; the
+// two batches issued ahead must stay within the vector-memory counter.
+constexpr bool rb_fits(int MT, int NS, int XM, int GS) {
+    const int nf = GS < 4 ? 4 / GS : 1;
+    const int xloads = XM >= 8 ? XM / 4 : 0;
+    return MT == 1 && 2 * decode_nb(MT, NS, XM) * (NS * (1 + 2 * nf) + xloads) <= 63;
+}
+
 // Static LDS of the ring mode: two rings of WK x NB slots of XM rows.
 uint32_t ring_lds(const Plan &p) {
     return p.xm >= 8 ? (uint32_t)(2 * p.wk * decode_nb(p.mt, p.ns, p.xm) * p.xm * kBlockK * 2) : 0u;
 }
 
 uint32_t plan_lds(const Plan &p, int M, int G, int slice_blocks) {
-    return decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xm).total() + ring_lds(p);
+    return decode_lds(M, p.mt, p.ns, p.wk, slice_blocks, G, p.xm, p.rb).total() + ring_lds(p);
 }
 
 // A plan may use all of a CU's LDS when it runs one workgroup per CU (the
@@ -573,28 +624,47 @@ Plan make_plan(int M, int N, int K, int G, int splits, int num_cus) {
     while (splits < nblk && !fits(splits)) ++splits;
     p.slice_blocks = slice_for(K, G, splits);
     p.splits = (nblk + p.slice_blocks - 1) / p.slice_blocks;
+    // Records with the batches when a wave's whole run is in flight after
+    // the first two batches (graph-timed on MI355X, 4096 x 6144: M = 1 5.72
+    // -> 5.46 us, M = 8 6.44 -> 6.11, M = 16 7.32 -> 6.97; on longer runs
+    // the per-batch record loads cost more than the staging saves: 14336 x
+    // 4096 at M = 1, 7.97 -> 9.73 us). W4A16_DECODE_RB (0, 1) overrides.
+    const int per = (p.slice_blocks + p.wk - 1) / p.wk;
+    const bool ok = rb_fits(p.mt, p.ns, p.xm, G / 32);
+    p.rb = ok && per <= 2 * decode_nb(p.mt, p.ns, p.xm);
+    const int erb = env_int("W4A16_DECODE_RB", -1);
+    if (ok && (erb == 0 || erb == 1)) p.rb = erb == 1;
     return p;
 }
 
-template <int MT, int NS, int WK, int GS, int XM>
+template <int MT, int NS, int WK, int GS, int XM, bool RB>
 hipError_t launch_one(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y,
                       float *part, const Plan &p, hipStream_t stream) {
     constexpr int NB = decode_nb(MT, NS, XM);
-    const DecodeLds L = decode_lds(M, MT, NS, WK, p.slice_blocks, 32 * GS, XM);
+    const DecodeLds L = decode_lds(M, MT, NS, WK, p.slice_blocks, 32 * GS, XM, RB);
     const int tiles = (N / kStripCols + NS - 1) / NS;
-    hipLaunchKernelGGL((decode_kernel<MT, NS, WK, NB, GS, XM>), dim3(tiles, p.splits), dim3(WK * 64),
+    hipLaunchKernelGGL((decode_kernel<MT, NS, WK, NB, GS, XM, RB>), dim3(tiles, p.splits), dim3(WK * 64),
                        L.total(), stream, X, packed, Y, part, M, N, K, p.splits, p.slice_blocks);
     return hipGetLastError();
+}
+
+template <int MT, int NS, int WK, int GS, int XM>
+hipError_t launch_rb(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y, float *part,
+                     const Plan &p, hipStream_t stream) {
+    if constexpr (rb_fits(MT, NS, XM, GS)) {
+        if (p.rb) return launch_one<MT, NS, WK, GS, XM, true>(X, packed, M, N, K, Y, part, p, stream);
+    }
+    return launch_one<MT, NS, WK, GS, XM, false>(X, packed, M, N, K, Y, part, p, stream);
 }
 
 template <int MT, int NS, int WK, int XM>
 hipError_t launch_g(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
                     float *part, const Plan &p, hipStream_t stream) {
     switch (G) {
-        case 32: return launch_one<MT, NS, WK, 1, XM>(X, packed, M, N, K, Y, part, p, stream);
-        case 64: return launch_one<MT, NS, WK, 2, XM>(X, packed, M, N, K, Y, part, p, stream);
-        case 128: return launch_one<MT, NS, WK, 4, XM>(X, packed, M, N, K, Y, part, p, stream);
-        case 256: return launch_one<MT, NS, WK, 8, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 32: return launch_rb<MT, NS, WK, 1, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 64: return launch_rb<MT, NS, WK, 2, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 128: return launch_rb<MT, NS, WK, 4, XM>(X, packed, M, N, K, Y, part, p, stream);
+        case 256: return launch_rb<MT, NS, WK, 8, XM>(X, packed, M, N, K, Y, part, p, stream);
         default: return hipErrorInvalidValue;
     }
 }
