@@ -344,7 +344,11 @@ PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
     if (splits <= 0) {
         const int slots = num_cus * per_cu;
         splits = tiles >= slots ? 1 : slots / tiles;
-        const int cap = nblk / 8 > 1 ? nblk / 8 : 1;  // keep 8+ blocks per split
+        // keep 16+ blocks of K per split: below that the fp32 partials
+        // (written, then read back by the reduce kernel) cost more than the
+        // idle slots (graph-timed, 3584 x 8192 at M = 1024: 82.3 us with 2
+        // splits of 14 blocks, 69.8 us unsplit)
+        const int cap = nblk / 16 > 1 ? nblk / 16 : 1;
         if (splits > cap) splits = cap;
     }
     if (splits > nblk) splits = nblk;

@@ -136,13 +136,47 @@ w8a8_quant_act_kernel(const uint16_t *__restrict__ X, int K, int8_t *__restrict_
 }
 
 // ------------------------------------------------------------ weights
-// Per-column maxima: one thread per column, rows in order.
+// Per-column maxima of |W| in two passes (the maximum does not depend on
+// the order, so the result equals a plain loop over the rows). Pass 1: a
+// workgroup takes 64 columns x 256 rows; each thread reads two adjacent
+// columns (one 4-byte load) on every eighth row of the slice, so a wave
+// reads whole 128-byte row segments, and the eight row phases meet in LDS.
+// The partial maxima [K / 256][N] go to `part` (the packed output buffer,
+// K * N bytes, which the pack kernel overwrites afterwards). Pass 2: one
+// thread per column takes the maximum over the slices and writes the scale.
 __global__ void __launch_bounds__(256)
-w8a8_weight_scale_kernel(const uint16_t *__restrict__ W, int K, int N, float *__restrict__ ws) {
+w8a8_weight_colmax_kernel(const uint16_t *__restrict__ W, int K, int N, float *__restrict__ part) {
+    __shared__ float red[8][64];
+    const int t = threadIdx.x;
+    const int p = t & 31, h = t >> 5;
+    const int c = blockIdx.x * 64 + 2 * p;
+    const int r0 = blockIdx.y * 256;
+    float m0 = 0.f, m1 = 0.f;
+    if (c < N) {  // N is even: both columns of a pair exist or neither
+#pragma unroll 8
+        for (int i = 0; i < 32; ++i) {
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(W + (size_t)(r0 + h + 8 * i) * N + c);
+            m0 = __builtin_fmaxf(m0, __builtin_fabsf(h2f((uint16_t)(v & 0xFFFFu))));
+            m1 = __builtin_fmaxf(m1, __builtin_fabsf(h2f((uint16_t)(v >> 16))));
+        }
+    }
+    red[h][2 * p] = m0;
+    red[h][2 * p + 1] = m1;
+    __syncthreads();
+    if (t < 64 && blockIdx.x * 64 + t < N) {
+        float m = red[0][t];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) m = __builtin_fmaxf(m, red[q][t]);
+        part[(size_t)blockIdx.y * N + blockIdx.x * 64 + t] = m;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+w8a8_weight_scale_kernel(const float *__restrict__ part, int slices, int N, float *__restrict__ ws) {
     const int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     float amax = 0.f;
-    for (int k = 0; k < K; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(h2f(W[(size_t)k * N + n])));
+    for (int s = 0; s < slices; ++s) amax = __builtin_fmaxf(amax, part[(size_t)s * N + n]);
     ws[n] = amax > 0.f ? amax / 127.0f : 1.0f;
 }
 
@@ -193,7 +227,13 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
     const int col = lane & 15, kq = lane >> 4;
     const int nblk = K / kW8Block;
     const int nstrip = N / 16;
-    const int tile = blockIdx.x;
+    // XCD-aware remap, as in the W4A16 prefill kernel: workgroups are
+    // dispatched round-robin over the eight XCDs, so give each XCD a
+    // contiguous run of tiles with M varying fastest: the row tiles that
+    // share a column slab of weights then read it through one L2.
+    const int ntiles = (int)gridDim.x;  // tiles_m x tiles_n
+    int tile = blockIdx.x;
+    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
     const int tm = tile % tiles_m, tn = tile / tiles_m;
     const int split = blockIdx.y;
     const int bb = split * slice_blocks;
@@ -481,8 +521,14 @@ hipError_t launch_w8a8_quant_act(const uint16_t *X, int M, int K, int8_t *xq, fl
 }
 
 hipError_t launch_w8a8_quant_weights(const uint16_t *W, int K, int N, uint8_t *packed, float *ws, hipStream_t stream) {
-    hipLaunchKernelGGL(w8a8_weight_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, W, K, N, ws);
+    float *part = reinterpret_cast<float *>(packed);  // [K / 256][N] partial maxima, overwritten by the pack
+    hipLaunchKernelGGL(w8a8_weight_colmax_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)(K / 256)), dim3(256), 0,
+                       stream, W, K, N, part);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(w8a8_weight_scale_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream, part,
+                       K / 256, N, ws);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(w8a8_weight_pack_kernel, dim3(grid_for((int64_t)K * N / 16)), dim3(256), 0, stream, W, K, N,
                        ws, reinterpret_cast<u32x4 *>(packed));
