@@ -197,10 +197,8 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int pat
  *   workspace, workspace_bytes: at least w4a16_workspace_bytes(...) bytes of
  *            device memory (any contents), or NULL/0 if that is 0. It holds
  *            the fp32 partial sums of the K splits between the GEMM kernel
- *            and the reduce kernel (or, where the automatic prefill plan
- *            splits only its last round of tiles in two along K, the two
- *            halves of those tiles until the fixup kernel adds them), so
- *            calls sharing one workspace must be ordered (same stream).
+ *            and the reduce kernel, so calls sharing one workspace must be
+ *            ordered (same stream).
  * Rounding depends on the plan, the exact result does not: the decode path
  * multiplies the exact integers (q - z) by X and applies each group's scale
  * to the group's fp32 partial sum; the prefill path rounds every dequantized
@@ -219,10 +217,7 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
  * capture, tight serving loops, harnesses that forbid hipMalloc.
  * w4a16_gemm with the same automatic plan and kernels (results bitwise equal
  * to w4a16_gemm's), whose split-K partials go to a fixed scratch array
- * inside the library instead of an allocated workspace (where the automatic
- * prefill plan's split last round would need more than the scratch, the
- * plan without that split is used instead: results then equal those of
- * w4a16_gemm_ex with that plan, within the same error bounds):
+ * inside the library instead of an allocated workspace:
  * W4A16_NOALLOC_SCRATCH_BYTES per GPU, placed when the library's code object
  * is loaded on that GPU and held until the process ends. The call allocates
  * nothing (no hipMalloc, hipFree or allocating library routine); its first

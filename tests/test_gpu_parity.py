@@ -257,41 +257,6 @@ def test_decode_records_with_batches(monkeypatch, M, K, N, G, splits, xm):
     assert_parity(out[1], oracle.gemm(X, q, z, s, G), f"rb M={M} K={K} N={N} G={G}")
 
 
-# Prefill with the split tail: more tiles than resident workgroup slots
-# (two 128 x 256 workgroups per CU: 512 on a 256-CU MI355X) and a partly
-# empty last round, whose tiles are split in two along K and added by a
-# fixup kernel. Ragged M and N tails, every G; the last case forces the
-# split onto every tile of a one-round grid. Both the split-tail plan and
-# the plan without it must meet the parity bar.
-TAIL_CASES = [
-    # (M, K, N, G, force)
-    (1000, 512, 18448, 128, None),
-    (1024, 1024, 18432, 64, None),
-    (1100, 768, 17920, 256, None),
-    (600, 768, 18432, 32, "1"),
-]
-
-
-@pytest.mark.parametrize("M,K,N,G,force", TAIL_CASES)
-def test_prefill_split_tail(monkeypatch, M, K, N, G, force):
-    say(f"prefill split tail: M={M} K={K} N={N} G={G} force={force}")
-    q, z, s, rng = _weights(K, N, G, seed=M + K + N + G)
-    X = synth.draw_x(rng, M, K)
-    packed = pack_dev(q, z, s, G)
-    ref = oracle.gemm(X, q, z, s, G)
-    if force is None:
-        tiles = -(-M // 128) * -(-N // 256)
-        assert tiles > 512 and 0 < tiles % 512 <= 384, "case must need a split tail"
-        # the automatic plan holds one 128 x 256 fp32 slot per tail half
-        assert w4.w4a16_workspace_bytes(M, N, K, G, PREFILL, 0) == 2 * (tiles % 512) * 128 * 256 * 4
-    else:
-        monkeypatch.setenv("W4A16_PREFILL_TAIL", force)
-    Y = run_gemm(X, packed, N, K, G, path=PREFILL, splits=0)
-    assert_parity(Y, ref, f"split tail M={M} K={K} N={N} G={G}")
-    monkeypatch.setenv("W4A16_PREFILL_TAIL", "0")
-    assert_parity(run_gemm(X, packed, N, K, G, path=PREFILL, splits=0), ref, "without the split tail")
-
-
 def test_parity_with_activation_outliers_both_paths():
     K, N, G, M = 2048, 512, 128, 48
     q, z, s, idx, rng = synth.draw_weights(K, N, G, seed=5, outliers=True)

@@ -202,7 +202,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits, 
     if (splits == 0)
         splits = path == W4A16_PATH_DECODE
                      ? w4a16::decode_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus)
-                     : w4a16::prefill_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus, true);
+                     : w4a16::prefill_auto_splits((int)M, (int)N, (int)K, (int)G, num_cus);
     p->path = path;
     p->splits = splits;
     return W4A16_OK;
@@ -211,7 +211,7 @@ int make_plan(int64_t M, int64_t N, int64_t K, int64_t G, int path, int splits, 
 size_t plan_workspace(const Plan &p, int64_t M, int64_t N, int64_t K, int64_t G, int num_cus) {
     if (p.path == W4A16_PATH_DECODE)
         return w4a16::decode_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits, num_cus);
-    return w4a16::prefill_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits, num_cus);
+    return w4a16::prefill_workspace_bytes((int)M, (int)N, (int)K, (int)G, p.splits);
 }
 
 int check_gemm_args(const uint16_t *X, const void *packed, int64_t M, int64_t N, int64_t K,
@@ -507,13 +507,7 @@ int w4a16_gemm_noalloc(const uint16_t *X, const void *packed, int64_t M, int64_t
     if ((rc = current_device(&dev)) || (rc = device_cus(dev, &cus))) return rc;
     Plan p;
     if ((rc = make_plan(M, N, K, G, W4A16_PATH_AUTO, 0, cus, &p))) return rc;
-    size_t need = plan_workspace(p, M, N, K, G, cus);
-    if (need > (size_t)W4A16_NOALLOC_SCRATCH_BYTES && p.path == W4A16_PATH_PREFILL &&
-        p.splits == w4a16::kPrefillSplitTail) {
-        // split-tail slots beyond the scratch: the automatic plan without it
-        p.splits = w4a16::prefill_auto_splits((int)M, (int)N, (int)K, (int)G, cus, false);
-        need = plan_workspace(p, M, N, K, G, cus);
-    }
+    const size_t need = plan_workspace(p, M, N, K, G, cus);
     if (need > (size_t)W4A16_NOALLOC_SCRATCH_BYTES)
         return fail(W4A16_ERR_WORKSPACE,
                     "the plan for M=%lld N=%lld K=%lld G=%lld needs %zu bytes of split-K partials; the fixed "

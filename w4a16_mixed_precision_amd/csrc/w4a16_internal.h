@@ -58,13 +58,9 @@ hipError_t launch_decode(const uint16_t *X, const uint8_t *packed, int M, int N,
                          uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 
 // Prefill path (any M): LDS-staged activations, MFMA tiles, optional split
-// of K across workgroups (fp32 partials + reduce kernel) for small grids,
-// or, for several rounds of tiles with a partly empty last round, the last
-// round's tiles split in two along K (kPrefillSplitTail as the split count;
-// fp32 halves + fixup kernel).
-constexpr int kPrefillSplitTail = -1;
-int prefill_auto_splits(int M, int N, int K, int G, int num_cus, bool allow_tail);
-size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits, int num_cus);
+// of K across workgroups (fp32 partials + reduce kernel) for small grids.
+int prefill_auto_splits(int M, int N, int K, int G, int num_cus);
+size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits);
 hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
                           uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream);
 

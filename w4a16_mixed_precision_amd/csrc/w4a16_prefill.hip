@@ -56,7 +56,7 @@ template <int MTW, int NSW, int WM, int WN, int GS, int OCC>
 __global__ void __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed,
                uint16_t *__restrict__ Y, float *__restrict__ part, int M, int N, int K, int tiles_m,
-               int tiles_n, int S, int slice_blocks, int tail_from, int tail_kh) {
+               int tiles_n, int S, int slice_blocks) {
     constexpr int WAVES = WM * WN;
     constexpr int THREADS = WAVES * 64;
     constexpr int BM = WM * MTW * 16;
@@ -77,33 +77,17 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     const int ngrp = K / (32 * GS);
     const int nstrip = N / kStripCols;
 
-    // Workgroup -> (tile, blocks [bb, be) of K). Ids below tail_from take a
-    // whole tile (and split blockIdx.y of K when S > 1). With a split tail
-    // (tail_from < tiles), the ids after it take one half of one of the
-    // last tiles, blocks [0, tail_kh) or [tail_kh, nblk), into the fp32 slot
-    // of that half (`thalf`); prefill_tail_fixup adds the two halves. The
-    // tail ids dispatch last, so the halves fill the last round of resident
-    // workgroups instead of leaving it partly empty.
-    // XCD-aware remap: consecutive dispatch ids go to consecutive XCDs, so
-    // give each XCD a contiguous run of tiles (of halves); within a run M
-    // varies fastest, so neighbours share columns of W.
-    int tile, thalf = -1, bb, be;
-    if ((int)blockIdx.x < tail_from) {
-        tile = blockIdx.x;
-        if (tail_from % 8 == 0) tile = (blockIdx.x % 8) * (tail_from / 8) + blockIdx.x / 8;
-        bb = blockIdx.y * slice_blocks;
-        be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
-    } else {
-        const int n2 = (int)gridDim.x - tail_from, id = (int)blockIdx.x - tail_from;
-        thalf = id;
-        if (n2 % 8 == 0) thalf = (id % 8) * (n2 / 8) + id / 8;
-        tile = tail_from + thalf / 2;
-        bb = (thalf & 1) ? tail_kh : 0;
-        be = (thalf & 1) ? nblk : tail_kh;
-    }
+    // XCD-aware remap: dispatch order id -> logical tile id. Consecutive ids
+    // go to consecutive XCDs, so give each XCD a contiguous run of tiles;
+    // within a run M varies fastest, so neighbours share columns of W.
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
     const int tm = tile % tiles_m;
     const int tn = tile / tiles_m;
     const int split = blockIdx.y;
+    const int bb = split * slice_blocks;
+    const int be = bb + slice_blocks < nblk ? bb + slice_blocks : nblk;
 
     const int m0 = tm * BM;
     const int strip_w = (tn * WN + wn) * NSW;  // first strip of this wave
@@ -249,11 +233,8 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
         wc = wnext;
     }
 
-    // Epilogue: fp32 -> fp16 (round to nearest even), fp32 split-K partials
-    // [S][M][N], or a tail half's fp32 slot [BM][BN]; rows beyond M and
-    // strips beyond N dropped.
-    constexpr int BN = WN * NSW * 16;
-    float *slot = thalf >= 0 ? part + (size_t)thalf * (BM * BN) : nullptr;
+    // Epilogue: fp32 -> fp16 (round to nearest even) or fp32 partials; rows
+    // beyond M and strips beyond N dropped.
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
@@ -263,42 +244,14 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
             const size_t n = (size_t)s * kStripCols + col;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rl = rbase + mt * 16 + 4 * kq + e;
-                const int row = m0 + rl;
+                const int row = m0 + rbase + mt * 16 + 4 * kq + e;
                 if (row >= M) continue;
-                if (slot)
-                    slot[rl * BN + (wn * NSW + j) * kStripCols + col] = acc[mt][j][e];
-                else if (S == 1)
+                if (S == 1)
                     Y[(size_t)row * N + n] = f32_to_f16_bits(acc[mt][j][e]);
                 else
                     part[((size_t)split * M + row) * N + n] = acc[mt][j][e];
             }
         }
-}
-
-// Y of the split tail tiles: the two halves' fp32 slots added in K order
-// (the first half, then the second), fp32 -> fp16. One workgroup per tile.
-template <int BM, int BN>
-__global__ void __launch_bounds__(256)
-prefill_tail_fixup(const float *__restrict__ part, uint16_t *__restrict__ Y, int M, int N, int tiles_m,
-                   int tail_from) {
-    typedef float floatx4_t __attribute__((ext_vector_type(4)));
-    const int t = tail_from + (int)blockIdx.x;
-    const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
-    const float *h0 = part + (size_t)(2 * blockIdx.x) * (BM * BN);
-    const float *h1 = h0 + BM * BN;
-    for (int i = threadIdx.x; i < BM * BN / 4; i += 256) {
-        const int r = i * 4 / BN, c = i * 4 % BN;
-        const int row = m0 + r, n = n0 + c;
-        if (row >= M || n >= N) continue;  // N % 16 == 0: four columns all in or all out
-        const floatx4_t v = *reinterpret_cast<const floatx4_t *>(h0 + r * BN + c) +
-                            *reinterpret_cast<const floatx4_t *>(h1 + r * BN + c);
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = f32_to_f16_bits(v[e]);
-        *reinterpret_cast<uint2 *>(Y + (size_t)row * N + n) =
-            uint2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-    }
 }
 
 __global__ void __launch_bounds__(256)
@@ -327,74 +280,55 @@ constexpr Cfg kCfgs[] = {
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-// tail_kh > 0: the tiles from tail_from on are split in two at block
-// tail_kh (one workgroup per half), then added by prefill_tail_fixup.
 template <int CI, int GS>
 hipError_t launch_cfg_g(const uint16_t *X, const uint8_t *packed, int M, int N, int K, uint16_t *Y,
-                        float *part, int S, int slice_blocks, int tail_from, int tail_kh, hipStream_t stream) {
+                        float *part, int S, int slice_blocks, hipStream_t stream) {
     constexpr Cfg c = kCfgs[CI];
     constexpr int BM = c.wm * c.mtw * 16, BN = c.wn * c.nsw * 16;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    const int tiles = tiles_m * tiles_n;
-    if (!tail_kh) tail_from = tiles;
-    const int wgs = tail_from + 2 * (tiles - tail_from);
-    hipLaunchKernelGGL((prefill_kernel<c.mtw, c.nsw, c.wm, c.wn, GS, c.occ>), dim3((unsigned)wgs, (unsigned)S),
-                       dim3(c.wm * c.wn * 64), 0, stream, X, packed, Y, part, M, N, K, tiles_m, tiles_n, S,
-                       slice_blocks, tail_from, tail_kh);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || tail_from == tiles) return e;
-    hipLaunchKernelGGL((prefill_tail_fixup<BM, BN>), dim3((unsigned)(tiles - tail_from)), dim3(256), 0, stream, part,
-                       Y, M, N, tiles_m, tail_from);
+    hipLaunchKernelGGL((prefill_kernel<c.mtw, c.nsw, c.wm, c.wn, GS, c.occ>),
+                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)S), dim3(c.wm * c.wn * 64), 0, stream, X,
+                       packed, Y, part, M, N, K, tiles_m, tiles_n, S, slice_blocks);
     return hipGetLastError();
 }
 
 template <int CI>
 hipError_t launch_cfg(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G, uint16_t *Y,
-                      float *part, int S, int slice_blocks, int tail_from, int tail_kh, hipStream_t stream) {
+                      float *part, int S, int slice_blocks, hipStream_t stream) {
     switch (G) {
-        case 32: return launch_cfg_g<CI, 1>(X, packed, M, N, K, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 64: return launch_cfg_g<CI, 2>(X, packed, M, N, K, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 128: return launch_cfg_g<CI, 4>(X, packed, M, N, K, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 256: return launch_cfg_g<CI, 8>(X, packed, M, N, K, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
+        case 32: return launch_cfg_g<CI, 1>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
+        case 64: return launch_cfg_g<CI, 2>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
+        case 128: return launch_cfg_g<CI, 4>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
+        case 256: return launch_cfg_g<CI, 8>(X, packed, M, N, K, Y, part, S, slice_blocks, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_index(int ci, const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
-                        uint16_t *Y, float *part, int S, int slice_blocks, int tail_from, int tail_kh,
-                        hipStream_t stream) {
+                        uint16_t *Y, float *part, int S, int slice_blocks, hipStream_t stream) {
     switch (ci) {
-        case 0: return launch_cfg<0>(X, packed, M, N, K, G, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 1: return launch_cfg<1>(X, packed, M, N, K, G, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 2: return launch_cfg<2>(X, packed, M, N, K, G, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 3: return launch_cfg<3>(X, packed, M, N, K, G, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        case 4: return launch_cfg<4>(X, packed, M, N, K, G, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
-        default: return launch_cfg<5>(X, packed, M, N, K, G, Y, part, S, slice_blocks, tail_from, tail_kh, stream);
+        case 0: return launch_cfg<0>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 1: return launch_cfg<1>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 2: return launch_cfg<2>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 3: return launch_cfg<3>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        case 4: return launch_cfg<4>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
+        default: return launch_cfg<5>(X, packed, M, N, K, G, Y, part, S, slice_blocks, stream);
     }
 }
 
 struct PrefillPlan {
     int ci, splits, slice_blocks;
-    int tail_from, tail_kh;  // split tail: first split tile and split block (tail_kh 0: none)
-    int bm, bn, tiles;
 };
 
-// Tile shape by M (64-row tiles up to M = 128, 128-row tiles above).
-// Several rounds of tiles (more tiles than resident workgroup slots) whose
-// last round would run at most three quarters full: that round's tiles are
-// split in two along K, one workgroup per half (a workgroup alone on a CU
-// runs no faster than two together, so a half-full last round costs a
-// whole round: MI355X, 2048 x 4096 x 28672, 1792 tiles for 512 slots).
-// One round or less: split K so that one round of resident workgroups
-// covers the GPU: the largest split count whose tiles x splits still fit
-// in one round. (A count that spills into a second, mostly empty round
-// costs more than it gains: graph-timed, 8192 x 10240 at M = 512 took
-// 125 us with 3 splits of its 160 tiles and 150 us with 4; 8192 x 57344 at
-// M = 256 took 241 us unsplit and 297 us with 2 splits of its 448 tiles.)
-// splits == 0: automatic; < 0: automatic without the split tail.
-// W4A16_PREFILL_CFG overrides the shape, W4A16_PREFILL_TAIL (0, 1) the
-// split-tail choice of the automatic plan (tuning).
+// Tile shape by M (64-row tiles up to M = 128, 128-row tiles above); split
+// K so that one round of resident workgroups covers the GPU: the largest
+// split count whose tiles x splits still fit in one round. (A count that
+// spills into a second, mostly empty round costs more than it gains:
+// graph-timed on MI355X, 8192 x 10240 at M = 512 took 125 us with 3 splits
+// of its 160 tiles and 150 us with 4; 8192 x 57344 at M = 256 took 241 us
+// unsplit and 297 us with 2 splits of its 448 tiles.)
+// W4A16_PREFILL_CFG overrides the shape (tuning).
 PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
     PrefillPlan p;
     p.ci = M <= 128 ? 3 : 2;
@@ -403,33 +337,12 @@ PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
         if (v >= 0 && v < kNumCfgs) p.ci = v;
     }
     const Cfg c = kCfgs[p.ci];
-    p.bm = c.wm * c.mtw * 16;
-    p.bn = c.wn * c.nsw * 16;
-    const int tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
-    p.tiles = tiles;
-    p.tail_from = tiles;
-    p.tail_kh = 0;
+    const int BM = c.wm * c.mtw * 16, BN = c.wn * c.nsw * 16;
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int nblk = K / kBlockK;
-    const int unit = G > kBlockK ? G / kBlockK : 1;  // blocks per quantization group
     const int per_cu = c.occ * 4 / (c.wm * c.wn) > 0 ? c.occ * 4 / (c.wm * c.wn) : 1;  // resident WGs per CU
-    const int slots = num_cus * per_cu;
-    if (splits == 0 && nblk >= 2 * unit) {
-        const int rem = tiles % slots;
-        bool tail = tiles > slots && rem != 0 && rem * 4 <= slots * 3;
-        if (const char *e = getenv("W4A16_PREFILL_TAIL")) {
-            const int v = atoi(e);
-            if (v == 0 || v == 1) tail = v == 1 && tiles > 1;
-        }
-        if (tail) {
-            p.tail_from = tiles - (rem ? rem : (tiles + 1) / 2);
-            p.tail_kh = (nblk / 2 + unit - 1) / unit * unit;
-            if (p.tail_kh >= nblk) p.tail_kh = nblk - unit;
-            p.splits = kPrefillSplitTail;
-            p.slice_blocks = nblk;
-            return p;
-        }
-    }
     if (splits <= 0) {
+        const int slots = num_cus * per_cu;
         splits = tiles >= slots ? 1 : slots / tiles;
         // keep 16+ blocks of K per split: below that the fp32 partials
         // (written, then read back by the reduce kernel) cost more than the
@@ -439,6 +352,7 @@ PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
         if (splits > cap) splits = cap;
     }
     if (splits > nblk) splits = nblk;
+    const int unit = G > kBlockK ? G / kBlockK : 1;
     int sb = (nblk + splits - 1) / splits;
     sb = (sb + unit - 1) / unit * unit;
     p.slice_blocks = sb;
@@ -448,26 +362,22 @@ PrefillPlan prefill_plan(int M, int N, int K, int G, int splits, int num_cus) {
 
 }  // namespace
 
-int prefill_auto_splits(int M, int N, int K, int G, int num_cus, bool allow_tail) {
-    return prefill_plan(M, N, K, G, allow_tail ? 0 : -1, num_cus).splits;
+int prefill_auto_splits(int M, int N, int K, int G, int num_cus) {
+    return prefill_plan(M, N, K, G, 0, num_cus).splits;
 }
 
-size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits, int num_cus) {
-    const PrefillPlan p = prefill_plan(M, N, K, G, splits == kPrefillSplitTail ? 0 : splits, num_cus);
-    if (p.tail_kh)  // one [BM][BN] fp32 slot per tail half
-        return (size_t)2 * (p.tiles - p.tail_from) * (size_t)p.bm * (size_t)p.bn * sizeof(float);
+size_t prefill_workspace_bytes(int M, int N, int K, int G, int splits) {
+    const PrefillPlan p = prefill_plan(M, N, K, G, splits, 256);
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
 hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N, int K, int G,
                           uint16_t *Y, void *workspace, int splits, int num_cus, hipStream_t stream) {
-    const PrefillPlan p = prefill_plan(M, N, K, G, splits == kPrefillSplitTail ? 0 : splits, num_cus);
-    if (splits == kPrefillSplitTail && !p.tail_kh) return hipErrorInvalidValue;  // plan differs from the sized one
-    float *part = (p.tail_kh || p.splits > 1) ? static_cast<float *>(workspace) : nullptr;
-    hipError_t e = launch_index(p.ci, X, packed, M, N, K, G, Y, part, p.tail_kh ? 1 : p.splits, p.slice_blocks,
-                                p.tail_from, p.tail_kh, stream);
-    if (e != hipSuccess || p.tail_kh || p.splits <= 1) return e;
+    const PrefillPlan p = prefill_plan(M, N, K, G, splits, num_cus);
+    float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    hipError_t e = launch_index(p.ci, X, packed, M, N, K, G, Y, part, p.splits, p.slice_blocks, stream);
+    if (e != hipSuccess || p.splits <= 1) return e;
     const int64_t MN = (int64_t)M * N;
     int64_t blocks = (MN + 255) / 256;
     if (blocks > 8192) blocks = 8192;
