@@ -358,7 +358,7 @@ int w4a16_w8a8_gemm(const int8_t *xq, const float *x_scales, const void *packed,
  * streams that many bytes ("LMDeploy" interview notes: each decode step
  * streams every weight byte once). Folds the data into one word per lane and
  * writes it to `sink` (64 uint32, device) only where it equals `never`, so
- * in practice nothing is written. 0 < bytes < 2^32. Asynchronous on `stream`.
+ * in practice nothing is written. 0 < bytes < 2^31. Asynchronous on `stream`.
  */
 int w4a16_stream_read(const void *buf, size_t bytes, uint32_t never, uint32_t *sink, void *stream);
 

@@ -140,6 +140,15 @@ def test_kv_and_w8a8_validation_before_any_hip_call():
     assert L.w4a16_w8a8_quantize_weights(FAKE, 256, 24, FAKE, FAKE, None) == w4.W4A16_ERR_SHAPE
 
 
+def test_stream_read_validation_before_any_hip_call():
+    L = w4.lib()
+    assert L.w4a16_stream_read(FAKE, 0, 0, FAKE, None) == w4.W4A16_ERR_SHAPE
+    # offsets past the end are steered to 2^31, so the buffer stays below it
+    assert L.w4a16_stream_read(FAKE, 1 << 31, 0, FAKE, None) == w4.W4A16_ERR_SHAPE
+    assert L.w4a16_stream_read(None, 1024, 0, FAKE, None) == w4.W4A16_ERR_NULL
+    assert L.w4a16_stream_read(MISALIGNED, 1024, 0, FAKE, None) == w4.W4A16_ERR_ALIGN
+
+
 def test_status_strings():
     for code in range(-7, 1):
         assert w4.w4a16_status_string(code) not in ("", "unknown status")

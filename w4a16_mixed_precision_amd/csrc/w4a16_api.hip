@@ -546,8 +546,8 @@ int w4a16_gemm_ex(const uint16_t *X, const void *packed, int64_t M, int64_t N, i
 
 int w4a16_stream_read(const void *buf, size_t bytes, uint32_t never, uint32_t *sink, void *stream) {
     if (!buf || !sink) return fail(W4A16_ERR_NULL, "buf and sink must be non-NULL");
-    if (bytes == 0 || bytes >= ((size_t)1 << 32))
-        return fail(W4A16_ERR_SHAPE, "stream read needs 0 < bytes < 2^32 (got %zu)", bytes);
+    if (bytes == 0 || bytes >= ((size_t)1 << 31))
+        return fail(W4A16_ERR_SHAPE, "stream read needs 0 < bytes < 2^31 (got %zu)", bytes);
     if (!aligned16(buf) || !aligned16(sink)) return fail(W4A16_ERR_ALIGN, "buf and sink must be 16-byte aligned");
     hipError_t e = w4a16::launch_stream_read((const uint8_t *)buf, bytes, never, sink, (hipStream_t)stream);
     if (e != hipSuccess) return fail_hip(e, "stream read launch");

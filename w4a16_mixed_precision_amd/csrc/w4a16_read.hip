@@ -8,8 +8,9 @@
 // Shape: one wave reads a contiguous run of 1 KiB chunks (one 16-byte load
 // per lane per chunk, non-temporal, all of the wave's chunks in flight at
 // once); a workgroup is WAVES such waves. The launch is sized so that the
-// whole buffer is covered by one round of resident workgroups. Loads past the
-// end read zeros (buffer descriptor bound) and make no memory request. The
+// whole buffer is covered by one round of resident workgroups. A load's whole
+// offset is its per-lane (vector) offset, and chunks past the end take an
+// offset past the descriptor: they read zeros and make no memory request. The
 // data are folded into one word per lane that is stored only if it equals a
 // value the caller chooses not to expect, so nothing is written in practice
 // and the loads cannot be dropped.
@@ -32,9 +33,11 @@ stream_read_kernel(const uint8_t *__restrict__ buf, uint32_t bytes, int chunks_p
     for (int i = 0; i < chunks_per_wave; i += U) {
         u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 r, (uint32_t)lane * 16u, base + (uint32_t)(i + u) * 1024u, 2));
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = base + (uint32_t)(i + u) * 1024u;  // wave-uniform chunk start
+            v[u] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, c < bytes ? c + (uint32_t)lane * 16u : kOobOffset, 0, 2));
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
