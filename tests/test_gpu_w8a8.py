@@ -56,14 +56,22 @@ def test_w8a8_bit_exact(M, K, N):
     assert bad.size == 0, (bad[:5], Y[tuple(bad[0])], ref[tuple(bad[0])])
 
 
-def test_forced_tile_shapes_agree(monkeypatch):
+@pytest.mark.parametrize("M,K,N", [(40, 1024, 512), (300, 2048, 1040), (129, 768, 4112)])
+def test_forced_tile_shapes_agree(monkeypatch, M, K, N):
+    # 16-, 64- and 128-row tiles (ragged row tiles and strips, split and
+    # unsplit K by the plan) give the oracle's Y bit for bit
     import torch
-    X, W = _inputs(40, 1024, 512, 7)
+    X, W = _inputs(M, K, N, 7)
     outs = []
-    for t in ("16", "64"):
+    for t in ("16", "64", "128"):
         monkeypatch.setenv("W4A16_W8A8_TILE", t)
         outs.append(_gpu(X, W)[-1])
-    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+    monkeypatch.delenv("W4A16_W8A8_TILE")
+    qw, sw = w8a8.quantize_weights(W)
+    qx, sx = w8a8.quantize_activations(X)
+    ref = w8a8.gemm(qx, sx, qw, sw)
+    for t, o in zip(("16", "64", "128"), outs):
+        assert np.array_equal(o.view(np.uint16), ref.view(np.uint16)), t
     torch.cuda.synchronize()
 
 

@@ -286,21 +286,29 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
 #pragma unroll
         for (int j = 0; j < NSW; ++j) acc[mt][j] = int32x4{0, 0, 0, 0};
 
+    // One 64-row step: row tile after row tile, each multiplied with the
+    // NSW strips' B operands of the step; a row tile's A operand is read
+    // from LDS two row tiles ahead, so only three A operands are live (what
+    // lets 128-row wave tiles keep two waves per SIMD).
     auto compute = [&](int stage, int half, const WHalf &w) {
         const uint8_t *st = lds + stage * STAGE;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int s = 2 * half + s2;
-            int32x4 a[MTW];
+            auto a_at = [&](int mt) {
+                return *reinterpret_cast<const int32x4 *>(st + (mt * 16 + col) * kW8Block + (((4 * s + kq) ^ col) * 16));
+            };
+            int32x4 a0 = a_at(0), a1 = MTW > 1 ? a_at(1) : a0;
 #pragma unroll
-            for (int mt = 0; mt < MTW; ++mt)
-                a[mt] = *reinterpret_cast<const int32x4 *>(st + (mt * 16 + col) * kW8Block + (((4 * s + kq) ^ col) * 16));
+            for (int mt = 0; mt < MTW; ++mt) {
+                const int32x4 a2 = mt + 2 < MTW ? a_at(mt + 2) : a0;
 #pragma unroll
-            for (int j = 0; j < NSW; ++j) {
-                const int32x4 bq = __builtin_bit_cast(int32x4, w[j][s2]);
-#pragma unroll
-                for (int mt = 0; mt < MTW; ++mt)
-                    acc[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt], bq, acc[mt][j], 0, 0, 0);
+                for (int j = 0; j < NSW; ++j)
+                    acc[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, __builtin_bit_cast(int32x4, w[j][s2]),
+                                                                       acc[mt][j], 0, 0, 0);
+                a0 = a1;
+                a1 = a2;
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -316,7 +324,10 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
             if (b + 1 < be) issue_x(b + 1, cur ^ 1);
             load_w(2 * b + 1, w1);
             compute(cur, 0, w0);
-            if (b + 1 < be) load_w(2 * b + 2, w0);
+            // unconditional (a conditional reload would keep the old set
+            // live beside the new one): after the last block it reads the
+            // block's first half again, inside the weights, and is not used
+            load_w(b + 1 < be ? 2 * b + 2 : 2 * b, w0);
             compute(cur, 1, w1);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
@@ -458,18 +469,16 @@ struct W8Plan {
     int decode, ns, wk;  // the decode kernel (M <= 16): strips per workgroup, waves along K
 };
 
-// 16-row tiles up to M = 16, 64-row tiles above (128-row tiles need one
-// wave per SIMD for their registers and measured slower: 416 against 367 us
-// at 2048 x 4096 x 28672); split K until the tiles times splits fill the
-// GPU's resident slots (two 4-wave workgroups per CU), keeping at least two
-// blocks of K per split.
+// The decode kernel up to M = 16, tiles of 64 or 128 rows above; split K
+// until the tiles times splits fill the GPU's resident slots (two 4-wave
+// workgroups per CU), keeping at least two blocks of K per split.
 W8Plan w8_plan(int M, int N, int K, int num_cus) {
     W8Plan p;
     p.bm = M <= 16 ? 16 : 64;
     p.decode = M <= 16;
     if (const char *e = getenv("W4A16_W8A8_TILE")) {  // forces the tiled kernel
         const int v = atoi(e);
-        if (v == 16 || v == 64) {
+        if (v == 16 || v == 64 || v == 128) {
             p.bm = v;
             p.decode = 0;
         }
@@ -495,10 +504,17 @@ W8Plan w8_plan(int M, int N, int K, int num_cus) {
         p.slice_blocks = K / kW8Block;
         return p;
     }
-    const int BM = p.bm;
-    const int tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
     const int nblk = K / kW8Block;
     const int slots = num_cus * 2;  // two 4-wave workgroups per CU
+    // 128-row tiles read each weight tile half as often as 64-row ones but
+    // give half as many workgroups: taken where 64-row tiles would fill the
+    // chip at least twice (graph-timed, 2048 x 4096 x 28672: 269-279 us
+    // against 325-378; 1024 x 8192 x 7168, under one round: 91 against 81.5)
+    if (getenv("W4A16_W8A8_TILE") == nullptr && M > 16 &&
+        ((M + 63) / 64) * ((N + 255) / 256) >= 2 * slots)
+        p.bm = 128;
+    const int BM = p.bm;
+    const int tiles = ((M + BM - 1) / BM) * ((N + 255) / 256);
     int s = tiles >= slots ? 1 : slots / tiles;
     const int cap = nblk / 2 > 1 ? nblk / 2 : 1;
     if (s > cap) s = cap;
@@ -551,7 +567,10 @@ hipError_t launch_w8a8_gemm(const int8_t *xq, const float *xs, const uint8_t *pa
     int32_t *part = p.splits > 1 ? static_cast<int32_t *>(workspace) : nullptr;
     const int tiles_m = (M + p.bm - 1) / p.bm, tiles_n = (N + 255) / 256;
     const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)p.splits);
-    if (p.bm == 64)
+    if (p.bm == 128)
+        hipLaunchKernelGGL((w8a8_gemm_kernel<8, 4, 2>), grid, dim3(256), 0, stream, xq, xs, packed, ws, Y, part, M, N,
+                           K, tiles_m, p.splits, p.slice_blocks);
+    else if (p.bm == 64)
         hipLaunchKernelGGL((w8a8_gemm_kernel<4, 4, 2>), grid, dim3(256), 0, stream, xq, xs, packed, ws, Y, part, M, N,
                            K, tiles_m, p.splits, p.slice_blocks);
     else
