@@ -122,6 +122,20 @@ def test_identity_activations_give_fp16_weights_bit_exact(G):
     assert np.array_equal(Y.view(np.uint16), expect[ks].view(np.uint16))
 
 
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
+def test_identity_prefill_split_bit_exact(G):
+    # X = I through the tiled path with K split three ways: slices start in
+    # the middle of a four-group window of scales and zero codes, and the
+    # last window runs past the strip's last group (K / G % 4 != 0 for G >= 64).
+    K = 1536 if G == 256 else 1408
+    N = 80
+    q, z, s, _ = _weights(K, N, G, seed=G + 1)
+    packed = pack_dev(q, z, s, G)
+    expect = oracle.dequant(q, z, s, G).astype(np.float16)
+    Y = run_gemm(np.eye(K, dtype=np.float16), packed, N, K, G, path=PREFILL, splits=3)
+    assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
+
+
 @pytest.mark.parametrize("path,M", [(DECODE, 1), (DECODE, 13), (DECODE, 64), (PREFILL, 5), (PREFILL, 300)])
 def test_integer_weights_bit_exact(path, M):
     # s = 1, X in {-1, 0, 1}, K = 128: |Y| <= 15 * 128 < 2048, exact in fp16.
@@ -169,6 +183,9 @@ SMALL = [
     (300, 512, 256, 32, PREFILL, 1),
     (300, 1152, 256, 64, PREFILL, 0),
     (517, 2304, 784, 256, PREFILL, 2),
+    (130, 1152, 272, 64, PREFILL, 2),    # slice 2 starts mid-window
+    (150, 640, 272, 32, PREFILL, 2),
+    (257, 1664, 528, 128, PREFILL, 3),
     (513, 768, 320, 256, 0, 0),
     (1, 29568, 64, 64, DECODE, 0),
     (40, 29568, 64, 64, 0, 0),

@@ -45,11 +45,9 @@ namespace {
 // Packed weights of one K block for the wave's NSW strips, kept raw until
 // use (combining them right after the load would make the compiler wait on
 // every load in flight, including the next block's prefetch).
-template <int NSW, int NF>
+template <int NSW>
 struct WSet {
     u32x4 w[NSW];
-    uint32_t sc[NF][NSW];  // fp16 scale bits
-    uint32_t zb[NF][NSW];  // byte holding the zero code
 };
 
 template <int MTW, int NSW, int WM, int WN, int GS, int OCC>
@@ -129,18 +127,26 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
                 r, (lds_void *)(lds + stage * STAGE + (i * WAVES + wave) * 1024), 16, xoff, b * 256, 0, 0);
         }
     };
-    typedef WSet<NSW, NF> Set;
+    typedef WSet<NSW> Set;
     auto load_w = [&](int b, Set &w) {
 #pragma unroll
-        for (int j = 0; j < NSW; ++j) {
+        for (int j = 0; j < NSW; ++j)
             w.w[j] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (sstrip[j] * nblk + b) * kTileBytes, 0));
+    };
+    // Scales and zero codes come in windows of four consecutive groups of a
+    // strip (GS blocks): lane (col, kq) loads column col's scale and zero
+    // byte of group 4 w + kq, so one 16-bit and one 8-bit load per strip
+    // serve GS blocks, where every lane loading its own group's pair would
+    // take 2 NF loads per strip and block (the four kq rows of a column
+    // need the same values). Groups past the strip's last are clamped to it.
+    auto load_sz = [&](int b, uint32_t (&sc)[NSW], uint32_t (&zb)[NSW]) {
+        const int g = (b / GS) * 4 + kq < ngrp ? (b / GS) * 4 + kq : ngrp - 1;
 #pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const int g = sstrip[j] * ngrp + (b * 4 + f * F) / GS;
-                w.sc[f][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, g * 32, 0);
-                w.zb[f][j] = __builtin_amdgcn_raw_buffer_load_b8(rz, zoff, g * 8, 0);
-            }
+        for (int j = 0; j < NSW; ++j) {
+            const uint32_t rec = (uint32_t)(sstrip[j] * ngrp + g);
+            sc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, rec * 32u + soff, 0, 0);
+            zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, rec * 8u + zoff, 0, 0);
         }
     };
 
@@ -163,24 +169,44 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     // after the last strip of a step, each row tile's A operand for the next
     // step is read from LDS right behind that row tile's MFMA. The matrix
     // unit thus runs while the VALU converts weights and the LDS serves reads.
-    auto compute = [&](int stage, const Set &w) {
+    auto compute = [&](int b, int stage, const Set &w, const uint32_t (&sz)[NSW]) {
         const uint8_t *st = lds + stage * STAGE;
-        uint32_t nbl[NF][NSW], nbh[NF][NSW], s2[NF][NSW];
+        // scale and zero code of each group the block uses, from the lane of
+        // the same column that loaded it (row kq = the group's place in its
+        // window)
+        uint32_t gsz[NF][NSW];
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
+        for (int f = 0; f < NF; ++f) {
+            const int src = (((b * 4 + f * F) / GS) & 3) * 64 + col * 4;  // byte index of the source lane
+#pragma unroll
+            for (int j = 0; j < NSW; ++j) gsz[f][j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sz[j]);
+        }
+        // Per strip, the fp16 bias -(1024 + z) or -(64 + z) and the scale
+        // of each step, two 16-bit values to a register: steps t and t + 2
+        // share register t % NP (low half for t < 2, high half above), and
+        // the packed add and multiply read the half they need broadcast.
+        constexpr int NP = F == 1 ? 2 : 1;
+        uint32_t bp[NP][NSW], sp[NP][NSW];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
 #pragma unroll
             for (int j = 0; j < NSW; ++j) {
-                nbl[f][j] = (0xE400u | ((w.zb[f][j] >> zsh) & 15u)) * 0x10001u;
-                nbh[f][j] = neg_bias64_from_1024(nbl[f][j]);
-                s2[f][j] = (w.sc[f][j] & 0xFFFFu) * 0x10001u;
+                const int f0 = p / F, f1 = (p + 2) / F;  // groups of steps p and p + 2
+                bp[p][j] = (0xE400u | (gsz[f0][j] >> 16)) | ((0xD400u | ((gsz[f1][j] >> 16) << 4)) << 16);
+                sp[p][j] = (gsz[f0][j] & 0xFFFFu) | (gsz[f1][j] << 16);
             }
+        auto half_of = [](uint32_t x, bool hi) -> half2v {
+            const half2v h = as_h2(x);
+            return hi ? __builtin_shufflevector(h, h, 1, 1) : __builtin_shufflevector(h, h, 0, 0);
+        };
         // word v of strip j's B operand for step t: two fp16 weights
         auto bword = [&](int t, int j, int v) -> uint32_t {
-            const int f = t / F;
+            const int p = t % NP;
+            const bool hi = t >= 2;
             const uint32_t src = (t & 1) ? (w.w[j][v] >> 8) : w.w[j][v];
             const half2v r = (as_h2(and_or(src, t < 2 ? kLoMask : kHiMask, t < 2 ? m_lo : m_hi)) +
-                              as_h2(t < 2 ? nbl[f][j] : nbh[f][j])) *
-                             as_h2(s2[f][j]);
+                              half_of(bp[p][j], hi)) *
+                             half_of(sp[p][j], hi);
             return __builtin_bit_cast(uint32_t, r);
         };
         half8 a[MTW];
@@ -217,17 +243,24 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     };
 
     Set wc, wnext;
+    uint32_t scn[NSW], zbn[NSW], sz[NSW];
     issue_x(bb, 0);
     load_w(bb, wc);
+    load_sz(bb, scn, zbn);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int b = bb; b < be; ++b) {
         const int cur = (b - bb) & 1;
-        if (b + 1 < be) {
-            issue_x(b + 1, cur ^ 1);
-            load_w(b + 1, wnext);
+        if (b == bb || b % GS == 0) {  // a new window (loaded during the previous block)
+#pragma unroll
+            for (int j = 0; j < NSW; ++j) sz[j] = (scn[j] & 0xFFFFu) | (((zbn[j] >> zsh) & 15u) << 16);
         }
-        compute(cur, wc);
+        if (b + 1 < be) issue_x(b + 1, cur ^ 1);
+        // unconditional (a conditional reload would keep the old set live
+        // beside the new one): after the last block it reloads that block
+        load_w(b + 1 < be ? b + 1 : b, wnext);
+        if (b + 1 < be && (b + 1) % GS == 0) load_sz(b + 1, scn, zbn);
+        compute(b, cur, wc, sz);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         wc = wnext;
