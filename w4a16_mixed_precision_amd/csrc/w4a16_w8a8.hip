@@ -286,22 +286,25 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
 #pragma unroll
         for (int j = 0; j < NSW; ++j) acc[mt][j] = int32x4{0, 0, 0, 0};
 
-    // One 64-row step: row tile after row tile, each multiplied with the
-    // NSW strips' B operands of the step; a row tile's A operand is read
-    // from LDS two row tiles ahead, so only three A operands are live (what
-    // lets 128-row wave tiles keep two waves per SIMD).
-    auto compute = [&](int stage, int half, const WHalf &w) {
-        const uint8_t *st = lds + stage * STAGE;
+    // A 64-row step: row tile after row tile, each multiplied with the NSW
+    // strips' B operands of the step. A operands stream from LDS two row
+    // tiles ahead, across the block's four steps (only three are live, which
+    // lets 128-row wave tiles keep two waves per SIMD); a0 and a1 carry the
+    // stream from one half block to the next.
+    auto a_at = [&](int stage, int s, int mt) {
+        return *reinterpret_cast<const int32x4 *>(lds + stage * STAGE + (mt * 16 + col) * kW8Block +
+                                                  (((4 * s + kq) ^ col) * 16));
+    };
+    auto compute = [&](int stage, int half, const WHalf &w, int32x4 &a0, int32x4 &a1) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             const int s = 2 * half + s2;
-            auto a_at = [&](int mt) {
-                return *reinterpret_cast<const int32x4 *>(st + (mt * 16 + col) * kW8Block + (((4 * s + kq) ^ col) * 16));
-            };
-            int32x4 a0 = a_at(0), a1 = MTW > 1 ? a_at(1) : a0;
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
-                const int32x4 a2 = mt + 2 < MTW ? a_at(mt + 2) : a0;
+                // the operand two places further along the (step, row tile)
+                // stream; nothing past the block's last step
+                const int nx = s * MTW + mt + 2;
+                const int32x4 a2 = nx < 4 * MTW ? a_at(stage, nx / MTW, nx % MTW) : a0;
 #pragma unroll
                 for (int j = 0; j < NSW; ++j)
                     acc[mt][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, __builtin_bit_cast(int32x4, w[j][s2]),
@@ -317,20 +320,35 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
         WHalf w0, w1;
         issue_x(bb, 0);
         load_w(2 * bb, w0);
+        load_w(2 * bb + 1, w1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        for (int b = bb; b < be; ++b) {
+        // weights two half blocks ahead: three half-block sets rotate, so a
+        // half is requested while the two halves before it are multiplied
+        const int hlast = 2 * be - 1;
+        auto block = [&](int b, WHalf &p, WHalf &q, WHalf &r) {
             const int cur = (b - bb) & 1;
+            int32x4 a0 = a_at(cur, 0, 0), a1 = MTW > 1 ? a_at(cur, 0, 1) : a_at(cur, 1, 0);
             if (b + 1 < be) issue_x(b + 1, cur ^ 1);
-            load_w(2 * b + 1, w1);
-            compute(cur, 0, w0);
-            // unconditional (a conditional reload would keep the old set
-            // live beside the new one): after the last block it reads the
-            // block's first half again, inside the weights, and is not used
-            load_w(b + 1 < be ? 2 * b + 2 : 2 * b, w0);
-            compute(cur, 1, w1);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            // unconditional, clamped to the slice's last half (reloaded,
+            // not used) so that every path issues the same loads
+            load_w(2 * b + 2 < hlast ? 2 * b + 2 : hlast, r);
+            compute(cur, 0, p, a0, a1);
+            load_w(2 * b + 3 < hlast ? 2 * b + 3 : hlast, p);
+            compute(cur, 1, q, a0, a1);
+            // the next block's X copies, issued before the 4 NSW weight
+            // loads of this block, have landed; the barrier makes every
+            // wave's copies visible and frees the stage just read
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NSW));
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        WHalf w2;
+        for (int b = bb; b < be; b += 3) {
+            block(b, w0, w1, w2);
+            if (b + 1 < be) block(b + 1, w2, w0, w1);
+            if (b + 2 < be) block(b + 2, w1, w2, w0);
         }
     }
 
