@@ -112,7 +112,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(packed + weight_bytes(K, N), (uint32_t)scale_bytes(K, N, 32 * GS));
     const __amdgpu_buffer_rsrc_t rz =
         make_rsrc(packed + weight_bytes(K, N) + scale_bytes(K, N, 32 * GS), (uint32_t)zero_bytes(K, N, 32 * GS));
-    const uint32_t woff = lane * 16, soff = col * 2, zoff = col >> 1;
+    const uint32_t woff = lane * 16;
     int sstrip[NSW];
 #pragma unroll
     for (int j = 0; j < NSW; ++j) sstrip[j] = strip_w + j < nstrip ? strip_w + j : nstrip - 1;
@@ -139,14 +139,22 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     // byte of group 4 w + kq, so one 16-bit and one 8-bit load per strip
     // serve GS blocks, where every lane loading its own group's pair would
     // take 2 NF loads per strip and block (the four kq rows of a column
-    // need the same values). Groups past the strip's last are clamped to it.
+    // need the same values). Groups past the strip's last read the next
+    // strip's records, or zeros past the last strip (the whole offset is the
+    // per-lane one, so the descriptor bound decides); they are not used.
+    // The lane's byte offsets within a window, kq 32 + 2 col and kq 8 +
+    // col / 2, are woff / 8 and woff / 32: recomputed at each window (the
+    // asm keeps the compiler from holding them, or spilling them, across
+    // the loop).
     auto load_sz = [&](int b, uint32_t (&sc)[NSW], uint32_t (&zb)[NSW]) {
-        const int g = (b / GS) * 4 + kq < ngrp ? (b / GS) * 4 + kq : ngrp - 1;
+        uint32_t ls, lz;
+        asm volatile("v_lshrrev_b32 %0, 3, %1" : "=v"(ls) : "v"(woff));
+        asm volatile("v_lshrrev_b32 %0, 5, %1" : "=v"(lz) : "v"(woff));
 #pragma unroll
         for (int j = 0; j < NSW; ++j) {
-            const uint32_t rec = (uint32_t)(sstrip[j] * ngrp + g);
-            sc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, rec * 32u + soff, 0, 0);
-            zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, rec * 8u + zoff, 0, 0);
+            const uint32_t rec = (uint32_t)(sstrip[j] * ngrp + (b / GS) * 4);
+            sc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, rec * 32u + ls, 0, 0);
+            zb[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, rec * 8u + lz, 0, 0);
         }
     };
 
@@ -159,7 +167,6 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     // LDS byte offset of this lane's A operand for row tile mt, step t.
     const int rbase = wm * MTW * 16;
     auto a_off = [&](int mt, int t) { return (rbase + mt * 16 + col) * 256 + (((4 * t + kq) ^ col) * 16); };
-    const int zsh = (col & 1) * 4;
 
     // One K block: four 32-row steps x NSW strips = 4 NSW strip groups of MTW
     // MFMAs each. The B operand of a strip for the next step is dequantized
@@ -252,6 +259,9 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     for (int b = bb; b < be; ++b) {
         const int cur = (b - bb) & 1;
         if (b == bb || b % GS == 0) {  // a new window (loaded during the previous block)
+            // this column's nibble of the zero byte: (woff / 4) & 4 = 4 (col & 1)
+            uint32_t zsh;
+            asm volatile("v_lshrrev_b32 %0, 2, %1\n\tv_and_b32 %0, 4, %0" : "=&v"(zsh) : "v"(woff));
 #pragma unroll
             for (int j = 0; j < NSW; ++j) sz[j] = (scn[j] & 0xFFFFu) | (((zbn[j] >> zsh) & 15u) << 16);
         }
