@@ -297,13 +297,18 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
         }
 }
 
+// Sum of the S fp32 partials in split order, rounded once to fp16: four
+// outputs per thread (one 16-byte load per split, one 8-byte store); M N is
+// a multiple of four (N % 16 == 0).
 __global__ void __launch_bounds__(256)
-prefill_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ Y, int64_t MN, int S) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < MN;
+prefill_reduce_kernel(const floatx4 *__restrict__ part, uint32_t *__restrict__ Y, int64_t n4, int S) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
          i += (int64_t)gridDim.x * blockDim.x) {
-        float v = 0.f;
-        for (int s = 0; s < S; ++s) v += part[(size_t)s * MN + i];
-        Y[i] = f32_to_f16_bits(v);
+        floatx4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int s = 0; s < S; ++s) v += part[(size_t)s * n4 + i];
+        Y[2 * i] = (uint32_t)f32_to_f16_bits(v[0]) | ((uint32_t)f32_to_f16_bits(v[1]) << 16);
+        Y[2 * i + 1] = (uint32_t)f32_to_f16_bits(v[2]) | ((uint32_t)f32_to_f16_bits(v[3]) << 16);
     }
 }
 
@@ -421,11 +426,11 @@ hipError_t launch_prefill(const uint16_t *X, const uint8_t *packed, int M, int N
     float *part = p.splits > 1 ? static_cast<float *>(workspace) : nullptr;
     hipError_t e = launch_index(p.ci, X, packed, M, N, K, G, Y, part, p.splits, p.slice_blocks, stream);
     if (e != hipSuccess || p.splits <= 1) return e;
-    const int64_t MN = (int64_t)M * N;
-    int64_t blocks = (MN + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, Y, MN,
-                       p.splits);
+    const int64_t n4 = (int64_t)M * N / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(prefill_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const floatx4 *>(part), reinterpret_cast<uint32_t *>(Y), n4, p.splits);
     return hipGetLastError();
 }
 
