@@ -55,6 +55,37 @@ def test_quantize_matches_oracle(K, N, G):
     _check_packed(W, G, q, z, s)
 
 
+def test_quotients_near_half_integers():
+    # Millions of weights placed at and around the half-integers (n + 1/2) s
+    # of their group's stored scale: exact ties where fp16 can hold them,
+    # their fp16 neighbours one and two steps away otherwise. The codes must
+    # be the oracle's (float64 division) bit for bit.
+    G, K, N = 128, 128 * 16, 4096
+    rng = np.random.default_rng(77)
+    ngrp = K // G
+    lo = -np.float16(rng.uniform(0.0, 4.0, size=(ngrp, N)))
+    span = np.exp2(rng.uniform(-10.0, 3.0, size=(ngrp, N)))
+    hi = (lo.astype(np.float64) + span).astype(np.float16)
+    W = np.repeat(lo, G, axis=0).reshape(ngrp, G, N).copy()
+    W[:, 0, :] = hi
+    _, z, s = oracle.quantize(W.reshape(K, N), G)   # the stored scales of these ranges
+    n = rng.integers(0, 16, size=(ngrp, G - 2, N)) - z[:, None, :].astype(np.int64)
+    t = ((n + 0.5) * s[:, None, :].astype(np.float64)).astype(np.float16)
+    steps = rng.integers(-2, 3, size=t.shape).astype(np.int16)
+    bits = t.view(np.int16)
+    moved = np.where(t >= 0, bits + steps, bits - steps).astype(np.int16).view(np.float16)
+    moved = np.where(np.isfinite(moved), moved, t)
+    W[:, 2:, :] = np.clip(moved, lo[:, None, :], hi[:, None, :])
+    W = W.reshape(K, N)
+    _, z2, s2 = oracle.quantize(W, G)
+    assert np.array_equal(z2, z) and np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+    ties = np.modf(np.abs(W.reshape(ngrp, G, N).astype(np.float64) / s[:, None, :]))[0] == 0.5
+    say(f"near-half-integer quotients: {W.size} weights, {int(ties.sum())} exact ties")
+    assert ties.sum() > 1000
+    q, z, s = _check_plain(W, G)
+    _check_packed(W, G, q, z, s)
+
+
 def _edge_matrix(G):
     """Columns of hand-built groups, one case per 16-column strip."""
     K, N = 2 * max(G, 128), 144

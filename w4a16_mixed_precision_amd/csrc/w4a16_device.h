@@ -154,6 +154,23 @@ constexpr float kScaleFloor = 6.103515625e-05f;
 // unless |x / s| < 1/2, where c = 0 and r = x), so comparing |r| with s / 2
 // settles the decision: beyond it c moves one step towards x / s, at it
 // (an exact tie) the even neighbour wins.
+// 1.5 * 2^23 + rint(x / s) for an fp16 value x and an fp16 value s
+// (normal; inv = fp32(1/s)), valid while |x / s| < 2^12. The reciprocal
+// product p = x inv and one correction step p' = p + (x - p s) inv give the
+// quotient within |x / s| 2^-46 before p' is rounded to float32: an exact
+// tie n + 1/2 (representable) comes out exact and rounds to even when the
+// magic constant is added, and every other quotient of two fp16 numbers lies
+// at least 2^-12 from a half-integer, farther than p' can be off (its
+// rounding moves it by at most 2^-20 there). Four operations where the
+// residual test of round_quotient_magic takes about nine; not valid for a
+// float32 scale, whose quotients can come within 2^-25 of a half-integer.
+__device__ inline float round_quotient_fp16(float x, float s, float inv) {
+    const float p = x * inv;
+    const float r = __builtin_fmaf(-p, s, x);
+    const float q = __builtin_fmaf(r, inv, p);
+    return q + kRoundMagic;
+}
+
 __device__ inline float round_quotient_magic(float x, float s, float inv, float half_s) {
     float y = __builtin_fmaf(x, inv, kRoundMagic);
     const float c = y - kRoundMagic;

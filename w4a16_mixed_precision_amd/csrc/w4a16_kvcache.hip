@@ -141,13 +141,13 @@ __device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c
     const float s32 = __builtin_fmaxf((xmax - xmin) / (float)L, kScaleFloor);
     const _Float16 s16 = (_Float16)s32;
     const float sf = (float)s16;
-    const float inv = 1.0f / sf, half_s = 0.5f * sf;
+    const float inv = 1.0f / sf;
     // float64 division decides rint of an fp16 quotient exactly
     const double zr = __builtin_rint(-(double)xmin / (double)sf);
     const int z = zr < 0.0 ? 0 : (zr > (double)L ? L : (int)zr);
     const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
-    const float y0 = __builtin_amdgcn_fmed3f(round_quotient_magic(x0, sf, inv, half_s), lo, hi);
-    const float y1 = __builtin_amdgcn_fmed3f(round_quotient_magic(x1, sf, inv, half_s), lo, hi);
+    const float y0 = __builtin_amdgcn_fmed3f(round_quotient_fp16(x0, sf, inv), lo, hi);
+    const float y1 = __builtin_amdgcn_fmed3f(round_quotient_fp16(x1, sf, inv), lo, hi);
     c0 = __builtin_bit_cast(uint32_t, y0) - kRoundMagicBits + z;
     c1 = __builtin_bit_cast(uint32_t, y1) - kRoundMagicBits + z;
     par = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)z << 16);

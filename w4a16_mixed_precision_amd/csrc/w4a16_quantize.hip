@@ -60,14 +60,13 @@ struct QParams {
     float hi;      // lo + 15
     uint32_t zb;   // z - bits(1.5 * 2^23)
     float s;       // the stored scale, in float32
-    float half_s;  // s / 2 (exact)
 };
 
-// 1.5 * 2^23 + clamp(rint(w / s) + z, 0, 15) as a float (see the header
-// comment: one fused multiply-add gives rint of the reciprocal product, and
-// the exact residual moves an exact tie to its even neighbour).
+// 1.5 * 2^23 + clamp(rint(w / s) + z, 0, 15) as a float (w and s are fp16
+// values: the corrected reciprocal product decides rint of the exact
+// quotient, ties to even)
 __device__ inline float code_float(float w, const QParams &p) {
-    return __builtin_amdgcn_fmed3f(round_quotient_magic(w, p.s, p.inv, p.half_s), p.lo, p.hi);
+    return __builtin_amdgcn_fmed3f(round_quotient_fp16(w, p.s, p.inv), p.lo, p.hi);
 }
 
 template <int KB, int CB>
@@ -185,7 +184,6 @@ quantize_kernel(const uint16_t *__restrict__ W, int K, int N, uint8_t *__restric
             pr.hi = pr.lo + 15.0f;
             pr.zb = (uint32_t)z - kRoundMagicBits;
             pr.s = sf;
-            pr.half_s = 0.5f * sf;
             prm[g][c] = pr;
             zl[g][c] = (uint8_t)z;
             const int n = c0 + c;
