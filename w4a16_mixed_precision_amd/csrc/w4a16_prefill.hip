@@ -235,9 +235,13 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
             for (int mt = 0; mt < MTW; ++mt) {
                 acc[mt][j] = mfma16x16x32(a[mt], __builtin_bit_cast(half8, bw[j]), acc[mt][j]);
                 if (t < 3 && j == NSW - 1) a[mt] = *reinterpret_cast<const half8 *>(st + a_off(mt, t + 1));
-                // two independent words at a time (their dependent op chains
-                // interleave), after every fourth MFMA (every second for MTW 4)
-                constexpr int kSlots = MTW >= 8 ? MTW / 4 : MTW / 2;  // dequant slots per group
+                // all four words after the group's last MFMA for 8 or more
+                // row tiles (graph-timed against two words after every
+                // fourth MFMA: 399 against 403 us at 2048 x 4096 x 28672,
+                // 98 against 102.5 us at 512 x 8192 x 10240, G = 64; one
+                // slot at the first, fourth or sixth MFMA sat in between);
+                // two words after every second MFMA for MTW 4
+                constexpr int kSlots = MTW >= 8 ? 1 : MTW / 2;  // dequant slots per group
                 constexpr int kEvery = MTW / kSlots;
                 if (pending && mt % kEvery == kEvery - 1) {
                     const int slot = mt / kEvery;
