@@ -14,7 +14,7 @@
 //   s = fp16(max(fp32(max - min) / L, 2^-14)),
 //   z = clamp(rint(-min / s), 0, L), c = clamp(rint(x / s) + z, 0, L)
 // with rint the nearest integer to the exact quotient, ties to even (the
-// zero by a float64 division, the codes by round_quotient_magic).
+// zero and the codes by round_quotient_fp16).
 //
 // Cache region of one (block, KV head), KC = 64 * 128 * bits / 8 bytes:
 //   [0, KC)        K codes, token-major rows of 128 codes
@@ -142,9 +142,10 @@ __device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c
     const _Float16 s16 = (_Float16)s32;
     const float sf = (float)s16;
     const float inv = 1.0f / sf;
-    // float64 division decides rint of an fp16 quotient exactly
-    const double zr = __builtin_rint(-(double)xmin / (double)sf);
-    const int z = zr < 0.0 ? 0 : (zr > (double)L ? L : (int)zr);
+    // the zero code: rint(-xmin / s) clamped to [0, L], decided like the
+    // codes (-xmin and s are fp16 values)
+    const float zf = __builtin_amdgcn_fmed3f(round_quotient_fp16(-xmin, sf, inv), kRoundMagic, kRoundMagic + (float)L);
+    const int z = (int)(__builtin_bit_cast(uint32_t, zf) - kRoundMagicBits);
     const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
     const float y0 = __builtin_amdgcn_fmed3f(round_quotient_fp16(x0, sf, inv), lo, hi);
     const float y1 = __builtin_amdgcn_fmed3f(round_quotient_fp16(x1, sf, inv), lo, hi);
