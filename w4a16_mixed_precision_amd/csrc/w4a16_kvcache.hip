@@ -138,10 +138,12 @@ __device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c
     const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
     float xmax, xmin;
     wave_range(pair, xmax, xmin);
-    const float s32 = __builtin_fmaxf((xmax - xmin) / (float)L, kScaleFloor);
+    const float s32 = __builtin_fmaxf(div_steps(xmax - xmin, (float)L, 1.0f / (float)L), kScaleFloor);
     const _Float16 s16 = (_Float16)s32;
     const float sf = (float)s16;
-    const float inv = 1.0f / sf;
+    // within one ulp of 1/s, which the code decision allows (its corrected
+    // product stays within |x/s| 2^-44 of the quotient)
+    const float inv = __builtin_amdgcn_rcpf(sf);
     // the zero code: rint(-xmin / s) clamped to [0, L], decided like the
     // codes (-xmin and s are fp16 values)
     const float zf = __builtin_amdgcn_fmed3f(round_quotient_fp16(-xmin, sf, inv), kRoundMagic, kRoundMagic + (float)L);
