@@ -170,9 +170,9 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 
     // One K block: four 32-row steps x NSW strips = 4 NSW strip groups of MTW
     // MFMAs each. The B operand of a strip for the next step is dequantized
-    // during the following strip group, two 32-bit words (four fp16 weights)
-    // after every fourth MFMA, into the registers the strip's own MFMAs have
-    // finished reading;
+    // once that strip's group has issued its MFMAs (all four 32-bit words
+    // after the group's last MFMA for 8 row tiles per wave, two words after
+    // every second one for 4), into the registers those MFMAs read;
     // after the last strip of a step, each row tile's A operand for the next
     // step is read from LDS right behind that row tile's MFMA. The matrix
     // unit thus runs while the VALU converts weights and the LDS serves reads.
