@@ -165,25 +165,28 @@ quantize_kernel(const uint16_t *__restrict__ W, int K, int N, uint8_t *__restric
                 wmin = __builtin_elementwise_minimum(wmin, (float)__builtin_bit_cast(half2v, pmin[sl][c >> 1])[c & 1]);
             }
             if (!__builtin_isfinite(wmax) || !__builtin_isfinite(wmin)) *bad = 1;
-            const float s32 = __builtin_fmaxf((wmax - wmin) / 15.0f, kScaleFloor);
+            // s = fp16(max(fp32(max - min) / 15, 2^-14)): the division in
+            // three operations (correctly rounded for every float32
+            // difference of fp16 numbers)
+            const float s32 = __builtin_fmaxf(div_steps(wmax - wmin, 15.0f, 1.0f / 15.0f), kScaleFloor);
             const _Float16 s16 = (_Float16)s32;
             const float sf = (float)s16;
-            const double sd = (double)sf;
-            // float64 division decides rint of these quotients exactly (see the
-            // header comment; |w / s| < 2^31 for fp16 w and s >= 2^-14)
-            const double zr = __builtin_rint(-(double)wmin / sd);
-            const int z = zr < 0.0 ? 0 : (zr > 15.0 ? 15 : (int)zr);
-            // codes are monotone in w: the group's extremes bound |q - z|
-            const double qlo = __builtin_fmin(__builtin_fmax(__builtin_rint((double)wmin / sd) + z, 0.0), 15.0);
-            const double qhi = __builtin_fmin(__builtin_fmax(__builtin_rint((double)wmax / sd) + z, 0.0), 15.0);
-            const double dmax = __builtin_fmax(__builtin_fabs(qlo - z), __builtin_fabs(qhi - z));
-            if (!(dmax * sd < 65520.0)) *bad = 1;
             QParams pr;
-            pr.inv = 1.0f / sf;
+            pr.inv = __builtin_amdgcn_rcpf(sf);  // one ulp is within what the code decision allows
+            // z = clamp(rint(-min / s), 0, 15), decided like the codes (the
+            // operands are fp16); the codes are monotone in w, so the
+            // group's extremes bound |q - z| for the fp16 range check
+            const float zf = __builtin_amdgcn_fmed3f(round_quotient_fp16(-wmin, sf, pr.inv), kRoundMagic,
+                                                     kRoundMagic + 15.0f);
+            const int z = (int)(__builtin_bit_cast(uint32_t, zf) - kRoundMagicBits);
             pr.lo = kRoundMagic - (float)z;
             pr.hi = pr.lo + 15.0f;
             pr.zb = (uint32_t)z - kRoundMagicBits;
             pr.s = sf;
+            const int qlo = (int)(__builtin_bit_cast(uint32_t, code_float(wmin, pr)) - kRoundMagicBits);  // q - z
+            const int qhi = (int)(__builtin_bit_cast(uint32_t, code_float(wmax, pr)) - kRoundMagicBits);
+            const int dmax = qlo < 0 ? (-qlo > qhi ? -qlo : qhi) : qhi;
+            if (!((float)dmax * sf < 65520.0f)) *bad = 1;
             prm[g][c] = pr;
             zl[g][c] = (uint8_t)z;
             const int n = c0 + c;
