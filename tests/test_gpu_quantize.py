@@ -169,16 +169,20 @@ def test_quantize_pack_equals_pack_of_quantize():
     assert np.array_equal(a, b)
 
 
-def test_tile_width_knob_gives_the_same_bytes(monkeypatch):
-    W = synth.draw_fp16_weights(512, 272, seed=4)
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
+def test_tile_width_knob_gives_the_same_bytes(monkeypatch, G):
+    # 64-, 128- and 256-column tiles (256 where the group size allows it,
+    # else the knob falls back to 128) and a ragged column tail
+    W = synth.draw_fp16_weights(512, 592, seed=4)
     Wd = dev(W)
     outs = []
-    for cb in ("64", "128"):
+    for cb in ("64", "128", "256"):
         monkeypatch.setenv("W4A16_QUANTIZE_CB", cb)
-        outs.append(host(w4.w4a16_quantize_pack(Wd, 128)))
-        q, z, s = (host(t) for t in w4.w4a16_quantize(Wd, 128))
-        outs.append(np.concatenate([q.ravel(), z.ravel(), s.view(np.uint8).ravel()]))
-    assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+        packed = host(w4.w4a16_quantize_pack(Wd, G))
+        q, z, s = (host(t) for t in w4.w4a16_quantize(Wd, G))
+        outs.append((packed, np.concatenate([q.ravel(), z.ravel(), s.view(np.uint8).ravel()])))
+    for packed, plain in outs[1:]:
+        assert np.array_equal(packed, outs[0][0]) and np.array_equal(plain, outs[0][1])
 
 
 def test_quantized_weights_through_the_gemm():

@@ -284,12 +284,20 @@ hipError_t launch_gs(const uint16_t *W, int K, int N, int cb, uint8_t *packed, u
                      uint16_t *s, int *bad, hipStream_t stream) {
     constexpr int KB = 32 * GS > kBlockK ? 32 * GS : kBlockK;
     const int tiles = K / KB;
+    if (cb == 256 && !(GS == 2 || GS == 4)) cb = 128;  // 256-column tiles need 64-row range slices
     const int gx = (N + cb - 1) / cb;
     // tiles per workgroup: one (measured fastest on the 8192 x 57344 weight;
     // the pipelined loop is kept for other devices and shapes, via the knob)
     int tpb = 1;
     if (const char *e = getenv("W4A16_QUANTIZE_TPB")) tpb = atoi(e) > 0 ? atoi(e) : 1;
     const unsigned gy = (unsigned)((tiles + tpb - 1) / tpb);
+    if constexpr (GS == 2 || GS == 4) {
+        if (cb == 256) {
+            hipLaunchKernelGGL((quantize_kernel<GS, 256, PACKED>), dim3((unsigned)gx, gy), dim3(kQThreads), 0,
+                               stream, W, K, N, packed, q, z, s, bad, tpb);
+            return hipGetLastError();
+        }
+    }
     if (cb == 128) {
         hipLaunchKernelGGL((quantize_kernel<GS, 128, PACKED>), dim3((unsigned)gx, gy), dim3(kQThreads), 0,
                            stream, W, K, N, packed, q, z, s, bad, tpb);
@@ -304,9 +312,13 @@ template <bool PACKED>
 hipError_t launch_mode(const uint16_t *W, int K, int N, int G, uint8_t *packed, uint8_t *q, uint8_t *z,
                        uint16_t *s, int *bad, hipStream_t stream) {
     // 128 columns: 256-byte row segments (a read-only probe of this access
-    // pattern on the 8192 x 57344 weight: 225 us against 240 us for 64)
+    // pattern on the 8192 x 57344 weight: 225 us against 240 us for 64).
+    // 256 columns (G = 64, 128; W4A16_QUANTIZE_CB=256) measured 3% faster
+    // on that weight (264-268 against 274-276 us) but slower on smaller
+    // ones (4096 x 28672: 75-76 against 71-73 us; 4096 x 14336, G = 64: 53
+    // against 46 us), with half as many workgroups.
     int cb = 128;
-    if (const char *e = getenv("W4A16_QUANTIZE_CB")) cb = atoi(e) == 64 ? 64 : 128;
+    if (const char *e = getenv("W4A16_QUANTIZE_CB")) cb = atoi(e) == 64 ? 64 : (atoi(e) == 256 ? 256 : 128);
     switch (G) {
         case 32: return launch_gs<1, PACKED>(W, K, N, cb, packed, q, z, s, bad, stream);
         case 64: return launch_gs<2, PACKED>(W, K, N, cb, packed, q, z, s, bad, stream);
