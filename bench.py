@@ -60,13 +60,44 @@ if ROOT not in sys.path:
 METRIC = "W4A16 GEMM effective TB/s at M=1–16 and TFLOPS at M=2048 (% of roofline)"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+# Before each timed region the same work runs untimed for this long: after
+# an idle period the shader clock climbs over the first tens of milliseconds
+# of sustained load (a matrix-core-bound launch timed from idle runs ~20%
+# slower for its first few milliseconds), and every figure here is quoted at
+# the clock a sustained load holds.
+STEADY_MS = 250.0
+
+
+def steady(fn, min_ms=None):
+    """Calls fn() (asynchronous GPU work) in batches of about 20 ms, one
+    synchronization per batch, until at least `min_ms` (default STEADY_MS)
+    milliseconds have passed. Returns the number of calls made."""
+    import torch
+    min_ms = STEADY_MS if min_ms is None else min_ms
+    if min_ms <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    fn()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t, 1e-5)
+    k = max(1, int(0.02 / one))
+    n = 1
+    start = time.perf_counter()
+    while (time.perf_counter() - start) * 1e3 < min_ms:
+        for _ in range(k):
+            fn()
+        torch.cuda.synchronize()
+        n += k
+    return n
 
 
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=0, help="timed steps (default: one rotation, at least 40)")
-    p.add_argument("--warmup", type=int, default=0, help="untimed steps (default: one rotation)")
+    p.add_argument("--warmup", type=int, default=0,
+                   help="untimed steps (default: whole rotations for at least --steady-ms)")
     p.add_argument("--workload", default="llama3_8b_decode")
     p.add_argument("--instance", default="",
                    help="comma-separated instance names (workload/matrix/M...): run only these (profiling)")
@@ -78,6 +109,10 @@ def parse_args(argv=None):
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="before timing, run one device copy of BYTES bytes (reference for HBM counters)")
     p.add_argument("--detail", action="store_true", help="per-instance lines to stderr")
+    p.add_argument("--steady-ms", type=float, default=STEADY_MS,
+                   help="untimed run of the same work before each secondary and per-instance timing "
+                        "(and before the step when --warmup is not given), so timing starts at the "
+                        "sustained clock")
     p.add_argument("--quantizer-only", action="store_true",
                    help="time only the offline quantizer (fp16 W -> packed) and print its line")
     p.add_argument("--w8a8-only", action="store_true",
@@ -169,9 +204,11 @@ class Runner:
         torch.cuda.synchronize()
         return rotation, singles
 
-    def time_steps(self, steps, warmup, eager, only=None):
-        """Times exactly `steps` steps after `warmup` untimed ones; returns
-        ms per step."""
+    def time_steps(self, steps, warmup, eager, only=None, steady_ms=0.0):
+        """Times exactly `steps` steps after `warmup` untimed ones, followed
+        by whole untimed rotations for at least `steady_ms` milliseconds;
+        returns ms per step. `self.last_warmup` holds the number of untimed
+        steps run."""
         torch = self.torch
         C = self.copies
 
@@ -192,6 +229,8 @@ class Runner:
         if not eager:
             rotation, singles = self.capture(only)
         run(0, warmup)
+        warmup += C * steady(lambda: run(0, C), steady_ms)
+        self.last_warmup = warmup
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -275,7 +314,7 @@ def cpu_baseline(runner, sel=None, max_macs=4e9, min_seconds=10.0, max_passes=20
     }
 
 
-def read_yardstick_us(nbytes, rotate_bytes, reps=4):
+def read_yardstick_us(nbytes, rotate_bytes, reps=4, steady_ms=None):
     """Microseconds per launch of w4a16_stream_read over `nbytes` bytes: the
     same protocol as the GEMM instances (copies rotated so that every launch
     reads from HBM, one HIP graph holding a whole rotation, HIP events around
@@ -296,6 +335,7 @@ def read_yardstick_us(nbytes, rotate_bytes, reps=4):
             for b in bufs:
                 w4.w4a16_stream_read(b, sink, stream=st)
     g.replay()
+    steady(g.replay, steady_ms)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -364,7 +404,7 @@ def run_other_workloads(args):
         insts = synth.workload_instances(wl)
         r = Runner(insts, args.rotate_gib * 2 ** 30, max_copies=64 if wl == "tiny" else None)
         for k, inst in enumerate(insts):
-            ms = r.time_steps(2 * r.copies, r.copies, args.eager, only=k)
+            ms = r.time_steps(2 * r.copies, r.copies, args.eager, only=k, steady_ms=args.steady_ms)
             row = {"instance": inst.name, "M": inst.M, "K": inst.K, "N": inst.N, "G": inst.G,
                    "us": ms * 1e3, "kernel": kernel_name(inst), "rotation_copies": r.copies}
             row.update(roofline_row(inst, ms * 1e3))
@@ -383,8 +423,9 @@ def run_prefill_secondary(args):
     import synth
     inst = synth.workload_instances("llama3_8b_prefill")[0]
     r = Runner([inst], args.rotate_gib * 2 ** 30)
-    ms = r.time_steps(2 * r.copies, r.copies, args.eager)
+    ms = r.time_steps(4 * r.copies, r.copies, args.eager, steady_ms=args.steady_ms)
     tflops = inst.flops() / (ms * 1e-3) / 1e12
+    copies = r.copies
     del r
     torch.cuda.empty_cache()
     return {
@@ -393,6 +434,8 @@ def run_prefill_secondary(args):
         "unit": "TFLOP/s",
         "ms_per_launch": ms,
         "frac_of_mfma_f16_peak": tflops / MFMA_F16_PEAK_TFLOPS,
+        "timing": "HIP graph replay over %d rotated copies, %d launches timed after %.0f ms of the same "
+                  "launches untimed" % (copies, 4 * copies, args.steady_ms),
     }
 
 
@@ -416,6 +459,7 @@ def run_quantize_secondary(args, calls=20):
     packed = torch.empty(w4.w4a16_packed_bytes(K, N, G), dtype=torch.uint8, device="cuda")
     for _ in range(3):
         w4.w4a16_quantize_pack(W, G, packed)
+    steady(lambda: w4.w4a16_quantize_pack(W, G, packed), args.steady_ms)
     st = torch.cuda.current_stream()
     times = []
     for _ in range(calls):
@@ -436,7 +480,8 @@ def run_quantize_secondary(args, calls=20):
         "ms_per_call": ms,
         "bytes_per_call": nbytes,
         "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "timing": "median of %d synchronous calls, HIP events around each call" % calls,
+        "timing": "median of %d synchronous calls, HIP events around each call, after %.0f ms of "
+                  "untimed calls" % (calls, args.steady_ms),
     }
 
 
@@ -482,8 +527,11 @@ def run_kv_secondary(args, bits, reps=20):
     lengths = torch.full((B,), T, dtype=torch.int32, device="cuda")
     ws = torch.empty(w4.w4a16_kv_attention_workspace_bytes(B, hkv, nblk), dtype=torch.uint8, device="cuda")
     sm = 1 / math.sqrt(D)
-    for c in caches:
-        w4.w4a16_kv_attention(q, c, table, lengths, bits, hkv, sm, out=out, workspace=ws)
+    def attend_all():
+        for c in caches:
+            w4.w4a16_kv_attention(q, c, table, lengths, bits, hkv, sm, out=out, workspace=ws)
+    attend_all()
+    steady(attend_all, args.steady_ms)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -543,6 +591,7 @@ def run_fp16_library(args, rows, prefill_ms, reps=10):
             for W in Ws:
                 torch.matmul(X, W, out=Y)
         g.replay()
+        steady(g.replay, args.steady_ms)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -598,6 +647,7 @@ def run_w8a8_secondary(args, reps=20):
         with torch.cuda.graph(g):
             calls()
         g.replay()
+        steady(g.replay, args.steady_ms)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -681,10 +731,15 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    ms_step = runner.time_steps(steps, warmup, args.eager, only=in_metric)
+    # an explicit --warmup is exactly that many untimed steps; the default
+    # adds whole rotations until the clock has settled
+    ms_step = runner.time_steps(steps, warmup, args.eager, only=in_metric,
+                                steady_ms=0.0 if args.warmup else args.steady_ms)
+    warmup = runner.last_warmup
     ms_eager = ms_step if args.eager else runner.time_steps(runner.copies, 4, True, only=in_metric)
     # per-instance launch times: the same timed loop over one instance at a time
-    per = [runner.time_steps(2 * runner.copies, runner.copies, args.eager, only=i) for i in range(len(insts))]
+    per = [runner.time_steps(2 * runner.copies, runner.copies, args.eager, only=i, steady_ms=args.steady_ms)
+           for i in range(len(insts))]
 
     total_bytes = sum(insts[k].alg_bytes() for k in in_metric)
     total_flops = sum(insts[k].flops() for k in in_metric)
@@ -700,7 +755,7 @@ def main(argv=None):
         }
         if not prefill:
             # the achievable-read yardstick on the same byte count
-            rus = read_yardstick_us(inst.alg_bytes(), args.rotate_gib * 2 ** 30)
+            rus = read_yardstick_us(inst.alg_bytes(), args.rotate_gib * 2 ** 30, steady_ms=args.steady_ms)
             row["read_us"] = rus
             row["read_TBps"] = inst.alg_bytes() / (rus * 1e-6) / 1e12
             row["frac_of_read"] = rus / (ms * 1e3)
