@@ -46,6 +46,8 @@
 //   multiplied (two register sets), the pages' double-buffered KV pipeline.
 // * Each wave writes a partial (max, sum, unnormalized O) per head; a second
 //   kernel merges the chunks of a sequence (log-sum-exp).
+#include <stdlib.h>
+
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -68,76 +70,78 @@ struct KvGeom {
 
 __device__ inline int v_position(int t) { return 16 * ((t & 15) >> 2) + 8 * (t >> 5) + 4 * ((t >> 4) & 1) + (t & 3); }
 
-// Maximum and minimum of a wave's 128 fp16 values, two per lane, as the
-// fp16 pair (max, -min): one packed maximum per step, exchanging through
-// DPP inside each row of 16 lanes (lanes i ^ 1, i ^ 2, then the half-row
-// and row mirrors), then folding the four row results into lane 63 with
-// the row broadcasts. The result is read from lane 63 (uniform).
+// One step of a packed-fp16 maximum across lanes: each lane takes the
+// maximum of its value and the value DPP control CTRL brings from another
+// lane of its row of 16 (rows outside ROW_MASK keep their own value).
 template <int CTRL, int ROW_MASK>
 __device__ inline half2v dpp_step(half2v v) {
     const int b = __builtin_bit_cast(int, v);
-    // rows the mask leaves out keep their own value (max with itself)
     const int m = ROW_MASK == 0xF ? __builtin_amdgcn_mov_dpp(b, CTRL, 0xF, 0xF, false)
                                   : __builtin_amdgcn_update_dpp(b, b, CTRL, ROW_MASK, 0xF, false);
     return __builtin_elementwise_maximum(v, __builtin_bit_cast(half2v, m));
 }
-__device__ inline void wave_range(uint32_t pair, float &xmax, float &xmin) {
-    const half2v p = as_h2(pair);
-    half2v v = __builtin_elementwise_maximum(half2v{p.x, -p.x}, half2v{p.y, -p.y});
-    v = dpp_step<0xB1, 0xF>(v);   // quad_perm 1 0 3 2
-    v = dpp_step<0x4E, 0xF>(v);   // quad_perm 2 3 0 1
-    v = dpp_step<0x141, 0xF>(v);  // row_half_mirror
-    v = dpp_step<0x140, 0xF>(v);  // row_mirror: every lane holds its row's result
-    v = dpp_step<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
-    v = dpp_step<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
-    const half2v r = __builtin_bit_cast(half2v, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-    xmax = (float)r.x;
-    xmin = -(float)r.y;
-}
 
 // ------------------------------------------------------------------ append
-// One wave per unit of (KV head, 4 consecutive input tokens): lane l owns
-// dimensions 2l and 2l + 1 of each key and dimensions l and l + 64 of each
-// value (the two nibbles of one 4-bit V byte, so every byte of the cache
-// has one writer). Tokens with a negative slot, or a slot past the cache,
-// are skipped. Tokens t .. t + 3 of a block (t % 4 == 0) sit in 4
-// consecutive bytes of every V row, so when the unit's 4 slots are such a
-// run the wave stores one 32-bit word per V row instead of 4 bytes.
+// One wave per unit of (KV head, 4 consecutive input tokens). Row g of the
+// wave (lanes 16 g .. 16 g + 15) takes token g of the unit; lane i of the
+// row holds key dimensions 8 i .. 8 i + 7 and value dimensions 4 i .. 4 i + 3
+// and 64 + 4 i .. 64 + 4 i + 3 (4-bit: the two nibbles of V bytes
+// 4 i .. 4 i + 3, so every byte of the cache has one writer). A vector's
+// range is reduced inside its row, so each instruction of the quantization
+// serves the four tokens at once. Tokens with a negative slot, or a slot
+// past the cache, are skipped. Tokens t .. t + 3 of a block (t % 4 == 0)
+// sit in 4 consecutive bytes of every V row, so when the unit's 4 slots are
+// such a run the lanes exchange their V bytes (ds_bpermute) and lane L
+// stores the run's 32-bit word of V row L (and, 8-bit, of row 64 + L): one
+// store instruction covers 64 consecutive rows. Otherwise each lane stores
+// its own bytes.
 
 constexpr int kAppendQuad = 4;  // input tokens per unit
 
 // The inputs of one unit, fetched one unit ahead of their use.
 struct AppendIn {
-    int slot[kAppendQuad];
-    int h, n;                              // KV head, tokens present (1..4)
-    uint32_t kp[kAppendQuad], vp[kAppendQuad];  // this lane's fp16 key pair (2l, 2l + 1), value pair (l, l + 64)
+    int slot;      // slot of this row's token (-1: none)
+    int h, n;      // KV head, tokens present (1..4)
+    u32x4 kx, vx;  // this lane's 8 fp16 key and value elements
 };
 
+template <int BITS>
 __device__ inline void kv_append_fetch(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-                                       const int32_t *__restrict__ slots, int ntok, int quads, int Hkv, int64_t u,
-                                       int lane, AppendIn &in) {
-    const int h = (int)(u / quads), i0 = (int)(u % quads) * kAppendQuad;
+                                       const int32_t *__restrict__ slots, int ntok, int Hkv, int h, int qi, int lane,
+                                       AppendIn &in) {
+    const int i0 = qi * kAppendQuad;
+    const int g = lane >> 4, li = lane & 15;
     in.h = h;
     in.n = ntok - i0 < kAppendQuad ? ntok - i0 : kAppendQuad;
-#pragma unroll
-    for (int j = 0; j < kAppendQuad; ++j) {
-        const int i = i0 + j < ntok ? i0 + j : ntok - 1;  // a short last unit re-reads its last token
-        const size_t row = ((size_t)i * Hkv + h) * kHD;
-        in.slot[j] = slots[i];
-        in.kp[j] = *reinterpret_cast<const uint32_t *>(k + row + 2 * lane);
-        in.vp[j] = (uint32_t)v[row + lane] | ((uint32_t)v[row + lane + kHD / 2] << 16);
-    }
+    const int i = i0 + g < ntok ? i0 + g : ntok - 1;  // rows past a short last unit re-read its last token
+    const size_t row = ((size_t)i * Hkv + h) * kHD;
+    const int s = slots[i];
+    in.slot = i0 + g < ntok ? s : -1;
+    in.kx = *reinterpret_cast<const u32x4 *>(k + row + 8 * li);
+    const uint2 lo = *reinterpret_cast<const uint2 *>(v + row + 4 * li);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(v + row + kHD / 2 + 4 * li);
+    in.vx = u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
-// Codes of this lane's two values of one vector, and the vector's scale and
-// zero (the weight quantizer's reading with L = 2^BITS - 1).
+// (max, -min) of an fp16 pair as an fp16 pair
+__device__ inline half2v pair_range(uint32_t p) {
+    const half2v h = as_h2(p);
+    return __builtin_elementwise_maximum(half2v{h.x, -h.x}, half2v{h.y, -h.y});
+}
+
+// Codes c[0..7] of this lane's 8 elements of one vector, and the vector's
+// scale and zero (the weight quantizer's reading with L = 2^BITS - 1). The
+// vector's 128 elements are the 16 lanes of this lane's row.
 template <int BITS>
-__device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c1, uint32_t &par) {
+__device__ inline void kv_quantize_row(const u32x4 &x, uint32_t (&c)[8], uint32_t &par) {
     constexpr int L = (1 << BITS) - 1;
-    const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFF));
-    const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
-    float xmax, xmin;
-    wave_range(pair, xmax, xmin);
+    half2v r = __builtin_elementwise_maximum(__builtin_elementwise_maximum(pair_range(x[0]), pair_range(x[1])),
+                                             __builtin_elementwise_maximum(pair_range(x[2]), pair_range(x[3])));
+    r = dpp_step<0xB1, 0xF>(r);   // quad_perm 1 0 3 2
+    r = dpp_step<0x4E, 0xF>(r);   // quad_perm 2 3 0 1
+    r = dpp_step<0x141, 0xF>(r);  // row_half_mirror
+    r = dpp_step<0x140, 0xF>(r);  // row_mirror: every lane holds its row's (max, -min)
+    const float xmax = (float)r.x, xmin = -(float)r.y;
     const float s32 = __builtin_fmaxf(div_steps(xmax - xmin, (float)L, 1.0f / (float)L), kScaleFloor);
     const _Float16 s16 = (_Float16)s32;
     const float sf = (float)s16;
@@ -149,10 +153,14 @@ __device__ inline void kv_quantize_pair(uint32_t pair, uint32_t &c0, uint32_t &c
     const float zf = __builtin_amdgcn_fmed3f(round_quotient_fp16(-xmin, sf, inv), kRoundMagic, kRoundMagic + (float)L);
     const int z = (int)(__builtin_bit_cast(uint32_t, zf) - kRoundMagicBits);
     const float lo = kRoundMagic - (float)z, hi = lo + (float)L;
-    const float y0 = __builtin_amdgcn_fmed3f(round_quotient_fp16(x0, sf, inv), lo, hi);
-    const float y1 = __builtin_amdgcn_fmed3f(round_quotient_fp16(x1, sf, inv), lo, hi);
-    c0 = __builtin_bit_cast(uint32_t, y0) - kRoundMagicBits + z;
-    c1 = __builtin_bit_cast(uint32_t, y1) - kRoundMagicBits + z;
+    const uint32_t off = (uint32_t)z - kRoundMagicBits;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t w = x[e / 2];
+        const float xe = (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 1 ? w >> 16 : w & 0xFFFF));
+        const float y = __builtin_amdgcn_fmed3f(round_quotient_fp16(xe, sf, inv), lo, hi);
+        c[e] = __builtin_bit_cast(uint32_t, y) + off;
+    }
     par = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)z << 16);
 }
 
@@ -160,83 +168,131 @@ template <int BITS>
 __device__ inline void kv_append_store(const AppendIn &in, int Hkv, int64_t num_blocks, int lane,
                                        uint8_t *__restrict__ cache) {
     typedef KvGeom<BITS> Geo;
-    const int s0 = in.slot[0];
+    const int g = lane >> 4, li = lane & 15;
+    // the unit's four slots (uniform): a 4-aligned run inside one block?
+    const int s0 = __builtin_amdgcn_readlane(in.slot, 0);
     bool run = in.n == kAppendQuad && s0 >= 0 && (s0 & 3) == 0 && s0 / kBS < num_blocks;
 #pragma unroll
-    for (int j = 1; j < kAppendQuad; ++j) run = run && in.slot[j] == s0 + j;
-    uint32_t vw0 = 0, vw1 = 0;  // V code bytes of a run: rows l and l + 64 (8-bit) or row l (4-bit)
-#pragma unroll
-    for (int j = 0; j < kAppendQuad; ++j) {
-        const int slot = in.slot[j];
-        if (j >= in.n || slot < 0 || slot / kBS >= num_blocks) continue;
-        const int blk = slot / kBS, t = slot % kBS;
-        uint8_t *region = cache + ((size_t)blk * Hkv + in.h) * Geo::kRegion;
-        uint32_t c0, c1, kpar, vpar;
-        kv_quantize_pair<BITS>(in.kp[j], c0, c1, kpar);
-        uint8_t *row = region + t * Geo::kRowBytes;
+    for (int j = 1; j < kAppendQuad; ++j) run = run && __builtin_amdgcn_readlane(in.slot, 16 * j) == s0 + j;
+    const int slot = in.slot;
+    const bool valid = slot >= 0 && slot / kBS < num_blocks;
+    const int blk = valid ? slot / kBS : 0, t = slot & (kBS - 1);
+    uint8_t *region = cache + ((size_t)blk * Hkv + in.h) * Geo::kRegion;
+
+    uint32_t c[8], kpar, vpar;
+    kv_quantize_row<BITS>(in.kx, c, kpar);
+    if (valid) {
+        uint8_t *krow = region + t * Geo::kRowBytes;
         if constexpr (BITS == 8)
-            *reinterpret_cast<uint16_t *>(row + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+            *reinterpret_cast<uint2 *>(krow + 8 * li) =
+                make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
         else
-            row[lane] = (uint8_t)(c0 | (c1 << 4));
-        kv_quantize_pair<BITS>(in.vp[j], c0, c1, vpar);
-        if (run) {
-            if constexpr (BITS == 8) {
-                vw0 |= c0 << (8 * j);
-                vw1 |= c1 << (8 * j);
-            } else {
-                vw0 |= (c0 | (c1 << 4)) << (8 * j);
-            }
-        } else {
-            uint8_t *vrows = region + Geo::kCodeBytes;
-            const int p = v_position(t);
-            if constexpr (BITS == 8) {
-                vrows[lane * kBS + p] = (uint8_t)c0;
-                vrows[(lane + kHD / 2) * kBS + p] = (uint8_t)c1;
-            } else {
-                vrows[lane * kBS + p] = (uint8_t)(c0 | (c1 << 4));
-            }
-        }
-        if (lane == 0) {
-            *reinterpret_cast<uint32_t *>(region + Geo::kKPar + 4 * t) = kpar;
-            *reinterpret_cast<uint32_t *>(region + Geo::kVPar + 4 * t) = vpar;
-        }
+            *reinterpret_cast<uint32_t *>(krow + 4 * li) =
+                c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12) | (c[4] << 16) | (c[5] << 20) | (c[6] << 24) | (c[7] << 28);
+    }
+    kv_quantize_row<BITS>(in.vx, c, vpar);
+    if (valid && li == 0) {
+        *reinterpret_cast<uint32_t *>(region + Geo::kKPar + 4 * t) = kpar;
+        *reinterpret_cast<uint32_t *>(region + Geo::kVPar + 4 * t) = vpar;
+    }
+    // V code bytes of this lane: byte e of vb0 is dimension 4 li + e (4-bit:
+    // with dimension 64 + 4 li + e in its high nibble), byte e of vb1
+    // (8-bit) dimension 64 + 4 li + e
+    uint32_t vb0, vb1 = 0;
+    if constexpr (BITS == 8) {
+        vb0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        vb1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    } else {
+        vb0 = (c[0] | (c[4] << 4)) | ((c[1] | (c[5] << 4)) << 8) | ((c[2] | (c[6] << 4)) << 16) |
+              ((c[3] | (c[7] << 4)) << 24);
     }
     if (run) {
+        // row r = lane (+ 64): byte j of its word is token j's byte of that
+        // row, byte r % 4 of lane (j, r / 4 % 16)'s vb
         uint8_t *vrows = cache + ((size_t)(s0 / kBS) * Hkv + in.h) * Geo::kRegion + Geo::kCodeBytes;
-        const int p = v_position(s0 % kBS);  // positions p .. p + 3 hold the run's tokens
-        *reinterpret_cast<uint32_t *>(vrows + lane * kBS + p) = vw0;
-        if constexpr (BITS == 8) *reinterpret_cast<uint32_t *>(vrows + (lane + kHD / 2) * kBS + p) = vw1;
+        const int p = v_position(s0 & (kBS - 1));  // positions p .. p + 3 hold the run's tokens
+        const uint32_t b = lane & 3;
+        const uint32_t sel = b | ((4 + b) << 8);
+#pragma unroll
+        for (int half = 0; half < (BITS == 8 ? 2 : 1); ++half) {
+            const uint32_t vb = half ? vb1 : vb0;
+            uint32_t src[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) src[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (16 * j + (lane >> 2)), (int)vb);
+            const uint32_t t01 = __builtin_amdgcn_perm(src[1], src[0], sel);
+            const uint32_t t23 = __builtin_amdgcn_perm(src[3], src[2], sel);
+            *reinterpret_cast<uint32_t *>(vrows + (64 * half + lane) * kBS + p) = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+        }
+    } else if (valid) {
+        uint8_t *vrows = region + Geo::kCodeBytes;
+        const int p = v_position(t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vrows[(4 * li + e) * kBS + p] = (uint8_t)(vb0 >> (8 * e));
+            if constexpr (BITS == 8) vrows[(64 + 4 * li + e) * kBS + p] = (uint8_t)(vb1 >> (8 * e));
+        }
     }
 }
 
-constexpr int kAppendWaves = 4;     // waves per workgroup
-constexpr int kAppendWgPerCu = 8;   // resident workgroups per CU (8 waves per SIMD)
+constexpr int kAppendWaves = 16;   // waves per workgroup: one unit each, 64 tokens per task
+constexpr int kAppendWgPerCu = 2;   // resident workgroups per CU (8 waves per SIMD)
 
-// A resident grid: each wave loops over units u = h * quads + i / 4
-// (head-major), fetching the next unit's inputs before it quantizes and
-// stores the current one. Workgroups are dealt to the 8 XCDs round-robin,
-// so workgroup w takes position (w % 8)-th share start + w / 8 of each
-// grid-sized round: every XCD runs a contiguous range of units, and the
-// tokens of one cache block and head run on one XCD, where their V stores
-// meet in its L2 as whole lines.
+// A resident grid over tasks of (KV head, 64 consecutive input tokens),
+// one unit of 4 tokens per wave; each wave fetches its unit of the
+// workgroup's next task before it quantizes and stores the current one, and
+// the workgroup meets at a barrier after every task. When the slots run in
+// order a task is one cache block: the 16 partial writes that complete each
+// V line all come from one workgroup within one task, and an XCD has only
+// its resident workgroups' blocks open at a time, so the lines fill in its
+// L2 before they are written back (units dealt to waves across the whole
+// grid had drifted apart over the rounds and sent partly written lines to
+// memory: 1.9x the cache bytes written for 8-bit codes).
 template <int BITS>
 __global__ void __launch_bounds__(64 * kAppendWaves)
 kv_append_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, const int32_t *__restrict__ slots,
                  int ntok, int Hkv, int64_t num_blocks, uint8_t *__restrict__ cache) {
     const int lane = threadIdx.x & 63;
-    const int quads = (ntok + kAppendQuad - 1) / kAppendQuad;
-    const int64_t units = (int64_t)quads * Hkv;
-    const uint32_t grid = gridDim.x, w = blockIdx.x, x = w % 8, q = grid / 8, rem = grid % 8;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t stride = (int64_t)grid * kAppendWaves;
-    int64_t u = (int64_t)(x * q + (x < rem ? x : rem) + w / 8) * kAppendWaves + wave;
-    if (u >= units) return;
+    const int quads = (ntok + kAppendQuad - 1) / kAppendQuad;
+    const int chunks = (quads + kAppendWaves - 1) / kAppendWaves;  // tasks per head
+    const int64_t tasks = (int64_t)chunks * Hkv;
+    const uint32_t grid = gridDim.x;
+    int64_t T = blockIdx.x;
+    if (T >= tasks) return;
+    // task T = h * chunks + c, advanced by the grid without a division per task
+    int h = (int)(T / chunks), c = (int)(T % chunks);
+    const int64_t sh = grid / chunks;
+    const int sc = (int)(grid % chunks);
+    // every task fetches (a unit past the last token re-reads the last one,
+    // in bounds, marked empty), so the loads in flight are the same on every
+    // path
+    auto fetch = [&](int hh, int cc, bool live, AppendIn &in) {
+        const int qi = kAppendWaves * cc + wave;
+        const bool ok = live && qi < quads;
+        kv_append_fetch<BITS>(k, v, slots, ntok, Hkv, ok ? hh : Hkv - 1, ok ? qi : quads - 1, lane, in);
+        if (!ok) {
+            in.slot = -1;
+            in.n = 0;
+        }
+    };
     AppendIn cur, nxt;
-    kv_append_fetch(k, v, slots, ntok, quads, Hkv, u, lane, cur);
-    for (; u < units; u += stride) {
-        if (u + stride < units) kv_append_fetch(k, v, slots, ntok, quads, Hkv, u + stride, lane, nxt);
+    fetch(h, c, true, cur);
+    while (true) {
+        const int64_t nT = T + grid;
+        int nc = c + sc;
+        const int carry = nc >= chunks;
+        nc -= carry ? chunks : 0;
+        const int64_t hn = h + sh + carry;
+        const int nh = hn < Hkv ? (int)hn : Hkv - 1;
+        const bool nlive = nT < tasks;  // uniform over the workgroup
+        fetch(nh, nc, nlive, nxt);
         kv_append_store<BITS>(cur, Hkv, num_blocks, lane, cache);
+        if (!nlive) break;
+        __syncthreads();
         cur = nxt;
+        h = nh;
+        c = nc;
+        T = nT;
     }
 }
 
@@ -588,10 +644,10 @@ size_t kv_region_bytes(int bits) { return bits == 8 ? KvGeom<8>::kRegion : KvGeo
 hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, const int32_t *slots, int ntok, int Hkv, int bits,
                             int64_t num_blocks, uint8_t *cache, int num_cus, hipStream_t stream) {
     if (ntok == 0) return hipSuccess;
-    const int64_t units = (int64_t)((ntok + kAppendQuad - 1) / kAppendQuad) * Hkv;
-    const int64_t wgs = (units + kAppendWaves - 1) / kAppendWaves;
+    const int64_t quads = (ntok + kAppendQuad - 1) / kAppendQuad;
+    const int64_t tasks = (quads + kAppendWaves - 1) / kAppendWaves * Hkv;
     const int64_t resident = (int64_t)num_cus * kAppendWgPerCu;
-    const dim3 grid((unsigned)(wgs < resident ? wgs : resident));
+    const dim3 grid((unsigned)(tasks < resident ? tasks : resident));
     const dim3 block(64 * kAppendWaves);
     if (bits == 8)
         hipLaunchKernelGGL(kv_append_kernel<8>, grid, block, 0, stream, k, v, slots, ntok, Hkv, num_blocks, cache);
