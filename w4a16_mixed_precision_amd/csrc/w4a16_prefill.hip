@@ -76,15 +76,18 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     const int nstrip = N / kStripCols;
 
     // XCD-aware remap: dispatch order id -> logical tile. Consecutive ids go
-    // to consecutive XCDs. Where the tiles split evenly, XCD x takes half of
-    // the row tiles (x % 2) and a quarter of the column slabs (x / 2), M
-    // varying fastest, so neighbours share columns of W in one L2 and each
-    // L2 sees half of X (2048 x 4096 x 28672: 390 against 399 us with each
-    // XCD taking all rows of a contiguous run of tiles); otherwise each XCD
-    // takes a contiguous run of tiles.
+    // to consecutive XCDs. With 8 or more row tiles (X too large for one L2)
+    // and tiles that split evenly, XCD x takes half of the row tiles (x % 2)
+    // and a quarter of the column slabs (x / 2), M varying fastest, so
+    // neighbours share columns of W in one L2 and each L2 sees half of X
+    // (2048 x 4096 x 28672: 389-398 against 401-404 us with each XCD taking
+    // all rows of a contiguous run of tiles). Otherwise each XCD takes a
+    // contiguous run of tiles, which reads every weight once (at M = 256 the
+    // half-rows order read the 70B gate/up weights twice and took 221-227
+    // against 212-214 us).
     const int ntiles = tiles_m * tiles_n;
     int tm, tn;
-    if (tiles_m % 2 == 0 && tiles_n % 4 == 0) {
+    if (tiles_m >= 8 && tiles_m % 2 == 0 && tiles_n % 4 == 0) {
         const int x = blockIdx.x % 8, i = blockIdx.x / 8, half_m = tiles_m / 2;
         tm = (x % 2) * half_m + i % half_m;
         tn = (x / 2) * (tiles_n / 4) + i / half_m;

@@ -228,8 +228,9 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
     const int nblk = K / kW8Block;
     const int nstrip = N / 16;
     // XCD-aware remap: workgroups are dispatched round-robin over the eight
-    // XCDs. Where the tiles split evenly, XCD x takes half of the row tiles
-    // (x % 2) and a quarter of the column slabs (x / 2), M varying fastest:
+    // XCDs. With 8 or more row tiles and tiles that split evenly, XCD x takes
+    // half of the row tiles (x % 2) and a quarter of the column slabs (x / 2),
+    // M varying fastest:
     // the row tiles that share a slab of weights read it through one L2,
     // and each L2 sees half of X (an XCD taking all rows of a quarter of
     // the slabs, the first form, was 1.3% slower at 2048 x 4096 x 28672 and
@@ -237,7 +238,7 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
     const int ntiles = (int)gridDim.x;  // tiles_m x tiles_n
     const int tiles_n = ntiles / tiles_m;
     int tm, tn;
-    if (tiles_m % 2 == 0 && tiles_n % 4 == 0) {
+    if (tiles_m >= 8 && tiles_m % 2 == 0 && tiles_n % 4 == 0) {
         const int x = blockIdx.x % 8, i = blockIdx.x / 8, half_m = tiles_m / 2;
         tm = (x % 2) * half_m + i % half_m;
         tn = (x / 2) * (tiles_n / 4) + i / half_m;
