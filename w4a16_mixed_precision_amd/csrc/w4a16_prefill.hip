@@ -293,8 +293,44 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
         wc = wnext;
     }
 
-    // Epilogue: fp32 -> fp16 (round to nearest even) or fp32 partials; rows
-    // beyond M and strips beyond N dropped.
+    // Epilogue, unsplit K: the fp16 tile goes through LDS so that each lane
+    // stores 16 bytes of a row (8 columns) instead of one 2-byte value per
+    // accumulator element; the two X stages hold the four waves' tiles
+    // (MTW 16 rows x NSW 16 columns x 2 bytes each). In a wave's region row
+    // r, column c sits at r * RB + 16 * ((c / 8) ^ (2 * ((r / 4) % 4))) +
+    // 2 * (c % 8): the four row groups a write instruction touches fall in
+    // different 16-byte chunks. Rows beyond M and strips beyond N dropped.
+    constexpr int RB = NSW * 32;  // bytes per row of a wave's tile
+    static_assert(WAVES * MTW * 16 * RB <= 2 * STAGE, "the wave tiles must fit the X stages");
+    static_assert(NSW % 2 == 0 || NSW == 1, "16-byte row chunks");
+    if (S == 1 && NSW % 2 == 0) {
+        __syncthreads();  // every wave is done with the last X stage
+        uint8_t *wt = lds + wave * (MTW * 16 * RB);
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int j = 0; j < NSW; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = mt * 16 + 4 * kq + e, cc = j * 16 + col;
+                    *reinterpret_cast<uint16_t *>(wt + r * RB + 16 * ((cc >> 3) ^ (2 * ((r >> 2) & 3))) + 2 * (cc & 7)) =
+                        f32_to_f16_bits(acc[mt][j][e]);
+                }
+        // each read covers RB / 16 chunks of 64 / (RB / 16) rows
+        constexpr int CPR = RB / 16;          // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;         // rows per instruction
+        const int k = lane % CPR, rr = lane / CPR;
+        const int s = strip_w + k / 2;
+#pragma unroll
+        for (int i = 0; i < MTW * 16 / RPI; ++i) {
+            const int r = i * RPI + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(wt + r * RB + 16 * (k ^ (2 * ((r >> 2) & 3))));
+            const int row = m0 + rbase + r;
+            if (row < M && s < nstrip)
+                *reinterpret_cast<u32x4 *>(Y + (size_t)row * N + (size_t)strip_w * kStripCols + 8 * k) = v;
+        }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
