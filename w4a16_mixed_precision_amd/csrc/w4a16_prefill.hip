@@ -297,9 +297,9 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
     // stores 16 bytes of a row (8 columns) instead of one 2-byte value per
     // accumulator element; the two X stages hold the four waves' tiles
     // (MTW 16 rows x NSW 16 columns x 2 bytes each). In a wave's region row
-    // r, column c sits at r * RB + 16 * ((c / 8) ^ (2 * ((r / 4) % 4))) +
-    // 2 * (c % 8): the four row groups a write instruction touches fall in
-    // different 16-byte chunks. Rows beyond M and strips beyond N dropped.
+    // r, column c sits at r * RB + 16 * ((c / 8) ^ x(r)) + 2 * (c % 8) with
+    // x(r) = 2 ((r / 4) % 4) mod the chunks per row: the four row groups a
+    // write instruction touches fall in different 16-byte chunks. Rows beyond M and strips beyond N dropped.
     constexpr int RB = NSW * 32;  // bytes per row of a wave's tile
     static_assert(WAVES * MTW * 16 * RB <= 2 * STAGE, "the wave tiles must fit the X stages");
     static_assert(NSW % 2 == 0 || NSW == 1, "16-byte row chunks");
@@ -313,7 +313,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = mt * 16 + 4 * kq + e, cc = j * 16 + col;
-                    *reinterpret_cast<uint16_t *>(wt + r * RB + 16 * ((cc >> 3) ^ (2 * ((r >> 2) & 3))) + 2 * (cc & 7)) =
+                    *reinterpret_cast<uint16_t *>(wt + r * RB + 16 * ((cc >> 3) ^ ((2 * ((r >> 2) & 3)) & (RB / 16 - 1))) + 2 * (cc & 7)) =
                         f32_to_f16_bits(acc[mt][j][e]);
                 }
         // each read covers RB / 16 chunks of 64 / (RB / 16) rows
@@ -324,10 +324,48 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 #pragma unroll
         for (int i = 0; i < MTW * 16 / RPI; ++i) {
             const int r = i * RPI + rr;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(wt + r * RB + 16 * (k ^ (2 * ((r >> 2) & 3))));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(wt + r * RB + 16 * (k ^ ((2 * ((r >> 2) & 3)) & (CPR - 1))));
             const int row = m0 + rbase + r;
             if (row < M && s < nstrip)
                 *reinterpret_cast<u32x4 *>(Y + (size_t)row * N + (size_t)strip_w * kStripCols + 8 * k) = v;
+        }
+        return;
+    }
+    // Split K: the fp32 partial tile takes the same route, half of the
+    // wave's rows at a time (a whole fp32 tile is twice the X stages), with
+    // 16-byte chunks of 4 columns and x(r) = 4 ((r / 4) % 4) mod the chunks
+    // per row. A wave reuses only its own region, and its LDS operations
+    // complete in order, so the halves need no barrier between them.
+    if (S > 1 && NSW % 2 == 0) {
+        constexpr int RB4 = NSW * 64;   // bytes per fp32 row
+        constexpr int HR = MTW * 8;     // rows per half
+        constexpr int CPR4 = RB4 / 16;  // 16-byte chunks per row
+        constexpr int RPI4 = 64 / CPR4; // rows per read instruction
+        static_assert(WAVES * HR * RB4 <= 2 * STAGE, "half wave tiles must fit the X stages");
+        __syncthreads();  // every wave is done with the last X stage
+        uint8_t *wt = lds + wave * (HR * RB4);
+        const int k = lane % CPR4, rr = lane / CPR4;
+        const int s = strip_w + k / 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int mt = 0; mt < MTW / 2; ++mt)
+#pragma unroll
+                for (int j = 0; j < NSW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = mt * 16 + 4 * kq + e, cc = j * 16 + col;
+                        *reinterpret_cast<float *>(wt + r * RB4 + 16 * ((cc >> 2) ^ ((4 * ((r >> 2) & 3)) & (CPR4 - 1))) +
+                                                   4 * (cc & 3)) = acc[h * (MTW / 2) + mt][j][e];
+                    }
+#pragma unroll
+            for (int i = 0; i < HR / RPI4; ++i) {
+                const int r = i * RPI4 + rr;
+                const floatx4 v = *reinterpret_cast<const floatx4 *>(wt + r * RB4 + 16 * (k ^ ((4 * ((r >> 2) & 3)) & (CPR4 - 1))));
+                const int row = m0 + rbase + h * HR + r;
+                if (row < M && s < nstrip)
+                    *reinterpret_cast<floatx4 *>(part + ((size_t)split * M + row) * N + (size_t)strip_w * kStripCols + 4 * k) = v;
+            }
         }
         return;
     }

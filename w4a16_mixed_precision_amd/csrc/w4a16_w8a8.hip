@@ -368,9 +368,9 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
     // Unsplit K: the fp16 tile goes through LDS so that each lane stores 16
     // bytes of a row (8 columns) instead of one 2-byte value per element; the
     // two X stages hold the four waves' tiles. In a wave's region row r,
-    // column c sits at r * RB + 16 * ((c / 8) ^ (2 * ((r / 4) % 4))) +
-    // 2 * (c % 8): the four row groups a write instruction touches fall in
-    // different 16-byte chunks. Rows beyond M and strips beyond N dropped.
+    // column c sits at r * RB + 16 * ((c / 8) ^ x(r)) + 2 * (c % 8) with
+    // x(r) = 2 ((r / 4) % 4) mod the chunks per row: the four row groups a
+    // write instruction touches fall in different 16-byte chunks. Rows beyond M and strips beyond N dropped.
     constexpr int RB = NSW * 32;  // bytes per row of a wave's tile
     static_assert(WAVES * MTW * 16 * RB <= 2 * STAGE, "the wave tiles must fit the X stages");
     if (S == 1 && NSW % 2 == 0) {
@@ -386,7 +386,7 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
                 for (int e = 0; e < 4; ++e) {
                     const int r = mt * 16 + 4 * kq + e, cc = j * 16 + col;
                     const float sx = xs[m0 + r < M ? m0 + r : M - 1];
-                    *reinterpret_cast<uint16_t *>(wt + r * RB + 16 * ((cc >> 3) ^ (2 * ((r >> 2) & 3))) + 2 * (cc & 7)) =
+                    *reinterpret_cast<uint16_t *>(wt + r * RB + 16 * ((cc >> 3) ^ ((2 * ((r >> 2) & 3)) & (RB / 16 - 1))) + 2 * (cc & 7)) =
                         scale_out(acc[mt][j][e], sx, swn);
                 }
         }
@@ -397,7 +397,7 @@ w8a8_gemm_kernel(const int8_t *__restrict__ X, const float *__restrict__ xs, con
 #pragma unroll
         for (int i = 0; i < MTW * 16 / RPI; ++i) {
             const int r = i * RPI + rr;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(wt + r * RB + 16 * (k ^ (2 * ((r >> 2) & 3))));
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(wt + r * RB + 16 * (k ^ ((2 * ((r >> 2) & 3)) & (CPR - 1))));
             if (m0 + r < M && sk < nstrip)
                 *reinterpret_cast<u32x4 *>(Y + (size_t)(m0 + r) * N + (size_t)strip_w * 16 + 8 * k) = v;
         }
