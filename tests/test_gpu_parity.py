@@ -136,6 +136,31 @@ def test_identity_prefill_split_bit_exact(G):
     assert np.array_equal(Y.view(np.uint16), expect.view(np.uint16))
 
 
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_tile_shapes_agree(monkeypatch, cfg, splits):
+    # Every instantiated workgroup tile shape of the tiled kernel (forced
+    # through W4A16_PREFILL_CFG: 256 x 256, 256 x 128, 128 x 256 and 64 x 256
+    # tiles, one or two rows of waves, 2 or 4 strips per wave) multiplies in
+    # the same order, so with the same split count its Y equals the automatic
+    # shape's bit for bit, unsplit and split (the two epilogues: fp16 tiles
+    # and fp32 partials), over ragged rows and strips; the identity rows give
+    # the fp16 weights.
+    K, N, G, M = 1408, 336, 64, 300
+    q, z, s, rng = _weights(K, N, G, seed=7)
+    packed = pack_dev(q, z, s, G)
+    X = synth.draw_x(rng, M, K)
+    eye = np.eye(K, dtype=np.float16)[:M]
+    monkeypatch.delenv("W4A16_PREFILL_CFG", raising=False)
+    ref = run_gemm(X, packed, N, K, G, path=PREFILL, splits=splits)
+    monkeypatch.setenv("W4A16_PREFILL_CFG", str(cfg))
+    Y = run_gemm(X, packed, N, K, G, path=PREFILL, splits=splits)
+    assert np.array_equal(Y.view(np.uint16), ref.view(np.uint16))
+    Yi = run_gemm(eye, packed, N, K, G, path=PREFILL, splits=splits)
+    expect = oracle.dequant(q, z, s, G).astype(np.float16)[:M]
+    assert np.array_equal(Yi.view(np.uint16), expect.view(np.uint16))
+
+
 @pytest.mark.parametrize("path,M", [(DECODE, 1), (DECODE, 13), (DECODE, 64), (PREFILL, 5), (PREFILL, 300)])
 def test_integer_weights_bit_exact(path, M):
     # s = 1, X in {-1, 0, 1}, K = 128: |Y| <= 15 * 128 < 2048, exact in fp16.
