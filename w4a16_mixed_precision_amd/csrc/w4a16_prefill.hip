@@ -30,6 +30,9 @@
 // * Split-K: when the tile grid alone cannot fill the GPU, workgroups also
 //   split K; each writes fp32 partials and a second kernel adds them in
 //   split order (the kernel boundary orders the two; no device-scope fence).
+// * Epilogue: the accumulators hold four rows of one column per lane, so the
+//   tile (fp16, or the fp32 partials half a tile at a time) is rearranged in
+//   LDS and leaves as 16-byte row chunks, whole lines of Y.
 // * Workgroups are dispatched round-robin over the eight XCDs; tile ids are
 //   remapped so that the workgroups resident on one XCD share rows of X and
 //   columns of W in that XCD's L2.

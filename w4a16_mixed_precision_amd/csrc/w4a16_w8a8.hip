@@ -24,7 +24,8 @@
 // global -> LDS by direct 16-byte loads (XOR-swizzled by row, two stages)
 // while the current one is multiplied; each wave streams its packed weight
 // tiles into registers half a block (two 64-row steps) ahead. Split-K writes int32 partials that
-// a second kernel adds (exactly) and scales.
+// a second kernel adds (exactly) and scales. Unsplit, the scaled fp16 tile
+// is rearranged in LDS and stored as 16-byte row chunks.
 #include <stdlib.h>
 
 #include "w4a16_device.h"
