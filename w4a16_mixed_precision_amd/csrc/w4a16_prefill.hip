@@ -241,6 +241,7 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 #pragma unroll
             for (int v = 0; v < 4; ++v) bw[j][v] = bword(0, j, v);
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int g = 0; g < 4 * NSW; ++g) {
             const int t = g / NSW, j = g % NSW;
@@ -291,6 +292,13 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
         load_w(b + 1 < be ? b + 1 : b, wnext);
         if (b + 1 < be && (b + 1) % GS == 0) load_sz(b + 1, scn, zbn);
         compute(b, cur, wc, sz);
+        // the block's matrix instructions run at raised wave priority, the
+        // wait for the next block at the normal one: the SIMD's other wave
+        // (the other workgroup's) then issues its own matrix work first
+        // while this one waits (graph-timed: 2048 x 4096 x 28672 383-389
+        // against 387-393 us, Qwen-shaped G = 64 pair 90-93 / 219-223
+        // against 93-95 / 224-230 us)
+        __builtin_amdgcn_s_setprio(0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         wc = wnext;
