@@ -410,10 +410,18 @@ decode_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packed
         // refill can reach past the run, and those blocks are out of range);
         // the last round only consumes.
         const int rounds = (we - b + 2 * NB - 1) / (2 * NB);
+        // The tiles' arithmetic runs at raised wave priority (the SIMD's
+        // other waves, waiting on their loads, issue behind it): the same
+        // results, up to 0.1 us less per launch (8B down projection at M = 1
+        // 7.52 against 7.61 us, graph-timed).
         for (int r = 1; r < rounds; ++r, b += 2 * NB) {
+            __builtin_amdgcn_s_setprio(1);
             compute(b, b0, xr0);
+            __builtin_amdgcn_s_setprio(0);
             load(b + 2 * NB, b0, xr0);
+            __builtin_amdgcn_s_setprio(1);
             compute(b + NB, b1, xr1);
+            __builtin_amdgcn_s_setprio(0);
             load(b + 3 * NB, b1, xr1);
         }
         compute(b, b0, xr0);
