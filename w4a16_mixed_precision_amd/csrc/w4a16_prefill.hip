@@ -241,10 +241,14 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
 #pragma unroll
             for (int v = 0; v < 4; ++v) bw[j][v] = bword(0, j, v);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int g = 0; g < 4 * NSW; ++g) {
             const int t = g / NSW, j = g % NSW;
+            // steps 1 and 2 run at raised wave priority, step 0 (behind the
+            // block start) and step 3 (ahead of the wait for the next block)
+            // at the normal one
+            if (g == NSW) __builtin_amdgcn_s_setprio(1);
+            if (g == 3 * NSW) __builtin_amdgcn_s_setprio(0);
             const int pg = g - 1;                      // previous strip group
             const int pt = pg / NSW + 1, pj = pg % NSW;  // its strip's next step
             const bool pending = g > 0 && pt < 4;
@@ -292,13 +296,15 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
         load_w(b + 1 < be ? b + 1 : b, wnext);
         if (b + 1 < be && (b + 1) % GS == 0) load_sz(b + 1, scn, zbn);
         compute(b, cur, wc, sz);
-        // the block's matrix instructions run at raised wave priority, the
-        // wait for the next block at the normal one: the SIMD's other wave
-        // (the other workgroup's) then issues its own matrix work first
-        // while this one waits (graph-timed: 2048 x 4096 x 28672 383-389
-        // against 387-393 us, Qwen-shaped G = 64 pair 90-93 / 219-223
-        // against 93-95 / 224-230 us)
-        __builtin_amdgcn_s_setprio(0);
+        // The middle two steps of each block run at raised wave priority
+        // (inside compute), the block start, the last step and the wait for
+        // the next block at the normal one: while one wave sets up or waits,
+        // the SIMD's other wave (the other workgroup's) issues its matrix
+        // work first. Graph-timed against no priority: 2048 x 4096 x 28672
+        // 379-382 against 387-393 us, 8192 x 57344 at M = 256 202-203
+        // against 212-214 us, Qwen-shaped G = 64 pair 86 / 214-219 against
+        // 93-95 / 224-230 us; raising it for the whole block, from the block
+        // start or from the barrier measured 1-4% slower than this window.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         wc = wnext;
