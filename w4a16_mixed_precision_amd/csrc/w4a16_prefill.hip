@@ -300,11 +300,12 @@ prefill_kernel(const uint16_t *__restrict__ X, const uint8_t *__restrict__ packe
         // (inside compute), the block start, the last step and the wait for
         // the next block at the normal one: while one wave sets up or waits,
         // the SIMD's other wave (the other workgroup's) issues its matrix
-        // work first. Graph-timed against no priority: 2048 x 4096 x 28672
-        // 379-382 against 387-393 us, 8192 x 57344 at M = 256 202-203
-        // against 212-214 us, Qwen-shaped G = 64 pair 86 / 214-219 against
-        // 93-95 / 224-230 us; raising it for the whole block, from the block
-        // start or from the barrier measured 1-4% slower than this window.
+        // work first. Graph-timed: 2048 x 4096 x 28672 378-385 us (387-393
+        // with no priority change), Qwen-shaped G = 64 pair 86-88 / 214-220
+        // us (93-95 / 224-230), 8192 x 57344 at M = 256 199-207 us (203-215
+        // with the whole block raised); raising it for the whole block, from
+        // the block start or from the barrier measured 1-4% slower than this
+        // window.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         wc = wnext;
